@@ -1,0 +1,275 @@
+"""Pins for the CPU oracle: facts fixed by the mathematics of the gated delta
+rule, independent of the oracle's own code.
+
+Every ``pin_*`` takes an oracle function ``fn(q, k, v, g_log, beta, scale,
+state) -> (out, state)`` and raises AssertionError when ``fn`` disagrees.
+``test_oracle.py`` runs them on the real oracle (all must hold);
+``test_oracle_mutants.py`` runs them on deliberately broken copies of the
+oracle's C source (each copy must fail at least one).
+
+The recurrence (standard gated delta rule, named by the "GDN CTE Kernel API
+Reference" page, introduction and Background):
+    S_t = e^{g_t} S_{t-1} + beta_t k_t (v_t - e^{g_t} S_{t-1}^T k_t)^T
+    o_t = scale S_t^T q_t,   value head h reads key head h // (Hv/Hk).
+"""
+import json
+import os
+
+import numpy as np
+
+from oracle.chunked import gdn_chunked
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def random_case(seed, B=1, Hk=1, Hv=1, S=8, Dk=4, Dv=3, decay=0.3, state=True):
+    """Small random float32 inputs (normalised q, k; beta in (0,1); g < 0)."""
+    r = _rng(seed)
+    q = _unit(r.standard_normal((B, Hk, S, Dk))).astype(np.float32)
+    k = _unit(r.standard_normal((B, Hk, S, Dk))).astype(np.float32)
+    v = r.standard_normal((B, Hv, S, Dv)).astype(np.float32)
+    g = (-decay * r.uniform(0.1, 2.0, (B, Hv, S))).astype(np.float32)
+    beta = r.uniform(0.05, 0.95, (B, Hv, S)).astype(np.float32)
+    s0 = (0.5 * r.standard_normal((B, Hv, Dk, Dv))).astype(np.float32) if state else None
+    return q, k, v, g, beta, s0
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, "%s: shape %s vs %s" % (what, a.shape, b.shape)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    ref = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
+    assert err <= tol * ref, "%s: max err %.3e > %.1e" % (what, err, tol * ref)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_beta_zero_pure_decay(fn):
+    """beta = 0 removes the write: S_T = e^{sum g} S_0 and
+    o_t = scale e^{sum_{tau<=t} g_tau} S_0^T q_t."""
+    q, k, v, g, beta, s0 = random_case(1, B=2, Hk=1, Hv=2, S=9, Dk=4, Dv=3)
+    beta[:] = 0.0
+    scale = 0.7
+    out, st = fn(q, k, v, g, beta, scale, s0)
+    G = np.cumsum(g.astype(np.float64), axis=-1)
+    for b in range(2):
+        for h in range(2):
+            S0 = s0[b, h].astype(np.float64)
+            for t in range(9):
+                exp_o = scale * np.exp(G[b, h, t]) * (S0.T @ q[b, 0, t].astype(np.float64))
+                _close(out[b, h, t], exp_o, 1e-12, "beta0 out")
+            _close(st[b, h], np.exp(G[b, h, -1]) * S0, 1e-12, "beta0 state")
+
+
+def pin_orthonormal_overwrite(fn):
+    """g = 0, beta = 1, S_0 = 0 and orthonormal keys: every write stores its
+    value exactly, S_n = sum_i k_i v_i^T, so S_n^T k_j = v_j; writing an
+    already-stored key again replaces its value (S^T k = new v)."""
+    r = _rng(2)
+    D, Dv = 6, 5
+    Qm, _ = np.linalg.qr(r.standard_normal((D, D)))
+    keys = Qm.T                                   # rows orthonormal
+    k = keys[None, None].astype(np.float32)       # S = D tokens
+    kd = k.astype(np.float64)[0, 0]
+    q = k.copy()                                  # read back with the keys themselves
+    v = r.standard_normal((1, 1, D, Dv)).astype(np.float32)
+    g = np.zeros((1, 1, D), np.float32)
+    beta = np.ones((1, 1, D), np.float32)
+    out, st = fn(q, k, v, g, beta, 1.0, None)
+    S_exp = sum(np.outer(kd[i], v[0, 0, i].astype(np.float64)) for i in range(D))
+    _close(st[0, 0], S_exp, 1e-6, "orthonormal state")
+    _close(st[0, 0].T @ kd.T, v[0, 0].T.astype(np.float64), 1e-6, "orthonormal recall")
+    # out_t = S_t^T k_t = v_t (the key just written is read back)
+    _close(out[0, 0], v[0, 0], 1e-6, "orthonormal out")
+    # overwrite: key 0 written twice, second time with a new value
+    k2 = np.concatenate([k, k[:, :, :1]], axis=2)
+    v_new = r.standard_normal((1, 1, 1, Dv)).astype(np.float32)
+    v2 = np.concatenate([v, v_new], axis=2)
+    g2 = np.zeros((1, 1, D + 1), np.float32)
+    b2 = np.ones((1, 1, D + 1), np.float32)
+    out2, st2 = fn(k2, k2, v2, g2, b2, 1.0, None)
+    _close(st2[0, 0].T @ kd[0], v_new[0, 0, 0], 1e-6, "overwrite recall")
+    _close(st2[0, 0].T @ kd[1], v[0, 0, 1], 1e-6, "other key untouched")
+
+
+def pin_single_token_projection(fn):
+    """One token, g = 0, beta = 1: S_1 = (I - k k^T) S_0 + k v^T."""
+    q, k, v, g, beta, s0 = random_case(3, S=1, Dk=5, Dv=3)
+    g[:] = 0.0
+    beta[:] = 1.0
+    out, st = fn(q, k, v, g, beta, 1.3, s0)
+    kk = k[0, 0, 0].astype(np.float64)
+    S1 = (np.eye(5) - np.outer(kk, kk)) @ s0[0, 0].astype(np.float64) \
+        + np.outer(kk, v[0, 0, 0].astype(np.float64))
+    _close(st[0, 0], S1, 1e-12, "projection state")
+    _close(out[0, 0, 0], 1.3 * S1.T @ q[0, 0, 0].astype(np.float64), 1e-12, "projection out")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def pin_golden_scalar(fn):
+    """Hand-worked Dk = Dv = 1 example (tests/golden/scalar_gdn.json)."""
+    d = _golden("scalar_gdn.json")
+    n = len(d["g_log"])
+    sh = lambda x: np.asarray(x, np.float32).reshape(1, 1, n, 1)
+    out, st = fn(sh(d["q"]), sh(d["k"]), sh(d["v"]),
+                 np.asarray(d["g_log"], np.float32).reshape(1, 1, n),
+                 np.asarray(d["beta"], np.float32).reshape(1, 1, n), d["scale"],
+                 np.full((1, 1, 1, 1), d["state0"], np.float32))
+    # g_log is stored as float32, so e^{g} is exact to ~1e-7 relative only
+    _close(out.reshape(n), d["out"], 1e-6, "golden scalar out")
+    _close(st.reshape(()), d["state"], 1e-6, "golden scalar state")
+
+
+def pin_golden_matrix(fn):
+    """Hand-worked Dk = Dv = 2 example with a non-zero start state."""
+    d = _golden("matrix_gdn.json")
+    n = len(d["g_log"])
+    out, st = fn(np.asarray(d["q"], np.float32).reshape(1, 1, n, 2),
+                 np.asarray(d["k"], np.float32).reshape(1, 1, n, 2),
+                 np.asarray(d["v"], np.float32).reshape(1, 1, n, 2),
+                 np.asarray(d["g_log"], np.float32).reshape(1, 1, n),
+                 np.asarray(d["beta"], np.float32).reshape(1, 1, n), d["scale"],
+                 np.asarray(d["state0"], np.float32).reshape(1, 1, 2, 2))
+    _close(out.reshape(n, 2), d["out"], 1e-6, "golden matrix out")
+    _close(st.reshape(2, 2), d["state"], 1e-6, "golden matrix state")
+
+
+# ------------------------------------------------------------- brute force
+
+def pin_bruteforce_products(fn):
+    """Explicit Dk x Dk transition products, a different association order:
+    Phi_t = e^{g_t} (I - beta_t k_t k_t^T);
+    S_t = (Phi_t ... Phi_1) S_0 + sum_{s<=t} (Phi_t ... Phi_{s+1}) beta_s k_s v_s^T;
+    o_t = scale S_t^T q_t. GQA with Hk = 2, Hv = 4 (contiguous groups), Dk != Dv."""
+    B, Hk, Hv, S, Dk, Dv = 2, 2, 4, 7, 5, 3
+    q, k, v, g, beta, s0 = random_case(4, B, Hk, Hv, S, Dk, Dv)
+    scale = 0.6
+    out, st = fn(q, k, v, g, beta, scale, s0)
+    f = lambda x: x.astype(np.float64)
+    for b in range(B):
+        for h in range(Hv):
+            j = h // (Hv // Hk)
+            Phi = [np.exp(f(g[b, h, t])) * (np.eye(Dk) - f(beta[b, h, t]) *
+                                            np.outer(f(k[b, j, t]), f(k[b, j, t])))
+                   for t in range(S)]
+            for t in range(S):
+                prod_all = np.eye(Dk)
+                for s in range(t + 1):
+                    prod_all = Phi[s] @ prod_all
+                St = prod_all @ f(s0[b, h])
+                for s in range(t + 1):
+                    tail = np.eye(Dk)
+                    for r in range(s + 1, t + 1):
+                        tail = Phi[r] @ tail
+                    St = St + tail @ (f(beta[b, h, s]) * np.outer(f(k[b, j, s]), f(v[b, h, s])))
+                _close(out[b, h, t], scale * St.T @ f(q[b, j, t]), 1e-11, "brute out")
+            _close(st[b, h], St, 1e-11, "brute state")
+
+
+def pin_chunked_agrees(fn):
+    """The chunk-parallel WY form (an independent derivation) agrees with the
+    token-serial result for chunk sizes 1, 2, 16 and 64, with GQA, ragged
+    last chunks and a carried state."""
+    for seed, (B, Hk, Hv, S, Dk, Dv), decay in (
+            (5, (1, 2, 4, 70, 8, 6), 0.3),
+            (6, (2, 1, 2, 131, 16, 12), 0.02),
+            (7, (1, 2, 2, 64, 4, 4), 2.0)):
+        q, k, v, g, beta, s0 = random_case(seed, B, Hk, Hv, S, Dk, Dv, decay=decay)
+        out, st = fn(q, k, v, g, beta, 0.35, s0)
+        for C in (1, 2, 16, 64):
+            oc, sc = gdn_chunked(q, k, v, g, beta, 0.35, s0, chunk=C)
+            _close(out, oc, 1e-10, "chunked out C=%d" % C)
+            _close(st, sc, 1e-10, "chunked state C=%d" % C)
+
+
+# --------------------------------------------------------------- invariants
+
+def pin_gqa_equals_repeat(fn):
+    """GQA (Hv = G * Hk) equals running with q, k explicitly repeated per
+    value head in contiguous groups (value head h uses key head h // G)."""
+    q, k, v, g, beta, s0 = random_case(8, B=2, Hk=2, Hv=6, S=11, Dk=4, Dv=5)
+    o1, s1 = fn(q, k, v, g, beta, 0.5, s0)
+    qr, kr = np.repeat(q, 3, axis=1), np.repeat(k, 3, axis=1)
+    o2, s2 = fn(qr, kr, v, g, beta, 0.5, s0)
+    _close(o1, o2, 1e-13, "gqa out")
+    _close(s1, s2, 1e-13, "gqa state")
+
+
+def pin_columns_independent(fn):
+    """Each value column evolves on its own: running Dv columns together equals
+    running each column alone (Dv = 1)."""
+    q, k, v, g, beta, s0 = random_case(9, B=1, Hk=1, Hv=2, S=13, Dk=5, Dv=4)
+    o, s = fn(q, k, v, g, beta, 1.0, s0)
+    for c in range(4):
+        oc, sc = fn(q, k, v[..., c:c + 1].copy(), g, beta, 1.0, s0[..., c:c + 1].copy())
+        _close(o[..., c:c + 1], oc, 1e-13, "column out")
+        _close(s[..., c:c + 1], sc, 1e-13, "column state")
+
+
+def pin_linear_in_values_and_state(fn):
+    """For fixed q, k, g, beta the map (V, S_0) -> (out, S_T) is linear."""
+    q, k, v, g, beta, s0 = random_case(10, B=1, Hk=1, Hv=1, S=12, Dk=4, Dv=3)
+    _, _, v2, _, _, s02 = random_case(11, B=1, Hk=1, Hv=1, S=12, Dk=4, Dv=3)
+    a, c = 0.75, -1.5
+    o1, t1 = fn(q, k, v, g, beta, 1.0, s0)
+    o2, t2 = fn(q, k, v2, g, beta, 1.0, s02)
+    o3, t3 = fn(q, k, (a * v + c * v2).astype(np.float32), g, beta, 1.0,
+                (a * s0 + c * s02).astype(np.float32))
+    # float32 rounding of the combined inputs bounds the agreement
+    _close(o3, a * o1 + c * o2, 1e-6, "linear out")
+    _close(t3, a * t1 + c * t2, 1e-6, "linear state")
+
+
+def pin_scale(fn):
+    """out is linear in scale; the state does not depend on it."""
+    q, k, v, g, beta, s0 = random_case(12, S=10)
+    o1, t1 = fn(q, k, v, g, beta, 1.0, s0)
+    o2, t2 = fn(q, k, v, g, beta, 0.125, s0)
+    _close(o2, 0.125 * o1, 1e-14, "scale out")
+    _close(t2, t1, 0.0, "scale state")
+
+
+def pin_split_carry(fn):
+    """Running S1 tokens, then S2 tokens from the carried state, equals
+    running S1 + S2 tokens at once (the state is the resume point)."""
+    q, k, v, g, beta, s0 = random_case(13, B=1, Hk=1, Hv=2, S=20, Dk=4, Dv=3)
+    o, s = fn(q, k, v, g, beta, 0.9, s0)
+    cut = 7
+    oa, sa = fn(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], g[..., :cut], beta[..., :cut],
+                0.9, s0)
+    ob, sb = fn(q[:, :, cut:], k[:, :, cut:], v[:, :, cut:], g[..., cut:], beta[..., cut:],
+                0.9, sa)
+    _close(np.concatenate([oa, ob], axis=2), o, 1e-6, "split out")
+    _close(sb, s, 1e-6, "split state")
+
+
+def pin_permutation(fn):
+    """Permuting batches permutes results; permuting value heads inside a GQA
+    group (which share q, k) permutes results."""
+    q, k, v, g, beta, s0 = random_case(14, B=3, Hk=1, Hv=3, S=6, Dk=4, Dv=3)
+    o, s = fn(q, k, v, g, beta, 1.0, s0)
+    pb, ph = [2, 0, 1], [1, 2, 0]
+    o2, s2 = fn(q[pb], k[pb], v[pb][:, ph], g[pb][:, ph], beta[pb][:, ph], 1.0, s0[pb][:, ph])
+    _close(o2, o[pb][:, ph], 1e-14, "perm out")
+    _close(s2, s[pb][:, ph], 1e-14, "perm state")
+
+
+ALL_PINS = [
+    pin_beta_zero_pure_decay, pin_orthonormal_overwrite, pin_single_token_projection,
+    pin_golden_scalar, pin_golden_matrix, pin_bruteforce_products, pin_chunked_agrees,
+    pin_gqa_equals_repeat, pin_columns_independent, pin_linear_in_values_and_state,
+    pin_scale, pin_split_carry, pin_permutation,
+]
