@@ -1,0 +1,239 @@
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one ``gdn_chunked_prefill`` call on the batched long prefill
+workload (B=4, Hk=16, Hv=32, Dk=Dv=128, S=8192, bf16 q/k/v, fp32 g/beta and
+state, state carried in place from step to step). All inputs are seeded,
+synthetic and resident in HBM before timing starts. W untimed warm-up steps,
+then exactly K timed steps bracketed by device synchronisation; each launch is
+also bracketed by HIP events on the launch stream to get the kernel's own
+duration for the roofline.
+
+The decode path (B=256 single-token steps, 64 autoregressive steps with fresh
+inputs) is measured the same way in the same run and reported under
+"decode". Prints ONE JSON line.
+
+Roofline (per launch, algorithmic, see the workload docstrings below):
+* prefill: HBM bytes = tokens x (q + k + v + out + g + beta) + state in/out;
+  algorithmic MFMA flops reported as "mfma_util" against the bf16 dense peak.
+* decode: HBM bytes = 2 x fp32 state + q, k, v, out, g, beta.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "GDN prefill tokens/s + MFMA util (S=8192); decode steps/s + HBM GB/s"
+
+
+def prefill_algorithmic(B, Hk, Hv, S, Dk, Dv, esize=2, chunk=64):
+    """Algorithmic HBM bytes and MFMA flops of one prefill call.
+
+    bytes: q, k [B,Hk,S,Dk] + v, out [B,Hv,S,Dv] in the operand type, g and
+    beta fp32 [B,Hv,S], the fp32 state read once and written once.
+    flops (per value head and chunk of C tokens; lower-triangular products
+    counted at half size; K K^T and Q K^T shared inside a GQA group):
+      W = T K and U~ = T V: C^2 (Dk + Dv); W S, Q S, K^T U: 3 x 2 C Dk Dv;
+      P U: C^2 Dv; T: C^3 / 3; per key head: K K^T, Q K^T: 2 x C^2 Dk.
+    """
+    tokens = B * S
+    nbytes = (tokens * (2 * Hk * Dk + 2 * Hv * Dv) * esize + tokens * Hv * 8
+              + 2 * B * Hv * Dk * Dv * 4)
+    C = chunk
+    per_chunk_vh = C * C * (Dk + Dv) + 6 * C * Dk * Dv + C * C * Dv + C ** 3 / 3.0
+    per_chunk_kh = 2 * C * C * Dk
+    nchunks = B * S / C
+    flops = nchunks * (Hv * per_chunk_vh + Hk * per_chunk_kh)
+    return float(nbytes), float(flops)
+
+
+def decode_algorithmic(B, Hk, Hv, Dk, Dv, esize=2):
+    """HBM bytes of one decode step: fp32 state read + write, q, k, v, out, g, beta."""
+    return float(2 * B * Hv * Dk * Dv * 4 + (2 * B * Hk * Dk + 2 * B * Hv * Dv) * esize
+                 + B * Hv * 8)
+
+
+def _events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def bench_prefill(torch, gdn, inputs, steps, warmup):
+    w = inputs.WORKLOADS["prefill_b4_s8192"]
+    d = inputs.draw_workload(w)
+    dev = torch.device("cuda", 0)
+    t = {k: torch.from_numpy(d[k]).to(dev) for k in d}
+    for k in ("q", "k", "v"):
+        t[k] = t[k].to(torch.bfloat16)
+    out = torch.empty((w.B, w.Hv, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], w.scale, t["state"],
+                            out=out, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    ev = _events(torch, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_step = (t1 - t0) * 1e3 / steps
+    nbytes, flops = prefill_algorithmic(w.B, w.Hk, w.Hv, w.S, w.Dk, w.Dv)
+    return w, d, ms_step, kern_ms, nbytes, flops
+
+
+def bench_decode(torch, gdn, inputs, reps, warmup):
+    w = inputs.WORKLOADS["decode_b256"]
+    state0, steps = inputs.draw_decode_steps(w)
+    dev = torch.device("cuda", 0)
+    st = torch.from_numpy(state0).to(dev)
+    dev_steps = []
+    for s in steps:
+        dev_steps.append({
+            "q": torch.from_numpy(s["q"][:, :, 0]).to(dev).to(torch.bfloat16),
+            "k": torch.from_numpy(s["k"][:, :, 0]).to(dev).to(torch.bfloat16),
+            "v": torch.from_numpy(s["v"][:, :, 0]).to(dev).to(torch.bfloat16),
+            "g": torch.from_numpy(np.ascontiguousarray(s["g_log"][:, :, 0])).to(dev),
+            "b": torch.from_numpy(np.ascontiguousarray(s["beta"][:, :, 0])).to(dev)})
+    out = torch.empty((w.B, w.Hv, w.Dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run64(evs=None):
+        for i, s in enumerate(dev_steps):
+            if evs is not None:
+                evs[i][0].record(stream)
+            gdn.decode_step(s["q"], s["k"], s["v"], s["g"], s["b"], w.scale, st, out=out,
+                            stream=stream)
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(warmup):
+        run64()
+    evs = [_events(torch, len(dev_steps)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(reps):
+        run64(evs[r])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n = reps * len(dev_steps)
+    kern_ms = float(np.mean([a.elapsed_time(b) for e in evs for a, b in e]))
+    ms_step = (t1 - t0) * 1e3 / n
+    return w, steps, state0, ms_step, kern_ms, decode_algorithmic(w.B, w.Hk, w.Hv, w.Dk, w.Dv)
+
+
+def cpu_baseline_prefill(w, d):
+    """The oracle on batch 0 of the prefill workload (1 x 8192 tokens x 32 heads)."""
+    import oracle
+    n = oracle.default_threads()
+    sl = lambda x: np.ascontiguousarray(x[:1])
+    t0 = time.perf_counter()
+    oracle.gdn_serial(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g_log"]), sl(d["beta"]), w.scale,
+                      sl(d["state"]), nthreads=n)
+    dt = time.perf_counter() - t0
+    return {"value": w.S / dt, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": "batch 0 of the prefill workload: 1 x %d tokens x %d value heads "
+                      "(1/%d of one step), fp64 token-serial, %.2f s" % (w.S, w.Hv, w.B, dt)}
+
+
+def cpu_baseline_decode(w, steps, state0, nsteps=8):
+    import oracle
+    n = oracle.default_threads()
+    st = state0.astype(np.float64)
+    t0 = time.perf_counter()
+    for s in steps[:nsteps]:
+        _, st = oracle.gdn_serial(s["q"], s["k"], s["v"], s["g_log"], s["beta"], w.scale, st,
+                                  nthreads=n, inplace=True)
+    dt = time.perf_counter() - t0
+    return {"value": nsteps / dt, "unit": "steps/s", "cores": n, "kind": "oracle",
+            "sample": "first %d of the 64 decode steps at B=%d, fp64, %.2f s" % (nsteps, w.B, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the recurrence has no cross-GPU step in this "
+              "library (per-GPU shards of (batch, key-head group) are independent); run with "
+              "--gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    from linear_attention_recurrence_chunked_amd import inputs
+    gdn.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w, d, ms_step, kern_ms, nbytes, flops = bench_prefill(torch, gdn, inputs, args.steps,
+                                                          args.warmup)
+    tokens = w.B * w.S
+    dw, dsteps, dstate0, dms, dkern_ms, dbytes = bench_decode(torch, gdn, inputs,
+                                                              max(1, args.steps // 10), 1)
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; normalised q/k, gates from random A_log/dt_bias)",
+        "config": {"workload": "prefill_b4_s8192", "B": w.B, "Hk": w.Hk, "Hv": w.Hv,
+                   "S": w.S, "Dk": w.Dk, "Dv": w.Dv, "tokens_per_step": tokens,
+                   "state": "fp32 in place, carried across steps"},
+        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_kernel",
+                     "achieved": nbytes / (kern_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": nbytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "kernel_ms": kern_ms,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "mfma_util": {"achieved_tflops": flops / (kern_ms / 1e3) / 1e12,
+                      "peak_tflops": BF16_PEAK_TFLOPS,
+                      "frac": flops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+                      "algorithmic_flops_per_launch": flops},
+        "decode": {"workload": "decode_b256", "B": dw.B, "Hk": dw.Hk, "Hv": dw.Hv,
+                   "value": 1e3 / dms, "unit": "steps/s", "ms_per_step": dms,
+                   "tokens_per_s": dw.B * 1e3 / dms,
+                   "roofline": {"bound": "hbm", "kernel": "gdn_decode_kernel",
+                                "achieved": dbytes / (dkern_ms / 1e3) / 1e9,
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dbytes / (dkern_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                "traffic": None, "kernel_ms": dkern_ms,
+                                "algorithmic_bytes_per_launch": dbytes}},
+        "host": {"cpu": platform.processor() or platform.machine(),
+                 "gpu": torch.cuda.get_device_name(0)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(w, d)
+        res["decode"]["cpu_baseline"] = cpu_baseline_decode(dw, dsteps, dstate0)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

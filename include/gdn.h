@@ -1,0 +1,135 @@
+/*
+ * gdn.h -- C ABI of libgdn: the gated delta-rule (GDN) linear-attention
+ * recurrence on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (standard gated delta rule, named by the "GDN CTE Kernel API
+ * Reference" page in its introduction and Background; the recurrence itself is
+ * not printed there):
+ *
+ *   S_t = e^{g_t} S_{t-1} + beta_t k_t (v_t - e^{g_t} S_{t-1}^T k_t)^T
+ *   o_t = scale * S_t^T q_t
+ *
+ * per batch b and value head h; value head h reads key/query head
+ * h / (Hv / Hk) (same page, Notes). S is [Dk][Dv], fp32.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers to contiguous row-major buffers
+ *   owned by the caller. The library allocates nothing on the call path and
+ *   keeps no mutable global state.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream). A GDN_OK return means the work was enqueued; device faults
+ *   surface at the caller's next synchronisation.
+ * - Arguments are validated on the host before anything is enqueued; on any
+ *   error return nothing has been launched and no buffer has been written.
+ * - q, k, v and out share the compute dtype (`dtype`); g_log, beta and the
+ *   state are always fp32 (page "GDN CTE Kernel API Reference", Parameters
+ *   g_log, beta, recurrent_state and Notes: the state is fp32 whatever the
+ *   compute dtype).
+ * - q and k must be L2-normalised per token and head (same page, Notes). This
+ *   is the caller's contract and is not checked. NaN/Inf inputs are not
+ *   checked either.
+ * - The state is updated IN PLACE: `state_inout` holds the initial state on
+ *   entry and the final state on return (same page, Parameters:
+ *   recurrent_state supplied and aliased). For a zero start the caller
+ *   zero-fills it.
+ * - Concurrent calls that share an output or state buffer race; calls on
+ *   disjoint buffers are independent.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Compute dtype of q, k, v and out. */
+typedef enum {
+    GDN_F32 = 0,   /* IEEE float32 operands; fp32 matrix-core products  */
+    GDN_BF16 = 1   /* bfloat16 operands; fp32 accumulation and state     */
+} gdn_dtype;
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,         /* a required pointer is NULL                          */
+    GDN_ERR_SHAPE = 2,        /* B, Hk, Hv, S < 1, Hv % Hk != 0, S % 64 != 0 (prefill) */
+    GDN_ERR_UNSUPPORTED = 3,  /* Dk or Dv outside [16, 128] or not a multiple of 16   */
+    GDN_ERR_DTYPE = 4,        /* dtype is not a gdn_dtype value                       */
+    GDN_ERR_ALIGN = 5,        /* a tensor pointer is not 16-byte aligned              */
+    GDN_ERR_ALIAS = 6,        /* out or state_inout overlaps another tensor argument  */
+    GDN_ERR_WORKSPACE = 7,    /* workspace smaller than the queried size              */
+    GDN_ERR_HIP = 8           /* the HIP runtime refused a launch                     */
+} gdn_status;
+
+/* Opaque stream handle: a hipStream_t. NULL selects the null stream. */
+typedef void* gdn_stream;
+
+/*
+ * gdn_chunked_prefill -- chunk-parallel prefill over S tokens.
+ *
+ * Follows "GDN CTE Kernel API Reference" (signature gdn_cte, Parameters,
+ * Returns, Notes): the chunked form of the recurrence above, returning the
+ * un-normalised output and the final state.
+ *
+ *   q, k        [B, Hk, S, Dk]  compute dtype, token-major, L2-normalised
+ *   v           [B, Hv, S, Dv]  compute dtype
+ *   g_log       [B, Hv, S]      fp32, per-token natural-log decay (<= 0)
+ *   beta        [B, Hv, S]      fp32, per-token write strength in (0, 1)
+ *   scale       query scaling (typically 1/sqrt(Dk)), applied on the device
+ *   state_inout [B, Hv, Dk, Dv] fp32, in: initial state, out: final state
+ *   out         [B, Hv, S, Dv]  compute dtype, written (head-major)
+ *   workspace   device scratch of at least
+ *               gdn_chunked_prefill_workspace_bytes(...) bytes; may be NULL
+ *               when that size is 0
+ *
+ * Constraints: Hv % Hk == 0; S % 64 == 0 (the chunk length); 16 <= Dk, Dv
+ * <= 128, multiples of 16 (the pages' MAX_HEAD_DIM = 128, Notes); all
+ * pointers 16-byte aligned; out and state_inout must not overlap each other
+ * or any input. The result is deterministic run to run.
+ */
+gdn_status gdn_chunked_prefill(const void* q, const void* k, const void* v,
+                               const float* g_log, const float* beta, float scale,
+                               float* state_inout, void* out,
+                               int B, int Hk, int Hv, int S, int Dk, int Dv,
+                               int dtype, void* workspace, size_t workspace_bytes,
+                               gdn_stream stream);
+
+/* Device scratch bytes gdn_chunked_prefill needs for these sizes (0 when the
+ * arguments are invalid or no scratch is needed). */
+size_t gdn_chunked_prefill_workspace_bytes(int B, int Hk, int Hv, int S, int Dk, int Dv,
+                                           int dtype);
+
+/*
+ * gdn_decode_step -- one token (S = 1) of the recurrence for every (b, h).
+ *
+ * The single-token recurrence that the "GDN Block TKG Kernel API Reference"
+ * page places inside its decode block (introduction: "single-token
+ * recurrence"), here on its own and in place.
+ *
+ *   q, k        [B, Hk, Dk]     compute dtype, L2-normalised
+ *   v           [B, Hv, Dv]     compute dtype
+ *   g_log, beta [B, Hv]         fp32
+ *   state_inout [B, Hv, Dk, Dv] fp32, updated in place
+ *   out         [B, Hv, Dv]     compute dtype
+ *
+ * Constraints as for gdn_chunked_prefill (without S).
+ */
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
+                           const float* g_log, const float* beta, float scale,
+                           float* state_inout, void* out,
+                           int B, int Hk, int Hv, int Dk, int Dv, int dtype,
+                           gdn_stream stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gdn_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

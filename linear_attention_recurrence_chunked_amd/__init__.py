@@ -1,0 +1,179 @@
+"""Python binding of libgdn: the gated delta-rule recurrence on MI355X.
+
+Argument marshalling only -- every step of the computation runs in the HIP
+kernels of ``libgdn.so`` (built from ``csrc/`` by
+``python -m linear_attention_recurrence_chunked_amd.build``). The names
+mirror the C ABI in ``include/gdn.h``:
+
+* :func:`chunked_prefill` -> ``gdn_chunked_prefill``
+* :func:`decode_step`     -> ``gdn_decode_step``
+* :func:`prefill_workspace_bytes` -> ``gdn_chunked_prefill_workspace_bytes``
+* :func:`status_string`   -> ``gdn_status_string``
+
+Tensors are torch tensors on the GPU; torch supplies device memory and the
+current stream, nothing else. If ``libgdn.so`` is missing these functions raise
+:class:`LibraryNotBuilt`; there is no fallback path.
+"""
+import ctypes
+import os
+
+__all__ = ["chunked_prefill", "decode_step", "prefill_workspace_bytes", "status_string",
+           "GdnError", "LibraryNotBuilt", "load_library", "LIB_PATH", "GDN_F32", "GDN_BF16"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
+          4: "GDN_ERR_DTYPE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
+          8: "GDN_ERR_HIP"}
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (%d): %s" % (STATUS.get(code, "?"), code, msg))
+        self.code = code
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def load_library():
+    """Load libgdn.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryNotBuilt("%s is not built; run `python -m "
+                              "linear_attention_recurrence_chunked_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.gdn_chunked_prefill.restype = _I
+    lib.gdn_chunked_prefill.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                        _I, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.gdn_chunked_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_chunked_prefill_workspace_bytes.argtypes = [_I] * 7
+    lib.gdn_decode_step.restype = _I
+    lib.gdn_decode_step.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                    _I, _I, _I, _I, _I, _I, _P]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [_I]
+    lib.gdn_version.restype = _I
+    lib.gdn_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_string(code):
+    return load_library().gdn_status_string(int(code)).decode()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError("q/k/v/out must be torch.bfloat16 or torch.float32, got %s" % t.dtype)
+
+
+def _check(t, name, dtype, device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(stream, device):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _raise(code):
+    if code != 0:
+        raise GdnError(code, status_string(code))
+
+
+def prefill_workspace_bytes(B, Hk, Hv, S, Dk, Dv, dtype_code):
+    return int(load_library().gdn_chunked_prefill_workspace_bytes(B, Hk, Hv, S, Dk, Dv,
+                                                                  dtype_code))
+
+
+def chunked_prefill(q, k, v, g_log, beta, scale, state, out=None, workspace=None, stream=None):
+    """Chunked gated delta-rule prefill (``gdn_chunked_prefill``).
+
+    q, k [B,Hk,S,Dk] and v [B,Hv,S,Dv] in bf16 or fp32 (one dtype); g_log, beta
+    [B,Hv,S] fp32; state [B,Hv,Dk,Dv] fp32, updated in place. Returns out
+    [B,Hv,S,Dv] in the compute dtype (allocated if not given).
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    code = _dtype_code(q)
+    B, Hk, S, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[3]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    for t, n in ((g_log, "g_log"), (beta, "beta"), (state, "state")):
+        _check(t, n, torch.float32, dev)
+    if k.shape != q.shape or v.shape[0] != B or v.shape[2] != S:
+        raise ValueError("q/k/v shapes disagree")
+    if g_log.shape != (B, Hv, S) or beta.shape != (B, Hv, S) or state.shape != (B, Hv, Dk, Dv):
+        raise ValueError("g_log/beta/state shapes disagree with q/v")
+    if out is None:
+        out = torch.empty((B, Hv, S, Dv), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", q.dtype, dev)
+        if out.shape != (B, Hv, S, Dv):
+            raise ValueError("out shape must be [B,Hv,S,Dv]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = lib.gdn_chunked_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), g_log.data_ptr(),
+                                 beta.data_ptr(), float(scale), state.data_ptr(), out.data_ptr(),
+                                 B, Hk, Hv, S, Dk, Dv, code, ws_ptr, ws_bytes,
+                                 _stream(stream, dev))
+    _raise(rc)
+    return out
+
+
+def decode_step(q, k, v, g_log, beta, scale, state, out=None, stream=None):
+    """One-token gated delta-rule step (``gdn_decode_step``), state in place.
+
+    q, k [B,Hk,Dk], v [B,Hv,Dv] (bf16 or fp32); g_log, beta [B,Hv] fp32; state
+    [B,Hv,Dk,Dv] fp32. Returns out [B,Hv,Dv].
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    code = _dtype_code(q)
+    B, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    for t, n in ((g_log, "g_log"), (beta, "beta"), (state, "state")):
+        _check(t, n, torch.float32, dev)
+    if k.shape != q.shape or v.shape[0] != B:
+        raise ValueError("q/k/v shapes disagree")
+    if g_log.shape != (B, Hv) or beta.shape != (B, Hv) or state.shape != (B, Hv, Dk, Dv):
+        raise ValueError("g_log/beta/state shapes disagree with q/v")
+    if out is None:
+        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", q.dtype, dev)
+        if out.shape != (B, Hv, Dv):
+            raise ValueError("out shape must be [B,Hv,Dv]")
+    rc = lib.gdn_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g_log.data_ptr(),
+                             beta.data_ptr(), float(scale), state.data_ptr(), out.data_ptr(),
+                             B, Hk, Hv, Dk, Dv, code, _stream(stream, dev))
+    _raise(rc)
+    return out

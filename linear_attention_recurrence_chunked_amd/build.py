@@ -1,0 +1,63 @@
+"""Build libgdn.so (HIP, gfx950) in-tree.
+
+    python -m linear_attention_recurrence_chunked_amd.build
+
+compiles every source under csrc/ with hipcc for gfx950 into
+``libgdn.so`` next to this file (always recompiles).
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libgdn.so")
+BUILD_DIR = os.path.join(HERE, "_build")
+ARCH = "gfx950"
+
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip"]
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    # Packed fp32 vector instructions are kept out of the generated code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def _hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def _compile(src):
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [_hipcc()] + HIPCC_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+    noisy = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln]
+    if noisy:
+        sys.stderr.write("\n".join(noisy) + "\n")
+    return obj
+
+
+def build(verbose=False):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), "-shared", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,137 @@
+// gdn_api.cpp -- the C ABI of libgdn (include/gdn.h): host-side validation
+// and dispatch to the HIP launchers. Validation runs entirely on the host and
+// before any HIP call, so every error path can be exercised without a GPU and
+// leaves all buffers untouched.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_launch.h"
+
+namespace {
+
+constexpr int kChunk = 64;        // prefill chunk length (tokens)
+constexpr int kMaxHeadDim = 128;  // Dk, Dv upper bound ("GDN CTE", Notes)
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// a * b * ... in uint64 with overflow detection; returns false on overflow.
+bool mul_ok(uint64_t& acc, uint64_t x) {
+    if (x != 0 && acc > UINT64_MAX / x) return false;
+    acc *= x;
+    return true;
+}
+
+bool extent(const void* p, std::initializer_list<uint64_t> dims, uint64_t elem, Range& r) {
+    uint64_t n = elem;
+    for (uint64_t d : dims)
+        if (!mul_ok(n, d)) return false;
+    const uintptr_t lo = (uintptr_t)p;
+    if (n > UINTPTR_MAX - lo) return false;
+    r = Range{lo, lo + (uintptr_t)n};
+    return true;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Common {
+    const void* q; const void* k; const void* v;
+    const float* g; const float* beta; float* state; void* out;
+    int B, Hk, Hv, S, Dk, Dv, dtype;
+};
+
+// Shared checks for prefill (S = sequence length) and decode (S = 1).
+gdn_status validate(const Common& c, bool prefill) {
+    if (!c.q || !c.k || !c.v || !c.g || !c.beta || !c.state || !c.out) return GDN_ERR_NULL;
+    if (c.dtype != GDN_F32 && c.dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (c.B < 1 || c.Hk < 1 || c.Hv < 1 || c.S < 1) return GDN_ERR_SHAPE;
+    if (c.Hv % c.Hk != 0) return GDN_ERR_SHAPE;
+    if (prefill && c.S % kChunk != 0) return GDN_ERR_SHAPE;
+    if ((int64_t)c.B * c.Hv > INT32_MAX) return GDN_ERR_SHAPE;
+    if (c.Dk < 16 || c.Dk > kMaxHeadDim || c.Dk % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    if (c.Dv < 16 || c.Dv > kMaxHeadDim || c.Dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    const void* ptrs[] = {c.q, c.k, c.v, c.g, c.beta, c.state, c.out};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_ALIGN;
+
+    const uint64_t es = c.dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t B = c.B, Hk = c.Hk, Hv = c.Hv, S = c.S, Dk = c.Dk, Dv = c.Dv;
+    Range rq, rk, rv, rg, rb, rs, ro;
+    if (!extent(c.q, {B, Hk, S, Dk}, es, rq) || !extent(c.k, {B, Hk, S, Dk}, es, rk) ||
+        !extent(c.v, {B, Hv, S, Dv}, es, rv) || !extent(c.g, {B, Hv, S}, 4, rg) ||
+        !extent(c.beta, {B, Hv, S}, 4, rb) || !extent(c.state, {B, Hv, Dk, Dv}, 4, rs) ||
+        !extent(c.out, {B, Hv, S, Dv}, es, ro))
+        return GDN_ERR_SHAPE;
+    // Written buffers may not overlap each other or anything read.
+    const Range reads[] = {rq, rk, rv, rg, rb};
+    for (const Range& r : reads)
+        if (overlaps(ro, r) || overlaps(rs, r)) return GDN_ERR_ALIAS;
+    if (overlaps(ro, rs)) return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_chunked_prefill_workspace_bytes(int B, int Hk, int Hv, int S, int Dk, int Dv,
+                                           int dtype) {
+    (void)B; (void)Hk; (void)Hv; (void)S; (void)Dk; (void)Dv; (void)dtype;
+    return 0;  // the fused chunk kernel keeps every intermediate on chip
+}
+
+gdn_status gdn_chunked_prefill(const void* q, const void* k, const void* v,
+                               const float* g_log, const float* beta, float scale,
+                               float* state_inout, void* out,
+                               int B, int Hk, int Hv, int S, int Dk, int Dv,
+                               int dtype, void* workspace, size_t workspace_bytes,
+                               gdn_stream stream) {
+    const Common c{q, k, v, g_log, beta, state_inout, out, B, Hk, Hv, S, Dk, Dv, dtype};
+    const gdn_status st = validate(c, /*prefill=*/true);
+    if (st != GDN_OK) return st;
+    const size_t need = gdn_chunked_prefill_workspace_bytes(B, Hk, Hv, S, Dk, Dv, dtype);
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return GDN_ERR_WORKSPACE;
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    const gdn::PrefillArgs a{q, k, v, g_log, beta, scale, state_inout, out,
+                             B, Hk, Hv, S, Dk, Dv};
+    return gdn::launch_prefill(a, dtype, (hipStream_t)stream) == hipSuccess ? GDN_OK
+                                                                             : GDN_ERR_HIP;
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
+                           const float* g_log, const float* beta, float scale,
+                           float* state_inout, void* out,
+                           int B, int Hk, int Hv, int Dk, int Dv, int dtype,
+                           gdn_stream stream) {
+    const Common c{q, k, v, g_log, beta, state_inout, out, B, Hk, Hv, 1, Dk, Dv, dtype};
+    const gdn_status st = validate(c, /*prefill=*/false);
+    if (st != GDN_OK) return st;
+    (void)hipGetLastError();
+    const gdn::DecodeArgs a{q, k, v, g_log, beta, scale, state_inout, out, B, Hk, Hv, Dk, Dv};
+    return gdn::launch_decode(a, dtype, (hipStream_t)stream) == hipSuccess ? GDN_OK
+                                                                           : GDN_ERR_HIP;
+}
+
+const char* gdn_status_string(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "invalid shape (sizes < 1, Hv % Hk != 0, S % 64 != 0, or overflow)";
+        case GDN_ERR_UNSUPPORTED: return "unsupported head dimension (Dk, Dv must be multiples of 16 in [16, 128])";
+        case GDN_ERR_DTYPE: return "invalid dtype";
+        case GDN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case GDN_ERR_ALIAS: return "out or state_inout overlaps another tensor argument";
+        case GDN_ERR_WORKSPACE: return "workspace too small";
+        case GDN_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int gdn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// gdn_decode.hip -- single-token (S = 1) gated delta-rule step, in place.
+//
+// The single-token recurrence of the "GDN Block TKG Kernel API Reference"
+// page (introduction: the decode layer's "single-token recurrence"):
+//   x = S^T k,  y = S^T q                       (contractions over Dk)
+//   u = beta (v - e^g x)
+//   S' = e^g S + k u^T
+//   o = scale S'^T q = scale (e^g y + (k . q) u)
+//
+// Memory-bound: the fp32 state (Dk x Dv, 64 KiB at 128 x 128) is read once and
+// written once per step; everything else is a few hundred bytes. One
+// workgroup of 256 threads owns one (b, h). Thread t holds columns
+// 4*(t%32) .. +3 of rows (t/32) + 8i, i = 0..15: every row of 128 floats is
+// read by 32 consecutive lanes as 16-byte vectors (fully coalesced), and the
+// 64 state values stay in registers between the read and the write. The Dk
+// reductions are per-thread partial sums followed by an 8-way LDS reduction
+// in a fixed order (deterministic). State traffic uses non-temporal hints: a
+// step's state is not re-read by the same step.
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+template <typename E>
+__global__ __launch_bounds__(256) void gdn_decode_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ g_log, const float* __restrict__ beta, float scale,
+    float* __restrict__ state, E* __restrict__ out, int Hk, int Hv, int Dk, int Dv)
+{
+    const int bh = blockIdx.x;                 // b * Hv + h
+    const int b = bh / Hv;
+    const int h = bh - b * Hv;
+    const int j = h / (Hv / Hk);               // GQA: contiguous groups of Hv/Hk
+    const int t = threadIdx.x;
+    const int cg = t & 31;                     // columns 4cg .. 4cg+3
+    const int r0 = t >> 5;                     // rows r0 + 8i
+
+    __shared__ float sk[128], sq[128], su[128];
+    __shared__ float red[2][8][128];
+    __shared__ float skq;
+
+    const size_t qk_off = ((size_t)b * Hk + j) * Dk;
+    if (t < 128) sk[t] = (t < Dk) ? to_f32(k[qk_off + t]) : 0.0f;
+    else         sq[t - 128] = (t - 128 < Dk) ? to_f32(q[qk_off + t - 128]) : 0.0f;
+
+    float* S = state + (size_t)bh * Dk * Dv;
+    const bool colok = 4 * cg < Dv;
+    f32x4 s[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = r0 + 8 * i;
+        if (colok && r < Dk)
+            s[i] = __builtin_nontemporal_load((const f32x4*)(S + (size_t)r * Dv + 4 * cg));
+        else
+            s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float a = __expf(g_log[bh]);
+    const float be = beta[bh];
+    __syncthreads();                           // sk, sq visible
+
+    f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = r0 + 8 * i;              // rows >= Dk hold zeros in s, sk, sq
+        x += s[i] * sk[r];
+        y += s[i] * sq[r];
+    }
+    *(f32x4*)&red[0][r0][4 * cg] = x;
+    *(f32x4*)&red[1][r0][4 * cg] = y;
+    if (t < 64) {
+        float p = sk[t] * sq[t] + sk[t + 64] * sq[t + 64];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+        if (t == 0) skq = p;
+    }
+    __syncthreads();
+
+    if (t < Dv) {
+        float xs = 0.f, ys = 0.f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) { xs += red[0][p][t]; ys += red[1][p][t]; }
+        const float vv = to_f32(v[(size_t)bh * Dv + t]);
+        const float u = be * (vv - a * xs);
+        su[t] = u;
+        out[(size_t)bh * Dv + t] = from_f32<E>(scale * (a * ys + skq * u));
+    }
+    __syncthreads();
+
+    if (colok) {
+        const f32x4 uu = *(const f32x4*)&su[4 * cg];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = r0 + 8 * i;
+            if (r < Dk) {
+                const f32x4 ns = a * s[i] + sk[r] * uu;
+                __builtin_nontemporal_store(ns, (f32x4*)(S + (size_t)r * Dv + 4 * cg));
+            }
+        }
+    }
+}
+
+template <typename E>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream)
+{
+    const unsigned grid = (unsigned)a.B * (unsigned)a.Hv;
+    hipLaunchKernelGGL(gdn_decode_kernel<E>, dim3(grid), dim3(256), 0, stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.g_log, a.beta, a.scale,
+                       a.state, (E*)a.out, a.Hk, a.Hv, a.Dk, a.Dv);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream)
+{
+    return dtype == 1 ? launch_decode_t<bf16>(a, stream) : launch_decode_t<float>(a, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,28 @@
+// gdn_launch.h -- internal host-side launchers behind the C ABI (include/gdn.h).
+// Arguments have been validated by the caller (gdn_api.cpp) when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gdn {
+
+struct PrefillArgs {
+    const void* q; const void* k; const void* v;
+    const float* g_log; const float* beta; float scale;
+    float* state; void* out;
+    int B, Hk, Hv, S, Dk, Dv;
+};
+
+struct DecodeArgs {
+    const void* q; const void* k; const void* v;
+    const float* g_log; const float* beta; float scale;
+    float* state; void* out;
+    int B, Hk, Hv, Dk, Dv;
+};
+
+// dtype: 0 = fp32 operands, 1 = bf16 operands (gdn_dtype).
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace gdn

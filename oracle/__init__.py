@@ -52,13 +52,15 @@ def _f32(x):
     return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
 
 
-def gdn_serial(q, k, v, g_log, beta, scale, state=None, nthreads=None):
+def gdn_serial(q, k, v, g_log, beta, scale, state=None, nthreads=None, inplace=False):
     """Token-serial fp64 gated delta rule.
 
     Shapes: q, k [B,Hk,S,Dk]; v [B,Hv,S,Dv]; g_log, beta [B,Hv,S];
     state [B,Hv,Dk,Dv] or None (zero initial state).
     Inputs are taken as float32 (bf16 values are exact in float32).
     Returns (out [B,Hv,S,Dv] float64, final state [B,Hv,Dk,Dv] float64).
+    With ``inplace=True`` a C-contiguous float64 ``state`` is updated in place
+    (and returned) instead of copied, for long chains of decode steps.
     """
     q, k, v, g_log, beta = (_f32(a) for a in (q, k, v, g_log, beta))
     B, Hk, S, Dk = q.shape
@@ -70,6 +72,11 @@ def gdn_serial(q, k, v, g_log, beta, scale, state=None, nthreads=None):
         raise ValueError("oracle: Hv must be a multiple of Hk")
     if state is None:
         st = np.zeros((B, Hv, Dk, Dv), dtype=np.float64)
+    elif inplace:
+        st = state
+        if not (isinstance(st, np.ndarray) and st.dtype == np.float64
+                and st.flags.c_contiguous and st.shape == (B, Hv, Dk, Dv)):
+            raise ValueError("oracle: inplace needs a C-contiguous float64 state of the right shape")
     else:
         st = np.array(state, dtype=np.float64, order="C", copy=True)
         if st.shape != (B, Hv, Dk, Dv):

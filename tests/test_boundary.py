@@ -1,0 +1,143 @@
+"""The C ABI on the CPU: libgdn.so loads without a GPU, exports every function
+include/gdn.h declares, and rejects every invalid argument with its status
+code before any HIP call (fake, never-dereferenced pointers are used)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_recurrence_chunked_amd as gdn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "gdn.h")
+
+OK, NULL, SHAPE, UNSUP, DTYPE, ALIGN, ALIAS, WS, HIP = range(9)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        from linear_attention_recurrence_chunked_amd import build
+        build.build()
+    return gdn.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"gdn_chunked_prefill", "gdn_decode_step",
+                          "gdn_chunked_prefill_workspace_bytes", "gdn_status_string",
+                          "gdn_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = lib.gdn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.gdn_status_string(99).decode() == "unknown status"
+    assert lib.gdn_version() >= 100
+
+
+def test_workspace_query_is_zero(lib):
+    assert lib.gdn_chunked_prefill_workspace_bytes(4, 16, 32, 8192, 128, 128, 1) == 0
+
+
+# Fake device addresses: far apart, 256-byte aligned, never dereferenced.
+BASE = 1 << 40
+GAP = 1 << 36
+
+
+def fake(i, off=0):
+    return BASE + i * GAP + off
+
+
+def prefill(lib, q=None, k=None, v=None, g=None, b=None, st=None, out=None,
+            B=2, Hk=2, Hv=4, S=128, Dk=64, Dv=64, dtype=1, ws=None, wsb=0):
+    P = lambda x, i: fake(i) if x is None else x
+    return lib.gdn_chunked_prefill(P(q, 0), P(k, 1), P(v, 2), P(g, 3), P(b, 4), 0.125,
+                                   P(st, 5), P(out, 6), B, Hk, Hv, S, Dk, Dv, dtype, ws, wsb,
+                                   None)
+
+
+def decode(lib, q=None, k=None, v=None, g=None, b=None, st=None, out=None,
+           B=2, Hk=2, Hv=4, Dk=64, Dv=64, dtype=1):
+    P = lambda x, i: fake(i) if x is None else x
+    return lib.gdn_decode_step(P(q, 0), P(k, 1), P(v, 2), P(g, 3), P(b, 4), 0.125,
+                               P(st, 5), P(out, 6), B, Hk, Hv, Dk, Dv, dtype, None)
+
+
+CALLS = {"prefill": prefill, "decode": decode}
+
+
+@pytest.mark.parametrize("which", sorted(CALLS))
+@pytest.mark.parametrize("arg", ["q", "k", "v", "g", "b", "st", "out"])
+def test_null_pointer(lib, which, arg):
+    # ctypes turns Python 0 into a NULL pointer
+    assert CALLS[which](lib, **{arg: 0}) == NULL
+
+
+@pytest.mark.parametrize("which", sorted(CALLS))
+def test_bad_dtype(lib, which):
+    assert CALLS[which](lib, dtype=2) == DTYPE
+    assert CALLS[which](lib, dtype=-1) == DTYPE
+
+
+@pytest.mark.parametrize("which", sorted(CALLS))
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Hk=0), dict(Hv=0), dict(Hk=3, Hv=4),
+                                dict(Hk=4, Hv=2), dict(B=-1)])
+def test_bad_shape(lib, which, kw):
+    assert CALLS[which](lib, **kw) == SHAPE
+
+
+@pytest.mark.parametrize("S", [0, 1, 63, 65, 100, 8191])
+def test_prefill_sequence_length_multiple_of_chunk(lib, S):
+    assert prefill(lib, S=S) == SHAPE
+
+
+@pytest.mark.parametrize("which", sorted(CALLS))
+@pytest.mark.parametrize("kw", [dict(Dk=0), dict(Dk=8), dict(Dk=136), dict(Dk=256),
+                                dict(Dk=72), dict(Dv=0), dict(Dv=8), dict(Dv=24),
+                                dict(Dv=144)])
+def test_unsupported_head_dims(lib, which, kw):
+    assert CALLS[which](lib, **kw) == UNSUP
+
+
+@pytest.mark.parametrize("which", sorted(CALLS))
+@pytest.mark.parametrize("arg", ["q", "k", "v", "g", "b", "st", "out"])
+def test_misaligned(lib, which, arg):
+    idx = ["q", "k", "v", "g", "b", "st", "out"].index(arg)
+    assert CALLS[which](lib, **{arg: fake(idx, 4)}) == ALIGN
+
+
+@pytest.mark.parametrize("which", sorted(CALLS))
+@pytest.mark.parametrize("victim", ["q", "k", "v", "g", "b"])
+def test_out_or_state_overlapping_inputs(lib, which, victim):
+    idx = ["q", "k", "v", "g", "b"].index(victim)
+    assert CALLS[which](lib, out=fake(idx, 16)) == ALIAS
+    assert CALLS[which](lib, st=fake(idx, 16)) == ALIAS
+
+
+@pytest.mark.parametrize("which", sorted(CALLS))
+def test_out_overlapping_state(lib, which):
+    assert CALLS[which](lib, out=fake(5, 256)) == ALIAS
+
+
+def test_adjacent_buffers_are_not_aliases(lib):
+    # q of B*Hk*S*Dk bf16 = 2*2*128*64*2 bytes; out may start right after it.
+    # (The call itself is not made valid: a bad dtype is reported first.)
+    nbytes = 2 * 2 * 128 * 64 * 2
+    assert prefill(lib, out=fake(0, nbytes), dtype=7) == DTYPE
+    assert prefill(lib, out=fake(0, nbytes), Dk=8) == UNSUP
+
+
+def test_size_overflow_is_a_shape_error(lib):
+    huge = 1 << 30
+    assert prefill(lib, B=huge, Hk=1, Hv=2, S=huge // 64 * 64) == SHAPE

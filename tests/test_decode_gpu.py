@@ -1,0 +1,70 @@
+"""gdn_decode_step on the GPU against the fp64 oracle (token-serial recurrence
+with S = 1, state carried across steps)."""
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_recurrence_chunked_amd import inputs
+from gpu_helpers import check, log, to_np, upload, TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_steps(w, nsteps, dtype=None, **over):
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    dtype = dtype or w.dtype
+    state0, steps = inputs.draw_decode_steps(w, nsteps=nsteps, **over)
+    st_dev = torch.from_numpy(state0).cuda()
+    st_ref = state0.astype(np.float64)
+    outs, refs = [], []
+    for d in steps:
+        t = upload(d, dtype)
+        # decode layout: drop the S = 1 axis
+        o = gdn.decode_step(t["q"][:, :, 0], t["k"][:, :, 0], t["v"][:, :, 0],
+                            t["g_log"][:, :, 0].contiguous(), t["beta"][:, :, 0].contiguous(),
+                            w.scale, st_dev)
+        outs.append(to_np(o))
+        ro, st_ref = oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], w.scale,
+                                       st_ref, inplace=True)
+        refs.append(ro[:, :, 0])
+    torch.cuda.synchronize()
+    return np.stack(outs), np.stack(refs), to_np(st_dev), st_ref
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [dict(B=3, Hk=2, Hv=4, Dk=128, Dv=128),
+                                   dict(B=2, Hk=1, Hv=3, Dk=64, Dv=32),
+                                   dict(B=2, Hk=2, Hv=2, Dk=48, Dv=80)])
+def test_decode_small(dtype, shape):
+    w = inputs.WORKLOADS["decode_b256"]
+    log("decode small", dtype, shape)
+    o, ro, s, rs = _run_steps(w, 8, dtype=dtype, **shape)
+    check("decode %s %s" % (dtype, shape), dtype, o, ro, s, rs)
+
+
+def test_decode_b256_64_steps():
+    """The full decode workload: B=256, Hk=16, Hv=32, Dk=Dv=128, 64 steps."""
+    w = inputs.WORKLOADS["decode_b256"]
+    log("decode_b256 x 64 steps")
+    o, ro, s, rs = _run_steps(w, w.steps)
+    check("decode_b256 64 steps", "bf16", o, ro, s, rs)
+
+
+def test_decode_deterministic():
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    w = inputs.WORKLOADS["decode_b256"]
+    state0, steps = inputs.draw_decode_steps(w, nsteps=2, B=8)
+    res = []
+    for _ in range(2):
+        st = torch.from_numpy(state0).cuda()
+        outs = []
+        for d in steps:
+            t = upload(d, "bf16")
+            outs.append(gdn.decode_step(t["q"][:, :, 0], t["k"][:, :, 0], t["v"][:, :, 0],
+                                        t["g_log"][:, :, 0].contiguous(),
+                                        t["beta"][:, :, 0].contiguous(), w.scale, st))
+        torch.cuda.synchronize()
+        res.append((torch.stack(outs).view(torch.int16).cpu(), st.cpu()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])

@@ -1,0 +1,158 @@
+"""gdn_chunked_prefill on the GPU against the fp64 oracle, element by element,
+on the named workloads at their full sizes and on edge cases (ragged value
+slices, padded key dims, GQA ratios, single chunk, weak/strong decay)."""
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_recurrence_chunked_amd import inputs
+from gpu_helpers import check, log, run_prefill, to_np, upload
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+
+
+def _parity(name, d, dtype, scale):
+    log("prefill parity:", name, {k: v.shape for k, v in d.items() if v is not None})
+    out, st = run_prefill(d, dtype, scale)
+    ro, rs = oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], scale, d["state"])
+    return check(name, dtype, out, ro, st, rs)
+
+
+def test_tiny_f32():
+    w = W["tiny_f32"]
+    _parity(w.name, inputs.draw_workload(w), "f32", w.scale)
+
+
+def test_prefill_s2048():
+    w = W["prefill_s2048"]
+    _parity(w.name, inputs.draw_workload(w), "bf16", w.scale)
+
+
+def test_prefill_b4_s8192_full():
+    """The bench workload, in the launch configuration the bench times."""
+    w = W["prefill_b4_s8192"]
+    _parity(w.name, inputs.draw_workload(w), "bf16", w.scale)
+
+
+@pytest.mark.parametrize("variant", ["std", "strong"])
+def test_prefill_s65536(variant):
+    w = W["prefill_s65536"]
+    _parity("%s/%s" % (w.name, variant), inputs.draw_workload(w, variant=variant), "bf16",
+            w.scale)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_weak_decay(dtype):
+    """Slow decay (e^g ~ 0.97): the inverse's off-diagonals and the carry
+    across chunks matter for many tokens."""
+    w = W["prefill_s2048"]
+    d = inputs.draw_prefill(B=1, Hk=4, Hv=8, S=1024, Dk=128, Dv=128, dtype=dtype,
+                            state="normal", decay="weak", seed=(1, 2, 0))
+    _parity("weak/%s" % dtype, d, dtype, w.scale)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [
+    dict(B=1, Hk=2, Hv=2, S=64, Dk=64, Dv=64),      # one chunk, G = 1
+    dict(B=2, Hk=1, Hv=4, S=192, Dk=128, Dv=128),   # G = 4
+    dict(B=1, Hk=2, Hv=4, S=256, Dk=80, Dv=48),     # padded Dk, ragged value slice
+    dict(B=3, Hk=3, Hv=3, S=128, Dk=16, Dv=112),    # smallest Dk
+    dict(B=1, Hk=1, Hv=2, S=320, Dk=128, Dv=16),    # smallest Dv
+])
+def test_shapes(dtype, shape):
+    d = inputs.draw_prefill(dtype=dtype, state="normal", decay="weak", seed=(9, 2, 1), **shape)
+    _parity("shape %s %s" % (dtype, shape), d, dtype, 1.0 / np.sqrt(shape["Dk"]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_beta_zero_pure_decay(dtype):
+    d = inputs.draw_prefill(B=1, Hk=2, Hv=4, S=128, Dk=128, Dv=128, dtype=dtype,
+                            state="normal", decay="weak", seed=(9, 2, 2))
+    d["beta"][:] = 0.0
+    _parity("beta=0 %s" % dtype, d, dtype, 0.5)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_state_no_decay(dtype):
+    d = inputs.draw_prefill(B=1, Hk=2, Hv=2, S=128, Dk=64, Dv=64, dtype=dtype,
+                            state="zero", decay="weak", seed=(9, 2, 3))
+    d["g_log"][:] = 0.0
+    _parity("g=0 %s" % dtype, d, dtype, 0.125)
+
+
+def test_split_sequence_carry_is_bitwise():
+    """prefill(S1) then prefill(S2) from the carried state equals
+    prefill(S1 + S2) bit for bit (chunk boundaries coincide)."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    d = inputs.draw_prefill(B=2, Hk=2, Hv=4, S=384, Dk=128, Dv=128, dtype="bf16",
+                            state="normal", decay="weak", seed=(9, 2, 4))
+    t = upload(d, "bf16")
+    st_full = t["state"].clone()
+    o_full = gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], 0.1, st_full)
+    st = t["state"].clone()
+    cut = 128
+    sl = lambda x, a, b: x[:, :, a:b].contiguous()
+    o1 = gdn.chunked_prefill(sl(t["q"], 0, cut), sl(t["k"], 0, cut), sl(t["v"], 0, cut),
+                             sl(t["g_log"], 0, cut), sl(t["beta"], 0, cut), 0.1, st)
+    o2 = gdn.chunked_prefill(sl(t["q"], cut, 384), sl(t["k"], cut, 384), sl(t["v"], cut, 384),
+                             sl(t["g_log"], cut, 384), sl(t["beta"], cut, 384), 0.1, st)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], dim=2).view(torch.int16), o_full.view(torch.int16))
+    assert torch.equal(st, st_full)
+
+
+def test_deterministic():
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    d = inputs.draw_prefill(B=2, Hk=4, Hv=8, S=512, Dk=128, Dv=128, dtype="bf16",
+                            state="normal", seed=(9, 0, 5))
+    t = upload(d, "bf16")
+    res = []
+    for _ in range(2):
+        st = t["state"].clone()
+        o = gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], 0.1, st)
+        torch.cuda.synchronize()
+        res.append((o.view(torch.int16).clone(), st.clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_decode_iterated_matches_prefill():
+    """64 decode steps from a state equal one 64-token prefill from it."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    d = inputs.draw_prefill(B=2, Hk=2, Hv=4, S=64, Dk=128, Dv=128, dtype="bf16",
+                            state="normal", decay="weak", seed=(9, 2, 6))
+    t = upload(d, "bf16")
+    st_p = t["state"].clone()
+    o_p = gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], 0.1, st_p)
+    st_d = t["state"].clone()
+    outs = []
+    for i in range(64):
+        outs.append(gdn.decode_step(t["q"][:, :, i].contiguous(), t["k"][:, :, i].contiguous(),
+                                    t["v"][:, :, i].contiguous(),
+                                    t["g_log"][:, :, i].contiguous(),
+                                    t["beta"][:, :, i].contiguous(), 0.1, st_d))
+    torch.cuda.synchronize()
+    o_d = torch.stack(outs, dim=2)
+    ro, rs = oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], 0.1, d["state"])
+    check("prefill vs oracle", "bf16", to_np(o_p), ro, to_np(st_p), rs)
+    check("decode x64 vs oracle", "bf16", to_np(o_d), ro, to_np(st_d), rs)
+
+
+def test_error_writes_nothing():
+    """An invalid call (S not a multiple of 64) leaves out and state untouched."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    d = inputs.draw_prefill(B=1, Hk=1, Hv=1, S=96, Dk=64, Dv=64, dtype="bf16",
+                            state="normal", seed=(9, 0, 7))
+    t = upload(d, "bf16")
+    out = torch.full((1, 1, 96, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    st = t["state"].clone()
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], 0.1, st, out=out)
+    assert e.value.code == 2
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.equal(st, t["state"])
