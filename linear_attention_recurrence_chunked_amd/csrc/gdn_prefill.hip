@@ -3,31 +3,36 @@
 // The chunked form that the "GDN CTE Kernel API Reference" page describes in
 // its introduction (work inside a chunk is parallel and goes through a
 // unit-lower-triangular inverse; a recurrence carries the state across
-// chunks). For one head and a chunk of C tokens with start state S0,
+// chunks). For one head and a chunk of C tokens with start state S0 and
 // gamma = within-chunk inclusive cumulative sum of g_log:
 //
 //   A  = diag(beta) (K K^T) (.) Mstrict     Mstrict[r,s] = e^{gamma_r-gamma_s}, s < r
 //   T  = (I + A)^{-1}                       unit lower triangular, fp32
-//   W  = T diag(beta e^gamma) K             U~ = T diag(beta) V
-//   U  = U~ - W S0                          the per-token updates u_t
-//   O  = scale (diag(e^gamma) Q S0 + (Q K^T (.) Mincl) U)     Mincl: s <= r
+//   R  = diag(beta) V - diag(beta e^gamma) K S0
+//   U  = T R                                the per-token updates u_t
+//   O  = scale (diag(e^gamma) Q S0 + P U),  P = Q K^T (.) Mincl  (s <= r)
 //   S1 = e^{gamma_C} S0 + K^T diag(e^{gamma_C - gamma}) U
 //
-// (derived from the token recurrence S_t = e^{g_t} S_{t-1} + beta_t k_t
-// (v_t - e^{g_t} S_{t-1}^T k_t)^T, o_t = scale S_t^T q_t).
+// derived from the token recurrence S_t = e^{g_t} S_{t-1} + beta_t k_t
+// (v_t - e^{g_t} S_{t-1}^T k_t)^T, o_t = scale S_t^T q_t: unrolling the chunk
+// gives (I + A) U = diag(beta) V - diag(beta e^gamma) K S0. The right-hand side
+// R is formed in fp32 before anything is rounded, so the cancellation between
+// new values and the state's prediction happens at full precision.
 //
 // Design (one fused kernel, no HBM intermediates): one workgroup of NW waves
 // owns one (batch, value head, BV-wide slice of Dv) and walks the chunks of
-// that sequence in order, holding its [Dk x BV] slice of the fp32 state in
-// MFMA accumulator registers the whole time. Per chunk only q, k, v, g, beta
-// are read and out is written, so HBM traffic is the algorithmic minimum. The
-// state-independent work of a chunk (gamma, A, T, W, U~, the masked Q K^T) is
-// recomputed by each Dv slice; BV is chosen per launch so the grid fills the
-// 256 compute units. Every product is a 16x16-tile MFMA from LDS (bf16
-// operands, fp32 accumulation; fp32 operands on the fp32 path). The
-// triangular inverse is computed in fp32: 16x16 diagonal blocks by forward
-// substitution (one lane per column), then doubling merges
-// T21 = -T22 A21 T11 on fp32 MFMA.
+// its sequence in order, holding its [Dk x BV] slice of the fp32 state in
+// MFMA accumulator registers throughout. Per chunk only q, k, v, g, beta are
+// read and out is written, so HBM traffic is the algorithmic minimum. The
+// state-independent work (gamma, A, T, the masked Q K^T) is recomputed by each
+// Dv slice; BV is chosen per launch so the grid fills the 256 compute units.
+// Products are 16x16-tile MFMAs from LDS. On the bf16 path every operand that
+// is not an exact input (S, T, R, P, U) is carried as a pair of bf16 numbers
+// hi + lo (hi = bf16(x), lo = bf16(x - hi)), and a product of two such values
+// is hi*hi + hi*lo + lo*hi, so results keep about 16 significant bits; q, k, v
+// are exact in bf16 and need one term. The triangular inverse is fp32: 16x16
+// diagonal blocks by forward substitution (one lane per column), then
+// doubling merges T21 = -T22 (A21 T11) on fp32 MFMA.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 #include "gdn_mfma.h"
@@ -40,11 +45,29 @@ template <typename E> struct Vec16;  // one 16-byte vector of E
 template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int N = 8; };
 template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
 
-__device__ __forceinline__ void store4(bf16* p, f32x4 x) {
-    bf16x4 y = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-    *(bf16x4*)p = y;
+// Writes 4 consecutive values as the operand type. With SPLIT the low parts
+// (x - hi) go to p + lo_off.
+template <bool SPLIT>
+__device__ __forceinline__ void store4(bf16* p, int lo_off, f32x4 x) {
+    bf16x4 hi = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    *(bf16x4*)p = hi;
+    if constexpr (SPLIT) {
+        bf16x4 lo = {(bf16)(x[0] - (float)hi[0]), (bf16)(x[1] - (float)hi[1]),
+                     (bf16)(x[2] - (float)hi[2]), (bf16)(x[3] - (float)hi[3])};
+        *(bf16x4*)(p + lo_off) = lo;
+    }
 }
-__device__ __forceinline__ void store4(float* p, f32x4 x) { *(f32x4*)p = x; }
+template <bool SPLIT>
+__device__ __forceinline__ void store4(float* p, int, f32x4 x) { *(f32x4*)p = x; }
+
+template <bool SPLIT>
+__device__ __forceinline__ void store1(bf16* p, int lo_off, float x) {
+    const bf16 hi = (bf16)x;
+    p[0] = hi;
+    if constexpr (SPLIT) p[lo_off] = (bf16)(x - (float)hi);
+}
+template <bool SPLIT>
+__device__ __forceinline__ void store1(float* p, int, float x) { p[0] = x; }
 
 // Linear index of a lower-triangular 16x16 tile (row-major over i >= j) -> (i, j).
 __device__ __forceinline__ void tri_index(int lt, int& i, int& j) {
@@ -56,49 +79,75 @@ __device__ __forceinline__ void tri_index(int lt, int& i, int& j) {
 template <typename E, int C, int DK, int BV, int NW>
 struct PrefillCfg {
     using M = Mfma<E>;
+    static constexpr bool SPLIT = sizeof(E) == 2;   // hi/lo operand pairs on the bf16 path
+    static constexpr int NP = SPLIT ? 2 : 1;        // parts per pair buffer row
     static constexpr int ES = (int)sizeof(E);
     static constexpr int VE = Vec16<E>::N;
-    static constexpr int LDK = DK + M::PAD;   // rows of [t][dk] (K, Q, -W) and [v][dk] (St)
-    static constexpr int LDC = C + M::PAD;    // rows of [x][t] (Kt, Vt, P, TK, TV, Ut, Ud)
-    static constexpr int LDF = C + 4;         // rows of fp32 [t][s] (A, Tf)
+    static constexpr int PAD = M::PAD;
+    static constexpr int LDK = DK + PAD;            // K, Q rows [t][dk]
+    static constexpr int LDKT = C + PAD;            // Kt rows [dk][t]
+    static constexpr int LDV = BV + PAD;            // V rows [t][v]
+    static constexpr int LDS2 = NP * DK + PAD;      // St pair rows [v][hi dk | lo dk]
+    static constexpr int LDC2 = NP * C + PAD;       // P, T, Rt, Ut, Ud pair rows [x][hi t | lo t]
+    static constexpr int LDF = C + 4;               // fp32 [t][s] rows (A, Tf)
     static constexpr int NT = C / 16;
     static constexpr int NKT = DK / 16;
     static constexpr int NVT = BV / 16;
     static constexpr int NLT = NT * (NT + 1) / 2;
-    static constexpr int NO = NT * NVT;       // out / U tiles
-    static constexpr int NS = NKT * NVT;      // state tiles
-    static constexpr int NWT = NT * NKT;      // W tiles
+    static constexpr int NO = NT * NVT;             // out / U / R tiles
+    static constexpr int NS = NKT * NVT;            // state tiles
     static constexpr int THREADS = NW * 64;
     static constexpr int OPW = (NO + NW - 1) / NW;
     static constexpr int SPW = (NS + NW - 1) / NW;
-    static constexpr int WPW = (NWT + NW - 1) / NW;
     static constexpr int JPW = (2 * NLT + NW - 1) / NW;
-    // LDS regions; buffers sharing a region have disjoint lifetimes in a chunk.
-    static constexpr int SZ_TD = C * LDK * ES;                         // K -> -W
-    static constexpr int SZ_Q = cmax(C * LDK * ES, C * LDF * 4);       // Q -> Tf
-    static constexpr int SZ_KT = DK * LDC * ES;                        // Kt
-    static constexpr int SZ_VT = BV * LDC * ES;                        // Vt
-    static constexpr int SZ_ST = BV * LDK * ES;                        // St (bf16/fp32 copy of S^T)
-    static constexpr int SZ_P = C * LDC * ES;                          // P = QK^T (.) Mincl
-    static constexpr int SZ_T = 2 * C * LDC * ES;                      // TK, TV
-    static constexpr int SZ_U = cmax(C * LDF * 4, 2 * BV * LDC * ES);  // A -> Ut, Ud
-    static constexpr int SZ_X = (C / 2) * (C / 2 + 4) * 4;             // merge scratch
-    static constexpr int SZ_SC = 8 * C * 4;                            // per-token scalars
-    static constexpr int OFF_TD = 0;
-    static constexpr int OFF_Q = OFF_TD + SZ_TD;
-    static constexpr int OFF_KT = OFF_Q + SZ_Q;
-    static constexpr int OFF_VT = OFF_KT + SZ_KT;
-    static constexpr int OFF_ST = OFF_VT + SZ_VT;
+    // Buffer sizes (bytes)
+    static constexpr int SZ_K = C * LDK * ES;
+    static constexpr int SZ_KT = DK * LDKT * ES;
+    static constexpr int SZ_V = C * LDV * ES;
+    static constexpr int SZ_ST = BV * LDS2 * ES;
+    static constexpr int SZ_PC = C * LDC2 * ES;     // C-row pair buffer (P, T)
+    static constexpr int SZ_PV = BV * LDC2 * ES;    // BV-row pair buffer (Rt, Ut, Ud)
+    static constexpr int SZ_F = C * LDF * 4;
+    static constexpr int SZ_X = (C / 2) * (C / 2 + 4) * 4;
+    static constexpr int SZ_SC = 8 * C * 4;
+    // Regions; buffers sharing a region have disjoint lifetimes within a chunk:
+    //   R1: K, Q (staging .. K S0 / Q S0)     -> T pair, Rt pair
+    //   R2: A, Tf (K K^T .. merges)           -> Ut pair, Ud pair
+    static constexpr int SZ_R1 = cmax(2 * SZ_K, SZ_PC + SZ_PV);
+    static constexpr int SZ_R2 = cmax(2 * SZ_F, 2 * SZ_PV);
+    static constexpr int OFF_R1 = 0;
+    static constexpr int OFF_R2 = OFF_R1 + SZ_R1;
+    static constexpr int OFF_KT = OFF_R2 + SZ_R2;
+    static constexpr int OFF_V = OFF_KT + SZ_KT;
+    static constexpr int OFF_ST = OFF_V + SZ_V;
     static constexpr int OFF_P = OFF_ST + SZ_ST;
-    static constexpr int OFF_T = OFF_P + SZ_P;
-    static constexpr int OFF_U = OFF_T + SZ_T;
-    static constexpr int OFF_X = OFF_U + SZ_U;
+    static constexpr int OFF_X = OFF_P + SZ_PC;
     static constexpr int OFF_SC = OFF_X + SZ_X;
     static constexpr int LDS_BYTES = OFF_SC + SZ_SC;
     static_assert(LDS_BYTES <= 160 * 1024, "chunk tiles exceed the 160 KiB LDS of a CU");
     static_assert(C % M::KS == 0 && DK % M::KS == 0, "tile sizes must match the MFMA depth");
-    static_assert(C >= 32 && (C & (C - 1)) == 0 && C <= 64, "chunk must be 32 or 64");
+    static_assert(C == 32 || C == 64, "chunk must be 32 or 64");
+    static_assert((SZ_K | SZ_KT | SZ_V | SZ_ST | SZ_PC | SZ_PV | SZ_F | SZ_X) % 16 == 0,
+                  "LDS buffers must stay 16-byte aligned");
 };
+
+// acc += A B over contraction range [k0, k1), both operands contraction-
+// contiguous in LDS. A pair operand has its low part at +lo_off elements in
+// the same row. Terms: hi*hi (+ hi*lo if B is a pair) (+ lo*hi if A is a pair).
+template <typename E, bool PA, bool PB>
+__device__ __forceinline__ f32x4 mma_range(f32x4 acc, const E* A, int lda, int ra, int alo,
+                                           const E* B, int ldb, int rb, int blo, int k0, int k1)
+{
+    using M = Mfma<E>;
+    for (int k = k0; k < k1; k += M::KS) {
+        const auto ah = M::ld(A, lda, ra, k);
+        const auto bh = M::ld(B, ldb, rb, k);
+        if constexpr (PB) acc = M::mma(ah, M::ld(B, ldb, rb, k + blo), acc);
+        if constexpr (PA) acc = M::mma(M::ld(A, lda, ra, k + alo), bh, acc);
+        acc = M::mma(ah, bh, acc);
+    }
+    return acc;
+}
 
 template <typename E, int C, int DK, int BV, int NW>
 __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
@@ -110,32 +159,33 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
     using Cf = PrefillCfg<E, C, DK, BV, NW>;
     using M = Mfma<E>;
     using VecE = typename Vec16<E>::type;
-    constexpr int VE = Cf::VE, LDK = Cf::LDK, LDC = Cf::LDC, LDF = Cf::LDF, NW_ = NW;
+    constexpr bool SP = Cf::SPLIT;
+    constexpr int VE = Cf::VE, LDK = Cf::LDK, LDKT = Cf::LDKT, LDV = Cf::LDV;
+    constexpr int LDS2 = Cf::LDS2, LDC2 = Cf::LDC2, LDF = Cf::LDF, NW_ = NW;
     constexpr int THREADS = Cf::THREADS, KS = M::KS;
+    constexpr int LO_C = C, LO_DK = DK;             // offsets of the low parts in pair rows
 
     __shared__ __attribute__((aligned(16))) char smem[Cf::LDS_BYTES];
-    E* sK = (E*)(smem + Cf::OFF_TD);
-    E* sW = sK;                                  // holds -W after the K^T products
-    E* sQ = (E*)(smem + Cf::OFF_Q);
-    float* sTf = (float*)(smem + Cf::OFF_Q);     // fp32 T after the Q products
+    E* sK = (E*)(smem + Cf::OFF_R1);
+    E* sQ = (E*)(smem + Cf::OFF_R1 + Cf::SZ_K);
+    E* sT = (E*)(smem + Cf::OFF_R1);                       // after K/Q are dead
+    E* sRt = (E*)(smem + Cf::OFF_R1 + Cf::SZ_PC);
+    float* sA = (float*)(smem + Cf::OFF_R2);
+    float* sTf = (float*)(smem + Cf::OFF_R2 + Cf::SZ_F);
+    E* sUt = (E*)(smem + Cf::OFF_R2);                      // after A/Tf are dead
+    E* sUd = (E*)(smem + Cf::OFF_R2 + Cf::SZ_PV);
     E* sKt = (E*)(smem + Cf::OFF_KT);
-    E* sVt = (E*)(smem + Cf::OFF_VT);
+    E* sV = (E*)(smem + Cf::OFF_V);
     E* sSt = (E*)(smem + Cf::OFF_ST);
     E* sP = (E*)(smem + Cf::OFF_P);
-    E* sTK = (E*)(smem + Cf::OFF_T);
-    E* sTV = sTK + C * LDC;
-    float* sA = (float*)(smem + Cf::OFF_U);
-    E* sUt = (E*)(smem + Cf::OFF_U);
-    E* sUd = sUt + BV * LDC;
     float* sX = (float*)(smem + Cf::OFF_X);
     float* sc = (float*)(smem + Cf::OFF_SC);
-    float* sc_g = sc;              // raw g_log
-    float* sc_b = sc + C;          // beta
+    float* sc_b = sc;              // beta
+    float* sc_eg = sc + C;         // e^gamma
     float* sc_gam = sc + 2 * C;    // gamma
-    float* sc_eg = sc + 3 * C;     // e^gamma
-    float* sc_bk = sc + 4 * C;     // beta e^gamma
-    float* sc_dl = sc + 5 * C;     // e^{gamma_C - gamma}
-    float* sc_misc = sc + 6 * C;   // [0] = e^{gamma_C}
+    float* sc_bk = sc + 3 * C;     // beta e^gamma
+    float* sc_dl = sc + 4 * C;     // e^{gamma_C - gamma}
+    float* sc_misc = sc + 5 * C;   // [0] = e^{gamma_C}
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -160,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
     E* ob = out + bh * (size_t)S * Dv + v0;
     float* sb = state + bh * (size_t)Dk * Dv + v0;
 
-    // ---- initial state: fp32 accumulators + LDS copy St[v][dk]
+    // ---- initial state: fp32 accumulators + LDS copy St[v][dk] (hi | lo)
     f32x4 accS[Cf::SPW];
 #pragma unroll
     for (int m = 0; m < Cf::SPW; ++m) {
@@ -174,21 +224,22 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
                 const int dk = 16 * tk + lr + e;
                 accS[m][e] = (dk < Dk && col < vcols) ? sb[(size_t)dk * Dv + col] : 0.f;
             }
-            store4(sSt + col * LDK + 16 * tk + lr, accS[m]);
+            store4<SP>(sSt + col * LDS2 + 16 * tk + lr, LO_DK, accS[m]);
         }
     }
 
     for (int c0 = 0; c0 < S; c0 += C) {
         __syncthreads();  // previous chunk (or the initial St) complete
 
-        // ---- P0: stage K (row-major and transposed), Q, V^T, g, beta
+        // ---- P0: stage K (row-major + transposed), Q, V; wave 0 also does
+        //      gamma = inclusive cumsum of g over the chunk and the scalars.
         for (int id = tid; id < C * DK / VE; id += THREADS) {
             const int t = id % C, d0 = (id / C) * VE;
             VecE x = {};
             if (d0 < Dk) x = *(const VecE*)(kb + (size_t)(c0 + t) * Dk + d0);
             *(VecE*)(sK + t * LDK + d0) = x;
 #pragma unroll
-            for (int e = 0; e < VE; ++e) sKt[(d0 + e) * LDC + t] = x[e];
+            for (int e = 0; e < VE; ++e) sKt[(d0 + e) * LDKT + t] = x[e];
         }
         for (int id = tid; id < C * DK / VE; id += THREADS) {
             const int d0 = (id % (DK / VE)) * VE, t = id / (DK / VE);
@@ -197,19 +248,14 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
             *(VecE*)(sQ + t * LDK + d0) = x;
         }
         for (int id = tid; id < C * BV / VE; id += THREADS) {
-            const int t = id % C, d0 = (id / C) * VE;
+            const int d0 = (id % (BV / VE)) * VE, t = id / (BV / VE);
             VecE x = {};
             if (d0 < vcols) x = *(const VecE*)(vb + (size_t)(c0 + t) * Dv + d0);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) sVt[(d0 + e) * LDC + t] = x[e];
+            *(VecE*)(sV + t * LDV + d0) = x;
         }
-        if (tid < C) sc_g[tid] = gb[c0 + tid];
-        else if (tid < 2 * C) sc_b[tid - C] = bb[c0 + tid - C];
-        __syncthreads();
-
-        // ---- P1: gamma = inclusive cumsum of g over the chunk (one wave)
         if (wave == 0) {
-            float x = (l < C) ? sc_g[l] : 0.f;
+            float x = (l < C) ? gb[c0 + l] : 0.f;
+            const float bt = (l < C) ? bb[c0 + l] : 0.f;
 #pragma unroll
             for (int off = 1; off < C; off <<= 1) {
                 const float y = __shfl_up(x, off);
@@ -218,18 +264,20 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
             const float gC = __shfl(x, C - 1);
             if (l < C) {
                 const float eg = __expf(x);
+                sc_b[l] = bt;
                 sc_gam[l] = x;
                 sc_eg[l] = eg;
-                sc_bk[l] = sc_b[l] * eg;
+                sc_bk[l] = bt * eg;
                 sc_dl[l] = __expf(gC - x);   // gC <= x: never overflows
             }
             if (l == 0) sc_misc[0] = __expf(gC);
         }
         __syncthreads();
 
-        // ---- P2: A = masked beta K K^T (fp32), P = masked Q K^T, and Q S0
-        //      Decay factors are formed as e^{gamma_r - gamma_s} only where
-        //      s <= r (a select, never a product with a masked value).
+        // ---- P1: A = masked beta K K^T (fp32), P = masked Q K^T (pair),
+        //      and, for owned tiles, K S0 and Q S0 (S0 as a pair).
+        //      Decay factors e^{gamma_r - gamma_s} are only used where s <= r
+        //      (a select, never a product with a masked value).
 #pragma unroll
         for (int m = 0; m < Cf::JPW; ++m) {
             const int job = wave + NW_ * m;
@@ -238,10 +286,8 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
                 int ti, tj;
                 tri_index(isQ ? job - Cf::NLT : job, ti, tj);
                 const E* Ab = isQ ? sQ : sK;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kk = 0; kk < DK; kk += KS)
-                    acc = M::mma(M::ld(Ab, LDK, 16 * ti, kk), M::ld(sK, LDK, 16 * tj, kk), acc);
+                f32x4 acc = mma_range<E, false, false>(zero4(), Ab, LDK, 16 * ti, 0, sK, LDK,
+                                                       16 * tj, 0, 0, DK);
                 const int s = 16 * tj + lc;
                 const float gs = sc_gam[s];
 #pragma unroll
@@ -249,30 +295,32 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
                     const int r = 16 * ti + lr + e;
                     const float dec = __expf(sc_gam[r] - gs);
                     if (!isQ) sA[r * LDF + s] = (s < r) ? sc_b[r] * dec * acc[e] : 0.f;
-                    else sP[r * LDC + s] = from_f32<E>((s <= r) ? dec * acc[e] : 0.f);
+                    else store1<SP>(sP + r * LDC2 + s, LO_C, (s <= r) ? dec * acc[e] : 0.f);
                 }
             }
         }
         for (int id = tid; id < C * C; id += THREADS) {   // zero the strictly-upper tiles of P
             const int r = id / C, s = id % C;
-            if ((s >> 4) > (r >> 4)) sP[r * LDC + s] = from_f32<E>(0.f);
+            if ((s >> 4) > (r >> 4)) store1<SP>(sP + r * LDC2 + s, LO_C, 0.f);
         }
-        f32x4 accO[Cf::OPW];
+        f32x4 accO[Cf::OPW], accR[Cf::OPW];
 #pragma unroll
         for (int m = 0; m < Cf::OPW; ++m) {
             const int id = wave + NW_ * m;
             accO[m] = zero4();
+            accR[m] = zero4();
             if (id < Cf::NO) {
                 const int ti = id / Cf::NVT, vj = id % Cf::NVT;
-#pragma unroll
-                for (int kk = 0; kk < DK; kk += KS)
-                    accO[m] = M::mma(M::ld(sQ, LDK, 16 * ti, kk), M::ld(sSt, LDK, 16 * vj, kk),
-                                     accO[m]);
+                accR[m] = mma_range<E, false, SP>(accR[m], sK, LDK, 16 * ti, 0, sSt, LDS2,
+                                                  16 * vj, LO_DK, 0, DK);
+                accO[m] = mma_range<E, false, SP>(accO[m], sQ, LDK, 16 * ti, 0, sSt, LDS2,
+                                                  16 * vj, LO_DK, 0, DK);
             }
         }
         __syncthreads();
 
-        // ---- P3a: 16x16 diagonal blocks of T by forward substitution (fp32)
+        // ---- P2a: 16x16 diagonal blocks of T by forward substitution (wave 0),
+        //      R = beta V - beta e^gamma (K S0) -> Rt pair (owners).
         if (wave == 0) {
             const int d = l >> 4, jc = l & 15;
             if (d < Cf::NT) {
@@ -290,9 +338,23 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
                 for (int r = 0; r < 16; ++r) Td[r * LDF + jc] = x[r];
             }
         }
+#pragma unroll
+        for (int m = 0; m < Cf::OPW; ++m) {
+            const int id = wave + NW_ * m;
+            if (id < Cf::NO) {
+                const int ti = id / Cf::NVT, vj = id % Cf::NVT;
+                const int vl = 16 * vj + lc, t0 = 16 * ti + lr;
+                f32x4 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    r[e] = sc_b[t0 + e] * to_f32(sV[(t0 + e) * LDV + vl]) -
+                           sc_bk[t0 + e] * accR[m][e];
+                store4<SP>(sRt + vl * LDC2 + t0, LO_C, r);
+            }
+        }
         __syncthreads();
 
-        // ---- P3b: doubling merges, T21 = -T22 (A21 T11), fp32 MFMA
+        // ---- P2b: doubling merges, T21 = -T22 (A21 T11), fp32 MFMA
 #pragma unroll
         for (int mb = 16; mb < C; mb *= 2) {
             const int nblk = C / (2 * mb);
@@ -326,66 +388,33 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
             __syncthreads();
         }
 
-        // ---- P3c: TK = T diag(beta e^gamma), TV = T diag(beta) in the operand type
+        // ---- P2c: T -> pair buffer in the operand type (upper triangle zero)
         for (int id = tid; id < C * C; id += THREADS) {
             const int r = id / C, s = id % C;
-            const float tv = (s <= r) ? sTf[r * LDF + s] : 0.f;
-            sTK[r * LDC + s] = from_f32<E>(tv * sc_bk[s]);
-            sTV[r * LDC + s] = from_f32<E>(tv * sc_b[s]);
+            store1<SP>(sT + r * LDC2 + s, LO_C, (s <= r) ? sTf[r * LDF + s] : 0.f);
         }
         __syncthreads();
 
-        // ---- P4: -W = -(TK K) into LDS; U~ = TV V in registers
-#pragma unroll
-        for (int m = 0; m < Cf::WPW; ++m) {
-            const int id = wave + NW_ * m;
-            if (id < Cf::NWT) {
-                const int ti = id / Cf::NKT, tk = id % Cf::NKT;
-                const int kend = ((16 * (ti + 1) + KS - 1) / KS) * KS;
-                f32x4 acc = zero4();
-                for (int s = 0; s < kend; s += KS)
-                    acc = M::mma(M::ld(sTK, LDC, 16 * ti, s), M::ld(sKt, LDC, 16 * tk, s), acc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sW[(16 * ti + lr + e) * LDK + 16 * tk + lc] = from_f32<E>(-acc[e]);
-            }
-        }
-        f32x4 accU[Cf::OPW];
-#pragma unroll
-        for (int m = 0; m < Cf::OPW; ++m) {
-            const int id = wave + NW_ * m;
-            accU[m] = zero4();
-            if (id < Cf::NO) {
-                const int ti = id / Cf::NVT, vj = id % Cf::NVT;
-                const int kend = ((16 * (ti + 1) + KS - 1) / KS) * KS;
-                for (int s = 0; s < kend; s += KS)
-                    accU[m] = M::mma(M::ld(sTV, LDC, 16 * ti, s), M::ld(sVt, LDC, 16 * vj, s),
-                                     accU[m]);
-            }
-        }
-        __syncthreads();
-
-        // ---- P5: U = U~ - W S0; store U^T and (diag(e^{gamma_C-gamma}) U)^T
+        // ---- P3: U = T R (owners) -> Ut pair, Ud = diag(e^{gamma_C-gamma}) U pair
 #pragma unroll
         for (int m = 0; m < Cf::OPW; ++m) {
             const int id = wave + NW_ * m;
             if (id < Cf::NO) {
                 const int ti = id / Cf::NVT, vj = id % Cf::NVT;
-#pragma unroll
-                for (int kk = 0; kk < DK; kk += KS)
-                    accU[m] = M::mma(M::ld(sW, LDK, 16 * ti, kk), M::ld(sSt, LDK, 16 * vj, kk),
-                                     accU[m]);
+                const int kend = ((16 * (ti + 1) + KS - 1) / KS) * KS;
+                const f32x4 u = mma_range<E, SP, SP>(zero4(), sT, LDC2, 16 * ti, LO_C, sRt, LDC2,
+                                                     16 * vj, LO_C, 0, kend);
                 const int vl = 16 * vj + lc, t0 = 16 * ti + lr;
-                store4(sUt + vl * LDC + t0, accU[m]);
+                store4<SP>(sUt + vl * LDC2 + t0, LO_C, u);
                 f32x4 ud;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ud[e] = accU[m][e] * sc_dl[t0 + e];
-                store4(sUd + vl * LDC + t0, ud);
+                for (int e = 0; e < 4; ++e) ud[e] = u[e] * sc_dl[t0 + e];
+                store4<SP>(sUd + vl * LDC2 + t0, LO_C, ud);
             }
         }
         __syncthreads();
 
-        // ---- P6: O = scale (e^gamma Q S0 + P U) -> out; S = e^{gamma_C} S0 + K^T Ud
+        // ---- P4: O = scale (e^gamma Q S0 + P U) -> out; S = e^{gamma_C} S0 + K^T Ud
 #pragma unroll
         for (int m = 0; m < Cf::OPW; ++m) {
             const int id = wave + NW_ * m;
@@ -394,9 +423,8 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) accO[m][e] *= sc_eg[16 * ti + lr + e];
                 const int kend = ((16 * (ti + 1) + KS - 1) / KS) * KS;
-                for (int s = 0; s < kend; s += KS)
-                    accO[m] = M::mma(M::ld(sP, LDC, 16 * ti, s), M::ld(sUt, LDC, 16 * vj, s),
-                                     accO[m]);
+                accO[m] = mma_range<E, SP, SP>(accO[m], sP, LDC2, 16 * ti, LO_C, sUt, LDC2,
+                                               16 * vj, LO_C, 0, kend);
                 const int col = 16 * vj + lc;
                 if (col < vcols) {
 #pragma unroll
@@ -414,11 +442,9 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
                 const int tk = id / Cf::NVT, vj = id % Cf::NVT;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) accS[m][e] *= egC;
-#pragma unroll
-                for (int t = 0; t < C; t += KS)
-                    accS[m] = M::mma(M::ld(sKt, LDC, 16 * tk, t), M::ld(sUd, LDC, 16 * vj, t),
-                                     accS[m]);
-                store4(sSt + (16 * vj + lc) * LDK + 16 * tk + lr, accS[m]);
+                accS[m] = mma_range<E, false, SP>(accS[m], sKt, LDKT, 16 * tk, 0, sUd, LDC2,
+                                                  16 * vj, LO_C, 0, C);
+                store4<SP>(sSt + (16 * vj + lc) * LDS2 + 16 * tk + lr, LO_DK, accS[m]);
             }
         }
     }
