@@ -1,60 +1,126 @@
-// gdn_mfma.h -- 16x16 matrix-core (MFMA) tile helpers for gfx950.
+// gdn_mfma.h -- matrix-core (MFMA) operand helpers for gfx950.
 //
-// Every product in the chunk kernel is built from 16x16 output tiles. Both
-// operands are read from LDS buffers stored "contraction-contiguous": the A
-// operand as A[m][k] and the B operand as Bt[n][k] (k contiguous), so one
-// fragment loader serves both sides.
+// All products are built from 16x16 fp32 output tiles contracted 32 deep.
+// The contraction index of a 32-deep step is split into two 16-blocks, and
+// lane l (group g = l/16) supplies the k values {4g .. 4g+3} of block 0 and
+// {16+4g .. 16+4g+3} of block 1. That is exactly the row set a lane holds in
+// the 16x16 fp32 accumulator layout (rows 4g + e, e = 0..3, column l%16), so
+// an accumulator tile pair can be fed back as the B operand of the next
+// product straight from registers, with no LDS round trip. A operands are
+// read from LDS with the same k mapping, either from a row-major [m][k]
+// buffer (two 8-byte reads per lane) or transposed from a row-major [k][m]
+// buffer (gfx950 LDS transpose reads).
 //
-// Lane layout of v_mfma_f32_16x16x32_bf16 (and of the fp32 16x16x4 form with
-// one element per lane), lane l = 0..63:
-//   A fragment: row (l % 16), contraction elements KPL*(l/16) .. +KPL-1
-//   B fragment: column (l % 16), the same contraction elements
-//   C/D tile:   4 floats, rows 4*(l/16) + e (e = 0..3), column (l % 16)
-// Any permutation of the contraction index that is the same for A and B gives
-// the same product, so only the row/column and C placements matter.
+// bf16: one v_mfma_f32_16x16x32_bf16 per step; computed operands are carried
+//       as a pair hi = bf16(x), lo = bf16(x - hi) and a product of pairs is
+//       hi*hi + hi*lo + lo*hi (about 16 significant bits).
+// fp32: eight v_mfma_f32_16x16x4f32 per step, one k value per lane each.
+//
+// Accumulator layout of a 16x16 tile (lane l, element e): row 4*(l/16) + e,
+// column l % 16.
 #pragma once
 
 #include "gdn_common.h"
 
 namespace gdn {
 
-template <typename E> struct Mfma;
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-template <> struct Mfma<bf16> {
-    static constexpr int KPL = 8;   // operand elements per lane
-    static constexpr int KS = 32;   // contraction length of one instruction
-    static constexpr int PAD = 8;   // LDS row padding (elements): 16-byte rows, no bank conflicts
-    typedef bf16x8 frag;
-    __device__ __forceinline__ static frag ld(const bf16* base, int ldm, int r0, int k0) {
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed LDS read: lanes j of a 16-lane group give the address of 4
+// consecutive elements of row j/4 (columns 4*(j%4)..+3) of a 4x16 block; lane
+// i receives column i of the block (rows 0..3).
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(const_cast<bf16*>(p)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Wave-local ordering of LDS accesses (no cross-wave barrier).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+}
+
+template <typename E> struct Op;
+
+template <> struct Op<bf16> {
+    static constexpr bool SPLIT = true;
+    typedef bf16x8 F;   // one 32-deep operand fragment
+
+    // A[r0 + l%16][k0 + {4g..4g+3, 16+4g..16+4g+3}] from row-major A.
+    __device__ __forceinline__ static F lda(const bf16* A, int ld, int r0, int k0) {
         const int l = lane_id();
-        return *(const bf16x8*)(base + (r0 + (l & 15)) * ldm + k0 + 8 * (l >> 4));
+        const bf16* p = A + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
+        const bf16x4 a = *(const bf16x4*)p;
+        const bf16x4 b = *(const bf16x4*)(p + 16);
+        return F{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
-    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    // (X^T)[m0 + l%16][k0 + ...] for row-major X[k][m], via transposed reads.
+    __device__ __forceinline__ static F lda_t(const bf16* X, int ld, int m0, int k0) {
+        const int l = lane_id(), g = l >> 4, j = l & 15;
+        const bf16* p = X + (k0 + 4 * g + (j >> 2)) * ld + m0 + 4 * (j & 3);
+        const bf16x4 a = lds_read_tr(p);
+        const bf16x4 b = lds_read_tr(p + 16 * ld);
+        return F{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+    // B fragment from two accumulator tiles (k block 0 = x0 rows, block 1 = x1 rows).
+    __device__ __forceinline__ static void split(f32x4 x0, f32x4 x1, F& hi, F& lo) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            hi[e] = (bf16)x0[e];
+            hi[4 + e] = (bf16)x1[e];
+            lo[e] = (bf16)(x0[e] - (float)hi[e]);
+            lo[4 + e] = (bf16)(x1[e] - (float)hi[4 + e]);
+        }
+    }
+    __device__ __forceinline__ static f32x4 mma(F a, F b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
 
-template <> struct Mfma<float> {
-    static constexpr int KPL = 1;
-    static constexpr int KS = 4;
-    static constexpr int PAD = 4;   // row stride = 4 (mod 64) words: (row, k) -> distinct banks
-    typedef float frag;
-    __device__ __forceinline__ static frag ld(const float* base, int ldm, int r0, int k0) {
+struct F8 { float v[8]; };
+
+template <> struct Op<float> {
+    static constexpr bool SPLIT = false;
+    typedef F8 F;
+
+    __device__ __forceinline__ static F lda(const float* A, int ld, int r0, int k0) {
         const int l = lane_id();
-        return base[(r0 + (l & 15)) * ldm + k0 + (l >> 4)];
+        const float* p = A + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
+        F a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a.v[e] = p[e]; a.v[4 + e] = p[16 + e]; }
+        return a;
     }
-    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    __device__ __forceinline__ static F lda_t(const float* X, int ld, int m0, int k0) {
+        const int l = lane_id();
+        const float* p = X + (k0 + 4 * (l >> 4)) * ld + m0 + (l & 15);
+        F a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a.v[e] = p[e * ld]; a.v[4 + e] = p[(16 + e) * ld]; }
+        return a;
+    }
+    __device__ __forceinline__ static void split(f32x4 x0, f32x4 x1, F& hi, F& lo) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { hi.v[e] = x0[e]; hi.v[4 + e] = x1[e]; }
+        lo = hi;  // unused on the fp32 path
+    }
+    __device__ __forceinline__ static f32x4 mma(const F& a, const F& b, f32x4 c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], c, 0, 0, 0);
+        return c;
     }
 };
 
-// fp32 B operand read from a row-major B[k][n] buffer (used by the fp32
-// triangular-inverse merges, where no transposed copy exists).
-__device__ __forceinline__ float ld_b_rowmajor(const float* base, int ldm, int k0, int n0) {
+// fp32 16x16x4 MFMA with both operands read from row-major fp32 LDS buffers:
+// A[r0 + l%16][k0 + l/16], B[k0 + l/16][n0 + l%16].
+__device__ __forceinline__ f32x4 mma_f32_rm(f32x4 c, const float* A, int lda, int r0,
+                                            const float* B, int ldb, int n0, int k0) {
     const int l = lane_id();
-    return base[(k0 + (l >> 4)) * ldm + n0 + (l & 15)];
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(A[(r0 + (l & 15)) * lda + k0 + (l >> 4)],
+                                                B[(k0 + (l >> 4)) * ldb + n0 + (l & 15)], c,
+                                                0, 0, 0);
 }
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 }  // namespace gdn

@@ -14,191 +14,134 @@
 //   S1 = e^{gamma_C} S0 + K^T diag(e^{gamma_C - gamma}) U
 //
 // derived from the token recurrence S_t = e^{g_t} S_{t-1} + beta_t k_t
-// (v_t - e^{g_t} S_{t-1}^T k_t)^T, o_t = scale S_t^T q_t: unrolling the chunk
-// gives (I + A) U = diag(beta) V - diag(beta e^gamma) K S0. The right-hand side
-// R is formed in fp32 before anything is rounded, so the cancellation between
-// new values and the state's prediction happens at full precision.
+// (v_t - e^{g_t} S_{t-1}^T k_t)^T, o_t = scale S_t^T q_t: unrolling a chunk
+// gives (I + A) U = diag(beta) V - diag(beta e^gamma) K S0. R is formed in
+// fp32 before any rounding, so the cancellation between new values and the
+// state's prediction happens at full precision.
 //
-// Design (one fused kernel, no HBM intermediates): one workgroup of NW waves
-// owns one (batch, value head, BV-wide slice of Dv) and walks the chunks of
-// its sequence in order, holding its [Dk x BV] slice of the fp32 state in
-// MFMA accumulator registers throughout. Per chunk only q, k, v, g, beta are
-// read and out is written, so HBM traffic is the algorithmic minimum. The
-// state-independent work (gamma, A, T, the masked Q K^T) is recomputed by each
-// Dv slice; BV is chosen per launch so the grid fills the 256 compute units.
-// Products are 16x16-tile MFMAs from LDS. On the bf16 path every operand that
-// is not an exact input (S, T, R, P, U) is carried as a pair of bf16 numbers
-// hi + lo (hi = bf16(x), lo = bf16(x - hi)), and a product of two such values
-// is hi*hi + hi*lo + lo*hi, so results keep about 16 significant bits; q, k, v
-// are exact in bf16 and need one term. The triangular inverse is fp32: 16x16
-// diagonal blocks by forward substitution (one lane per column), then
-// doubling merges T21 = -T22 (A21 T11) on fp32 MFMA.
+// One workgroup owns one (batch, value head, BV-wide slice of Dv) and walks
+// the C = 32 token chunks of its sequence. Its waves have fixed roles and
+// meet at one barrier per chunk:
+//
+//  * consumer waves, one per 16-column strip of the slice, keep their
+//    [Dk x 16] slice of the fp32 state in MFMA accumulator registers for the
+//    whole sequence. For chunk i they compute K S0 and Q S0 (state fed from
+//    registers as the B operand), R, U = T R, O = e^gamma Q S0 + P U and the
+//    state update K^T (dl U) -- every intermediate stays in registers; LDS is
+//    only read for K, Q, V, T and P of the chunk;
+//  * the inverse wave builds A and T = (I + A)^{-1} for chunk i+1 (fp32:
+//    16x16 diagonal blocks by forward substitution, one lane per column, then
+//    the merge T21 = -T22 (A21 T11) on fp32 MFMA);
+//  * the P wave builds P = Q K^T (.) Mincl for chunk i+1;
+//  * two stager waves move chunk i+2 from registers into LDS (with gamma and
+//    the per-token decay scalars) and prefetch chunk i+3 from HBM, so every
+//    HBM load has a chunk's worth of time to land.
+//
+// LDS holds three input slots (chunks i, i+1, i+2) and two T/P buffers.
+// The state-independent work of a chunk therefore never sits on the
+// sequential path. HBM traffic is the algorithmic minimum: q, k, v, g, beta
+// read once per slice, out written once, the state read and written once.
+// On the bf16 path every computed operand (S, T, R, P, U) is carried as a
+// hi/lo bf16 pair (see gdn_mfma.h), so products keep about 16 bits.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 #include "gdn_mfma.h"
 
 namespace gdn {
 
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-
 template <typename E> struct Vec16;  // one 16-byte vector of E
 template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int N = 8; };
 template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
 
-// Writes 4 consecutive values as the operand type. With SPLIT the low parts
-// (x - hi) go to p + lo_off.
+// Stores x (and, on the bf16 path, its low part x - bf16(x) at p + lo_off).
 template <bool SPLIT>
-__device__ __forceinline__ void store4(bf16* p, int lo_off, f32x4 x) {
-    bf16x4 hi = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-    *(bf16x4*)p = hi;
-    if constexpr (SPLIT) {
-        bf16x4 lo = {(bf16)(x[0] - (float)hi[0]), (bf16)(x[1] - (float)hi[1]),
-                     (bf16)(x[2] - (float)hi[2]), (bf16)(x[3] - (float)hi[3])};
-        *(bf16x4*)(p + lo_off) = lo;
-    }
-}
-template <bool SPLIT>
-__device__ __forceinline__ void store4(float* p, int, f32x4 x) { *(f32x4*)p = x; }
-
-template <bool SPLIT>
-__device__ __forceinline__ void store1(bf16* p, int lo_off, float x) {
+__device__ __forceinline__ void store_pair(bf16* p, int lo_off, float x) {
     const bf16 hi = (bf16)x;
     p[0] = hi;
     if constexpr (SPLIT) p[lo_off] = (bf16)(x - (float)hi);
 }
 template <bool SPLIT>
-__device__ __forceinline__ void store1(float* p, int, float x) { p[0] = x; }
+__device__ __forceinline__ void store_pair(float* p, int, float x) { p[0] = x; }
 
-// Linear index of a lower-triangular 16x16 tile (row-major over i >= j) -> (i, j).
-__device__ __forceinline__ void tri_index(int lt, int& i, int& j) {
-    i = 0;
-    while (lt > i) { lt -= i + 1; ++i; }
-    j = lt;
-}
-
-template <typename E, int C, int DK, int BV, int NW>
-struct PrefillCfg {
-    using M = Mfma<E>;
-    static constexpr bool SPLIT = sizeof(E) == 2;   // hi/lo operand pairs on the bf16 path
-    static constexpr int NP = SPLIT ? 2 : 1;        // parts per pair buffer row
+template <typename E, int C, int DK, int BV>
+struct PipeCfg {
+    using O = Op<E>;
+    static constexpr bool SP = O::SPLIT;
     static constexpr int ES = (int)sizeof(E);
     static constexpr int VE = Vec16<E>::N;
-    static constexpr int PAD = M::PAD;
-    static constexpr int LDK = DK + PAD;            // K, Q rows [t][dk]
-    static constexpr int LDKT = C + PAD;            // Kt rows [dk][t]
-    static constexpr int LDV = BV + PAD;            // V rows [t][v]
-    static constexpr int LDS2 = NP * DK + PAD;      // St pair rows [v][hi dk | lo dk]
-    static constexpr int LDC2 = NP * C + PAD;       // P, T, Rt, Ut, Ud pair rows [x][hi t | lo t]
-    static constexpr int LDF = C + 4;               // fp32 [t][s] rows (A, Tf)
+    static constexpr int NCW = BV / 16;            // consumer waves (16 value columns each)
+    static constexpr int W_T = NCW;                // inverse wave
+    static constexpr int W_P = NCW + 1;            // P wave
+    static constexpr int W_S = NCW + 2;            // first of two stager waves
+    static constexpr int NW = NCW + 4;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int NSLOT = 3;
+    static constexpr int PADE = SP ? 8 : 4;        // row padding (elements): 16-byte rows
+    static constexpr int LDK = DK + PADE;          // K, Q rows [t][dk]
+    static constexpr int LDV = BV + PADE;          // V rows [t][v]
+    static constexpr int LDP = (SP ? 2 : 1) * C + PADE;  // T, P rows [t][hi s | lo s]
+    static constexpr int LDF = C + 4;              // fp32 A, T rows
+    static constexpr int LDX = 16 + 4;             // fp32 merge scratch rows
     static constexpr int NT = C / 16;
     static constexpr int NKT = DK / 16;
-    static constexpr int NVT = BV / 16;
-    static constexpr int NLT = NT * (NT + 1) / 2;
-    static constexpr int NO = NT * NVT;             // out / U / R tiles
-    static constexpr int NS = NKT * NVT;            // state tiles
-    static constexpr int THREADS = NW * 64;
-    static constexpr int OPW = (NO + NW - 1) / NW;
-    static constexpr int SPW = (NS + NW - 1) / NW;
-    static constexpr int JPW = (2 * NLT + NW - 1) / NW;
-    // Buffer sizes (bytes)
+    static constexpr int NKS = DK / 32;
+    static constexpr int NVK = C * DK / VE / 64;   // 16-byte vectors per stager lane: K (and Q)
+    static constexpr int NVV = C * BV / VE / 64;   //                                  V
+    // LDS layout (bytes)
     static constexpr int SZ_K = C * LDK * ES;
-    static constexpr int SZ_KT = DK * LDKT * ES;
     static constexpr int SZ_V = C * LDV * ES;
-    static constexpr int SZ_ST = BV * LDS2 * ES;
-    static constexpr int SZ_PC = C * LDC2 * ES;     // C-row pair buffer (P, T)
-    static constexpr int SZ_PV = BV * LDC2 * ES;    // BV-row pair buffer (Rt, Ut, Ud)
-    static constexpr int SZ_F = C * LDF * 4;
-    static constexpr int SZ_X = (C / 2) * (C / 2 + 4) * 4;
     static constexpr int SZ_SC = 8 * C * 4;
-    // Regions; buffers sharing a region have disjoint lifetimes within a chunk:
-    //   R1: K, Q (staging .. K S0 / Q S0)     -> T pair, Rt pair
-    //   R2: A, Tf (K K^T .. merges)           -> Ut pair, Ud pair
-    static constexpr int SZ_R1 = cmax(2 * SZ_K, SZ_PC + SZ_PV);
-    static constexpr int SZ_R2 = cmax(2 * SZ_F, 2 * SZ_PV);
-    static constexpr int OFF_R1 = 0;
-    static constexpr int OFF_R2 = OFF_R1 + SZ_R1;
-    static constexpr int OFF_KT = OFF_R2 + SZ_R2;
-    static constexpr int OFF_V = OFF_KT + SZ_KT;
-    static constexpr int OFF_ST = OFF_V + SZ_V;
-    static constexpr int OFF_P = OFF_ST + SZ_ST;
-    static constexpr int OFF_X = OFF_P + SZ_PC;
-    static constexpr int OFF_SC = OFF_X + SZ_X;
-    static constexpr int LDS_BYTES = OFF_SC + SZ_SC;
-    static_assert(LDS_BYTES <= 160 * 1024, "chunk tiles exceed the 160 KiB LDS of a CU");
-    static_assert(C % M::KS == 0 && DK % M::KS == 0, "tile sizes must match the MFMA depth");
-    static_assert(C == 32 || C == 64, "chunk must be 32 or 64");
-    static_assert((SZ_K | SZ_KT | SZ_V | SZ_ST | SZ_PC | SZ_PV | SZ_F | SZ_X) % 16 == 0,
-                  "LDS buffers must stay 16-byte aligned");
+    static constexpr int OFF_SK = 0, OFF_SQ = SZ_K, OFF_SV = 2 * SZ_K, OFF_SSC = 2 * SZ_K + SZ_V;
+    static constexpr int SZ_SLOT = 2 * SZ_K + SZ_V + SZ_SC;
+    static constexpr int SZ_TP = C * LDP * ES;
+    static constexpr int SZ_F = C * LDF * 4;
+    static constexpr int SZ_X = 16 * LDX * 4;
+    static constexpr int OFF_T = NSLOT * SZ_SLOT;
+    static constexpr int OFF_P = OFF_T + 2 * SZ_TP;
+    static constexpr int OFF_A = OFF_P + 2 * SZ_TP;
+    static constexpr int OFF_TF = OFF_A + SZ_F;
+    static constexpr int OFF_X = OFF_TF + SZ_F;
+    static constexpr int LDS_BYTES = OFF_X + SZ_X;
+    // scalar arrays inside a slot (floats): gamma, e^gamma, beta, beta e^gamma,
+    // e^{gamma_C - gamma}, [0] = e^{gamma_C}
+    static constexpr int SC_GAM = 0, SC_EG = C, SC_B = 2 * C, SC_BK = 3 * C, SC_DL = 4 * C,
+                         SC_EGC = 5 * C;
+
+    static_assert(C == 32, "the pipeline is laid out for 32-token chunks");
+    static_assert(DK % 32 == 0 && BV % 16 == 0 && BV <= 64, "tile sizes");
+    static_assert((C * DK / VE) % 64 == 0 && (C * BV / VE) % 64 == 0, "stager vector split");
+    static_assert((SZ_K | SZ_V | SZ_SC | SZ_TP | SZ_F | SZ_X) % 16 == 0, "16-byte LDS alignment");
+    static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KiB LDS of a CU");
 };
 
-// acc += A B over contraction range [k0, k1), both operands contraction-
-// contiguous in LDS. A pair operand has its low part at +lo_off elements in
-// the same row. Terms: hi*hi (+ hi*lo if B is a pair) (+ lo*hi if A is a pair).
-template <typename E, bool PA, bool PB>
-__device__ __forceinline__ f32x4 mma_range(f32x4 acc, const E* A, int lda, int ra, int alo,
-                                           const E* B, int ldb, int rb, int blo, int k0, int k1)
-{
-    using M = Mfma<E>;
-    for (int k = k0; k < k1; k += M::KS) {
-        const auto ah = M::ld(A, lda, ra, k);
-        const auto bh = M::ld(B, ldb, rb, k);
-        if constexpr (PB) acc = M::mma(ah, M::ld(B, ldb, rb, k + blo), acc);
-        if constexpr (PA) acc = M::mma(M::ld(A, lda, ra, k + alo), bh, acc);
-        acc = M::mma(ah, bh, acc);
-    }
-    return acc;
-}
-
-template <typename E, int C, int DK, int BV, int NW>
-__global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
+template <typename E, int C, int DK, int BV>
+__global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ g_log, const float* __restrict__ beta, float scale,
     float* __restrict__ state, E* __restrict__ out,
     int Hk, int Hv, int S, int Dk, int Dv, int nvt)
 {
-    using Cf = PrefillCfg<E, C, DK, BV, NW>;
-    using M = Mfma<E>;
+    using Cf = PipeCfg<E, C, DK, BV>;
+    using O = typename Cf::O;
+    using F = typename O::F;
     using VecE = typename Vec16<E>::type;
-    constexpr bool SP = Cf::SPLIT;
-    constexpr int VE = Cf::VE, LDK = Cf::LDK, LDKT = Cf::LDKT, LDV = Cf::LDV;
-    constexpr int LDS2 = Cf::LDS2, LDC2 = Cf::LDC2, LDF = Cf::LDF, NW_ = NW;
-    constexpr int THREADS = Cf::THREADS, KS = M::KS;
-    constexpr int LO_C = C, LO_DK = DK;             // offsets of the low parts in pair rows
+    constexpr bool SP = Cf::SP;
+    constexpr int VE = Cf::VE, LDK = Cf::LDK, LDV = Cf::LDV, LDP = Cf::LDP, LDF = Cf::LDF;
+    constexpr int LDX = Cf::LDX, NT = Cf::NT, NKT = Cf::NKT, NKS = Cf::NKS;
 
     __shared__ __attribute__((aligned(16))) char smem[Cf::LDS_BYTES];
-    E* sK = (E*)(smem + Cf::OFF_R1);
-    E* sQ = (E*)(smem + Cf::OFF_R1 + Cf::SZ_K);
-    E* sT = (E*)(smem + Cf::OFF_R1);                       // after K/Q are dead
-    E* sRt = (E*)(smem + Cf::OFF_R1 + Cf::SZ_PC);
-    float* sA = (float*)(smem + Cf::OFF_R2);
-    float* sTf = (float*)(smem + Cf::OFF_R2 + Cf::SZ_F);
-    E* sUt = (E*)(smem + Cf::OFF_R2);                      // after A/Tf are dead
-    E* sUd = (E*)(smem + Cf::OFF_R2 + Cf::SZ_PV);
-    E* sKt = (E*)(smem + Cf::OFF_KT);
-    E* sV = (E*)(smem + Cf::OFF_V);
-    E* sSt = (E*)(smem + Cf::OFF_ST);
-    E* sP = (E*)(smem + Cf::OFF_P);
-    float* sX = (float*)(smem + Cf::OFF_X);
-    float* sc = (float*)(smem + Cf::OFF_SC);
-    float* sc_b = sc;              // beta
-    float* sc_eg = sc + C;         // e^gamma
-    float* sc_gam = sc + 2 * C;    // gamma
-    float* sc_bk = sc + 3 * C;     // beta e^gamma
-    float* sc_dl = sc + 4 * C;     // e^{gamma_C - gamma}
-    float* sc_misc = sc + 5 * C;   // [0] = e^{gamma_C}
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int l = tid & 63;
-    const int lc = l & 15;          // column of this lane in a 16x16 C tile
+    const int wave = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63;
+    const int lc = l & 15;          // column of this lane in a 16x16 accumulator tile
     const int lr = 4 * (l >> 4);    // first of its 4 rows
 
-    // blockIdx -> (v slice, value head, batch)
+    // blockIdx -> (value slice, value head, batch)
     int bid = blockIdx.x;
     const int vt = bid % nvt; bid /= nvt;
     const int h = bid % Hv;
     const int b = bid / Hv;
-    const int j = h / (Hv / Hk);
+    const int j = h / (Hv / Hk);               // GQA: contiguous groups of Hv/Hk
     const int v0 = vt * BV;
     const int vcols = min(BV, Dv - v0);
     const size_t bh = (size_t)b * Hv + h;
@@ -209,275 +152,334 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(
     const float* bb = beta + bh * (size_t)S;
     E* ob = out + bh * (size_t)S * Dv + v0;
     float* sb = state + bh * (size_t)Dk * Dv + v0;
+    const int NC = S / C;
 
-    // ---- initial state: fp32 accumulators + LDS copy St[v][dk] (hi | lo)
-    f32x4 accS[Cf::SPW];
+    auto slot_ptr = [&](int c) { return smem + (c % Cf::NSLOT) * Cf::SZ_SLOT; };
+
+    // ------------------------------------------------------------ stagers
+    // Two stager waves split each chunk: half 0 moves K, g and beta, half 1
+    // moves Q and V. A chunk's loads are issued one chunk ahead of its store.
+    const int half = wave - Cf::W_S;           // 0 or 1 on the stager waves
+    VecE rk[Cf::NVK], rv[Cf::NVV];             // half 0: K rows; half 1: Q rows (rk) and V (rv)
+    float rg = 0.f, rb = 0.f;
+    auto stage_load = [&](int c) {
+        const int c0 = c * C;
+        const E* src = half == 0 ? kb : qb;
 #pragma unroll
-    for (int m = 0; m < Cf::SPW; ++m) {
-        const int id = wave + NW_ * m;
-        accS[m] = zero4();
-        if (id < Cf::NS) {
-            const int tk = id / Cf::NVT, vj = id % Cf::NVT;
-            const int col = 16 * vj + lc;
+        for (int n = 0; n < Cf::NVK; ++n) {
+            const int id = l + 64 * n, t = id / (DK / VE), d0 = (id % (DK / VE)) * VE;
+            rk[n] = VecE{};
+            if (d0 < Dk) rk[n] = *(const VecE*)(src + (size_t)(c0 + t) * Dk + d0);
+        }
+        if (half == 0) {
+            if (l < C) { rg = gb[c0 + l]; rb = bb[c0 + l]; }
+        } else {
+#pragma unroll
+            for (int n = 0; n < Cf::NVV; ++n) {
+                const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
+                rv[n] = VecE{};
+                if (d0 < vcols) rv[n] = *(const VecE*)(vb + (size_t)(c0 + t) * Dv + d0);
+            }
+        }
+    };
+    auto stage_store = [&](int c) {
+        char* slot = slot_ptr(c);
+        E* dst = (E*)(slot + (half == 0 ? Cf::OFF_SK : Cf::OFF_SQ));
+#pragma unroll
+        for (int n = 0; n < Cf::NVK; ++n) {
+            const int id = l + 64 * n, t = id / (DK / VE), d0 = (id % (DK / VE)) * VE;
+            *(VecE*)(dst + t * LDK + d0) = rk[n];
+        }
+        if (half == 1) {
+            E* sV = (E*)(slot + Cf::OFF_SV);
+#pragma unroll
+            for (int n = 0; n < Cf::NVV; ++n) {
+                const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
+                *(VecE*)(sV + t * LDV + d0) = rv[n];
+            }
+            return;
+        }
+        // gamma = inclusive cumulative sum of g over the chunk, and the scalars
+        float* sc = (float*)(slot + Cf::OFF_SSC);
+        float x = (l < C) ? rg : 0.f;
+#pragma unroll
+        for (int off = 1; off < C; off <<= 1) {
+            const float y = __shfl_up(x, off);
+            if (l >= off) x += y;
+        }
+        const float gC = __shfl(x, C - 1);
+        if (l < C) {
+            const float eg = __expf(x);
+            sc[Cf::SC_GAM + l] = x;
+            sc[Cf::SC_EG + l] = eg;
+            sc[Cf::SC_B + l] = rb;
+            sc[Cf::SC_BK + l] = rb * eg;
+            sc[Cf::SC_DL + l] = __expf(gC - x);   // gC <= x: never overflows
+        }
+        if (l == 0) sc[Cf::SC_EGC] = __expf(gC);
+    };
+
+    // ------------------------------------------------------------ inverse wave
+    auto build_T = [&](int c) {
+        const char* slot = slot_ptr(c);
+        const E* sK = (const E*)(slot + Cf::OFF_SK);
+        const float* sc = (const float*)(slot + Cf::OFF_SSC);
+        float* sA = (float*)(smem + Cf::OFF_A);
+        float* sTf = (float*)(smem + Cf::OFF_TF);
+        float* sX = (float*)(smem + Cf::OFF_X);
+        E* Tp = (E*)(smem + Cf::OFF_T + (c & 1) * Cf::SZ_TP);
+        // A = diag(beta) (K K^T) (.) Mstrict on the three lower 16x16 tiles.
+        // Decay factors e^{gamma_r - gamma_s} are only used where s < r.
+#pragma unroll
+        for (int tt = 0; tt < 3; ++tt) {
+            const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int m = 0; m < NKS; ++m)
+                acc = O::mma(O::lda(sK, LDK, 16 * ti, 32 * m), O::lda(sK, LDK, 16 * tj, 32 * m), acc);
+            const int s = 16 * tj + lc;
+            const float gs = sc[Cf::SC_GAM + s];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int dk = 16 * tk + lr + e;
-                accS[m][e] = (dk < Dk && col < vcols) ? sb[(size_t)dk * Dv + col] : 0.f;
+                const int r = 16 * ti + lr + e;
+                const float dec = __expf(sc[Cf::SC_GAM + r] - gs);
+                sA[r * LDF + s] = (s < r) ? sc[Cf::SC_B + r] * dec * acc[e] : 0.f;
             }
-            store4<SP>(sSt + col * LDS2 + 16 * tk + lr, LO_DK, accS[m]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wave_lds_fence();
+        // Diagonal 16x16 blocks: lane (d, jc) solves column jc of block d by
+        // forward substitution, x_r = [r == jc] - sum_{s<r} A[r][s] x_s, in
+        // fp32, one row of A at a time (scheduling barriers keep the rows
+        // from all being loaded at once).
+        if (l < 32) {
+            const int d = l >> 4, jc = l & 15;
+            const float* Ad = sA + (16 * d) * LDF + 16 * d;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float a[16];
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const f32x4 w = *(const f32x4*)(Ad + r * LDF + 4 * c4);
+                    a[4 * c4] = w[0]; a[4 * c4 + 1] = w[1]; a[4 * c4 + 2] = w[2]; a[4 * c4 + 3] = w[3];
+                }
+                float acc = (r == jc) ? 1.f : 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < r; ++s2) acc -= a[s2] * x[s2];
+                x[r] = acc;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float* Td = sTf + (16 * d) * LDF + 16 * d;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Td[r * LDF + jc] = x[r];
+        }
+        wave_lds_fence();
+        // Merge: T21 = -T22 (A21 T11)
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) acc = mma_f32_rm(acc, sA, LDF, 16, sTf, LDF, 0, k0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sX[(lr + e) * LDX + lc] = acc[e];
+        wave_lds_fence();
+        acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) acc = mma_f32_rm(acc, sTf + 16, LDF, 16, sX, LDX, 0, k0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sTf[(16 + lr + e) * LDF + lc] = -acc[e];
+        wave_lds_fence();
+        // T -> operand buffer (upper triangle zero)
+#pragma unroll
+        for (int n = 0; n < C * C / 64; ++n) {
+            const int id = l + 64 * n, r = id / C, s = id % C;
+            store_pair<SP>(Tp + r * LDP + s, C, (s <= r) ? sTf[r * LDF + s] : 0.f);
+        }
+    };
+
+    // ------------------------------------------------------------ P wave
+    auto build_P = [&](int c) {
+        const char* slot = slot_ptr(c);
+        const E* sK = (const E*)(slot + Cf::OFF_SK);
+        const E* sQ = (const E*)(slot + Cf::OFF_SQ);
+        const float* sc = (const float*)(slot + Cf::OFF_SSC);
+        E* Pp = (E*)(smem + Cf::OFF_P + (c & 1) * Cf::SZ_TP);
+#pragma unroll
+        for (int tt = 0; tt < 3; ++tt) {
+            const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int m = 0; m < NKS; ++m)
+                acc = O::mma(O::lda(sQ, LDK, 16 * ti, 32 * m), O::lda(sK, LDK, 16 * tj, 32 * m), acc);
+            const int s = 16 * tj + lc;
+            const float gs = sc[Cf::SC_GAM + s];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * ti + lr + e;
+                const float dec = __expf(sc[Cf::SC_GAM + r] - gs);
+                store_pair<SP>(Pp + r * LDP + s, C, (s <= r) ? dec * acc[e] : 0.f);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {   // the upper 16x16 tile is zero
+            const int id = l + 64 * n;
+            store_pair<SP>(Pp + (id >> 4) * LDP + 16 + (id & 15), C, 0.f);
+        }
+    };
+
+    // ------------------------------------------------------------ consumers
+    const int vl = 16 * wave + lc;             // column of this lane within the slice
+    const bool vok = wave < Cf::NCW && vl < vcols;
+    f32x4 accS[NKT];                           // state rows 16 kt + lr + e, column vl
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int dk = 16 * kt + lr + e;
+            accS[kt][e] = (vok && dk < Dk) ? sb[(size_t)dk * Dv + vl] : 0.f;
         }
     }
-
-    for (int c0 = 0; c0 < S; c0 += C) {
-        __syncthreads();  // previous chunk (or the initial St) complete
-
-        // ---- P0: stage K (row-major + transposed), Q, V; wave 0 also does
-        //      gamma = inclusive cumsum of g over the chunk and the scalars.
-        for (int id = tid; id < C * DK / VE; id += THREADS) {
-            const int t = id % C, d0 = (id / C) * VE;
-            VecE x = {};
-            if (d0 < Dk) x = *(const VecE*)(kb + (size_t)(c0 + t) * Dk + d0);
-            *(VecE*)(sK + t * LDK + d0) = x;
+    auto consume = [&](int i) {
+        const char* slot = slot_ptr(i);
+        const E* sK = (const E*)(slot + Cf::OFF_SK);
+        const E* sQ = (const E*)(slot + Cf::OFF_SQ);
+        const E* sV = (const E*)(slot + Cf::OFF_SV);
+        const float* sc = (const float*)(slot + Cf::OFF_SSC);
+        const E* Tp = (const E*)(smem + Cf::OFF_T + (i & 1) * Cf::SZ_TP);
+        const E* Pp = (const E*)(smem + Cf::OFF_P + (i & 1) * Cf::SZ_TP);
+        const int c0 = i * C;
+        // K S0 and Q S0 with S0 from registers
+        f32x4 ks[NT], qs[NT];
 #pragma unroll
-            for (int e = 0; e < VE; ++e) sKt[(d0 + e) * LDKT + t] = x[e];
-        }
-        for (int id = tid; id < C * DK / VE; id += THREADS) {
-            const int d0 = (id % (DK / VE)) * VE, t = id / (DK / VE);
-            VecE x = {};
-            if (d0 < Dk) x = *(const VecE*)(qb + (size_t)(c0 + t) * Dk + d0);
-            *(VecE*)(sQ + t * LDK + d0) = x;
-        }
-        for (int id = tid; id < C * BV / VE; id += THREADS) {
-            const int d0 = (id % (BV / VE)) * VE, t = id / (BV / VE);
-            VecE x = {};
-            if (d0 < vcols) x = *(const VecE*)(vb + (size_t)(c0 + t) * Dv + d0);
-            *(VecE*)(sV + t * LDV + d0) = x;
-        }
-        if (wave == 0) {
-            float x = (l < C) ? gb[c0 + l] : 0.f;
-            const float bt = (l < C) ? bb[c0 + l] : 0.f;
+        for (int ti = 0; ti < NT; ++ti) { ks[ti] = zero4(); qs[ti] = zero4(); }
 #pragma unroll
-            for (int off = 1; off < C; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (l >= off) x += y;
-            }
-            const float gC = __shfl(x, C - 1);
-            if (l < C) {
-                const float eg = __expf(x);
-                sc_b[l] = bt;
-                sc_gam[l] = x;
-                sc_eg[l] = eg;
-                sc_bk[l] = bt * eg;
-                sc_dl[l] = __expf(gC - x);   // gC <= x: never overflows
-            }
-            if (l == 0) sc_misc[0] = __expf(gC);
-        }
-        __syncthreads();
-
-        // ---- P1: A = masked beta K K^T (fp32), P = masked Q K^T (pair),
-        //      and, for owned tiles, K S0 and Q S0 (S0 as a pair).
-        //      Decay factors e^{gamma_r - gamma_s} are only used where s <= r
-        //      (a select, never a product with a masked value).
+        for (int m = 0; m < NKS; ++m) {
+            F sh, sl;
+            O::split(accS[2 * m], accS[2 * m + 1], sh, sl);
 #pragma unroll
-        for (int m = 0; m < Cf::JPW; ++m) {
-            const int job = wave + NW_ * m;
-            if (job < 2 * Cf::NLT) {
-                const bool isQ = job >= Cf::NLT;
-                int ti, tj;
-                tri_index(isQ ? job - Cf::NLT : job, ti, tj);
-                const E* Ab = isQ ? sQ : sK;
-                f32x4 acc = mma_range<E, false, false>(zero4(), Ab, LDK, 16 * ti, 0, sK, LDK,
-                                                       16 * tj, 0, 0, DK);
-                const int s = 16 * tj + lc;
-                const float gs = sc_gam[s];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * ti + lr + e;
-                    const float dec = __expf(sc_gam[r] - gs);
-                    if (!isQ) sA[r * LDF + s] = (s < r) ? sc_b[r] * dec * acc[e] : 0.f;
-                    else store1<SP>(sP + r * LDC2 + s, LO_C, (s <= r) ? dec * acc[e] : 0.f);
+            for (int ti = 0; ti < NT; ++ti) {
+                const F ka = O::lda(sK, LDK, 16 * ti, 32 * m);
+                const F qa = O::lda(sQ, LDK, 16 * ti, 32 * m);
+                if constexpr (SP) {
+                    ks[ti] = O::mma(ka, sl, ks[ti]);
+                    qs[ti] = O::mma(qa, sl, qs[ti]);
                 }
+                ks[ti] = O::mma(ka, sh, ks[ti]);
+                qs[ti] = O::mma(qa, sh, qs[ti]);
             }
         }
-        for (int id = tid; id < C * C; id += THREADS) {   // zero the strictly-upper tiles of P
-            const int r = id / C, s = id % C;
-            if ((s >> 4) > (r >> 4)) store1<SP>(sP + r * LDC2 + s, LO_C, 0.f);
-        }
-        f32x4 accO[Cf::OPW], accR[Cf::OPW];
+        // R = beta V - beta e^gamma (K S0)
+        f32x4 r[NT];
 #pragma unroll
-        for (int m = 0; m < Cf::OPW; ++m) {
-            const int id = wave + NW_ * m;
-            accO[m] = zero4();
-            accR[m] = zero4();
-            if (id < Cf::NO) {
-                const int ti = id / Cf::NVT, vj = id % Cf::NVT;
-                accR[m] = mma_range<E, false, SP>(accR[m], sK, LDK, 16 * ti, 0, sSt, LDS2,
-                                                  16 * vj, LO_DK, 0, DK);
-                accO[m] = mma_range<E, false, SP>(accO[m], sQ, LDK, 16 * ti, 0, sSt, LDS2,
-                                                  16 * vj, LO_DK, 0, DK);
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * ti + lr + e;
+                r[ti][e] = sc[Cf::SC_B + t] * to_f32(sV[t * LDV + vl]) - sc[Cf::SC_BK + t] * ks[ti][e];
             }
-        }
-        __syncthreads();
-
-        // ---- P2a: 16x16 diagonal blocks of T by forward substitution (wave 0),
-        //      R = beta V - beta e^gamma (K S0) -> Rt pair (owners).
-        if (wave == 0) {
-            const int d = l >> 4, jc = l & 15;
-            if (d < Cf::NT) {
-                const float* Ad = sA + (16 * d) * LDF + 16 * d;
-                float x[16];
+        F rh, rl;
+        O::split(r[0], r[1], rh, rl);
+        // U = T R
+        f32x4 u[NT];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float acc = (r == jc) ? 1.f : 0.f;
-#pragma unroll
-                    for (int s = 0; s < r; ++s) acc -= Ad[r * LDF + s] * x[s];
-                    x[r] = acc;
-                }
-                float* Td = sTf + (16 * d) * LDF + 16 * d;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) Td[r * LDF + jc] = x[r];
+        for (int ti = 0; ti < NT; ++ti) {
+            const F th = O::lda(Tp, LDP, 16 * ti, 0);
+            u[ti] = zero4();
+            if constexpr (SP) {
+                u[ti] = O::mma(O::lda(Tp, LDP, 16 * ti, C), rh, u[ti]);
+                u[ti] = O::mma(th, rl, u[ti]);
             }
+            u[ti] = O::mma(th, rh, u[ti]);
         }
+        // O = scale (e^gamma Q S0 + P U)
+        F uh, ul;
+        O::split(u[0], u[1], uh, ul);
 #pragma unroll
-        for (int m = 0; m < Cf::OPW; ++m) {
-            const int id = wave + NW_ * m;
-            if (id < Cf::NO) {
-                const int ti = id / Cf::NVT, vj = id % Cf::NVT;
-                const int vl = 16 * vj + lc, t0 = 16 * ti + lr;
-                f32x4 r;
+        for (int ti = 0; ti < NT; ++ti) {
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = qs[ti][e] * sc[Cf::SC_EG + 16 * ti + lr + e];
+            const F ph = O::lda(Pp, LDP, 16 * ti, 0);
+            if constexpr (SP) {
+                o = O::mma(O::lda(Pp, LDP, 16 * ti, C), uh, o);
+                o = O::mma(ph, ul, o);
+            }
+            o = O::mma(ph, uh, o);
+            if (vok) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    r[e] = sc_b[t0 + e] * to_f32(sV[(t0 + e) * LDV + vl]) -
-                           sc_bk[t0 + e] * accR[m][e];
-                store4<SP>(sRt + vl * LDC2 + t0, LO_C, r);
+                    ob[(size_t)(c0 + 16 * ti + lr + e) * Dv + vl] = from_f32<E>(scale * o[e]);
             }
+        }
+        // S = e^{gamma_C} S0 + K^T diag(e^{gamma_C - gamma}) U
+        f32x4 ud[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ud[ti][e] = u[ti][e] * sc[Cf::SC_DL + 16 * ti + lr + e];
+        F dh, dlo;
+        O::split(ud[0], ud[1], dh, dlo);
+        const float egC = sc[Cf::SC_EGC];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            const F ka = O::lda_t(sK, LDK, 16 * kt, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accS[kt][e] *= egC;
+            if constexpr (SP) accS[kt] = O::mma(ka, dlo, accS[kt]);
+            accS[kt] = O::mma(ka, dh, accS[kt]);
+        }
+    };
+
+    // ------------------------------------------------------------ schedule
+    if (wave >= Cf::W_S) {                       // prologue: chunks 0, 1 stored, 2 loaded
+        for (int c = 0; c < 2 && c < NC; ++c) {
+            stage_load(c);
+            stage_store(c);
+        }
+        if (2 < NC) stage_load(2);
+    }
+    __syncthreads();
+    if (wave == Cf::W_T && NC > 0) build_T(0);
+    if (wave == Cf::W_P && NC > 0) build_P(0);
+    __syncthreads();
+
+    for (int i = 0; i < NC; ++i) {
+        if (wave < Cf::NCW) {
+            consume(i);
+        } else if (wave == Cf::W_T) {
+            if (i + 1 < NC) build_T(i + 1);
+        } else if (wave == Cf::W_P) {
+            if (i + 1 < NC) build_P(i + 1);
+        } else if (i + 2 < NC) {
+            stage_store(i + 2);
+            if (i + 3 < NC) stage_load(i + 3);
         }
         __syncthreads();
-
-        // ---- P2b: doubling merges, T21 = -T22 (A21 T11), fp32 MFMA
-#pragma unroll
-        for (int mb = 16; mb < C; mb *= 2) {
-            const int nblk = C / (2 * mb);
-            const int tpr = mb / 16;
-            const int tpb = tpr * tpr;
-            const int LDX = mb + 4;
-            for (int job = wave; job < nblk * tpb; job += NW_) {     // X = A21 T11
-                const int bk = job / tpb, tt = job % tpb, ti = tt / tpr, tj = tt % tpr;
-                const int base = 2 * mb * bk;
-                f32x4 acc = zero4();
-                for (int kk = 16 * tj; kk < mb; kk += 4)
-                    acc = Mfma<float>::mma(Mfma<float>::ld(sA, LDF, base + mb + 16 * ti, base + kk),
-                                           ld_b_rowmajor(sTf, LDF, base + kk, base + 16 * tj), acc);
-                float* Xb = sX + bk * mb * LDX;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Xb[(16 * ti + lr + e) * LDX + 16 * tj + lc] = acc[e];
-            }
-            __syncthreads();
-            for (int job = wave; job < nblk * tpb; job += NW_) {     // T21 = -T22 X
-                const int bk = job / tpb, tt = job % tpb, ti = tt / tpr, tj = tt % tpr;
-                const int base = 2 * mb * bk;
-                const float* Xb = sX + bk * mb * LDX;
-                f32x4 acc = zero4();
-                for (int kk = 0; kk < 16 * (ti + 1); kk += 4)
-                    acc = Mfma<float>::mma(Mfma<float>::ld(sTf, LDF, base + mb + 16 * ti, base + mb + kk),
-                                           ld_b_rowmajor(Xb, LDX, kk, 16 * tj), acc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sTf[(base + mb + 16 * ti + lr + e) * LDF + base + 16 * tj + lc] = -acc[e];
-            }
-            __syncthreads();
-        }
-
-        // ---- P2c: T -> pair buffer in the operand type (upper triangle zero)
-        for (int id = tid; id < C * C; id += THREADS) {
-            const int r = id / C, s = id % C;
-            store1<SP>(sT + r * LDC2 + s, LO_C, (s <= r) ? sTf[r * LDF + s] : 0.f);
-        }
-        __syncthreads();
-
-        // ---- P3: U = T R (owners) -> Ut pair, Ud = diag(e^{gamma_C-gamma}) U pair
-#pragma unroll
-        for (int m = 0; m < Cf::OPW; ++m) {
-            const int id = wave + NW_ * m;
-            if (id < Cf::NO) {
-                const int ti = id / Cf::NVT, vj = id % Cf::NVT;
-                const int kend = ((16 * (ti + 1) + KS - 1) / KS) * KS;
-                const f32x4 u = mma_range<E, SP, SP>(zero4(), sT, LDC2, 16 * ti, LO_C, sRt, LDC2,
-                                                     16 * vj, LO_C, 0, kend);
-                const int vl = 16 * vj + lc, t0 = 16 * ti + lr;
-                store4<SP>(sUt + vl * LDC2 + t0, LO_C, u);
-                f32x4 ud;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ud[e] = u[e] * sc_dl[t0 + e];
-                store4<SP>(sUd + vl * LDC2 + t0, LO_C, ud);
-            }
-        }
-        __syncthreads();
-
-        // ---- P4: O = scale (e^gamma Q S0 + P U) -> out; S = e^{gamma_C} S0 + K^T Ud
-#pragma unroll
-        for (int m = 0; m < Cf::OPW; ++m) {
-            const int id = wave + NW_ * m;
-            if (id < Cf::NO) {
-                const int ti = id / Cf::NVT, vj = id % Cf::NVT;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) accO[m][e] *= sc_eg[16 * ti + lr + e];
-                const int kend = ((16 * (ti + 1) + KS - 1) / KS) * KS;
-                accO[m] = mma_range<E, SP, SP>(accO[m], sP, LDC2, 16 * ti, LO_C, sUt, LDC2,
-                                               16 * vj, LO_C, 0, kend);
-                const int col = 16 * vj + lc;
-                if (col < vcols) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        ob[(size_t)(c0 + 16 * ti + lr + e) * Dv + col] =
-                            from_f32<E>(scale * accO[m][e]);
-                }
-            }
-        }
-        const float egC = sc_misc[0];
-#pragma unroll
-        for (int m = 0; m < Cf::SPW; ++m) {
-            const int id = wave + NW_ * m;
-            if (id < Cf::NS) {
-                const int tk = id / Cf::NVT, vj = id % Cf::NVT;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) accS[m][e] *= egC;
-                accS[m] = mma_range<E, false, SP>(accS[m], sKt, LDKT, 16 * tk, 0, sUd, LDC2,
-                                                  16 * vj, LO_C, 0, C);
-                store4<SP>(sSt + (16 * vj + lc) * LDS2 + 16 * tk + lr, LO_DK, accS[m]);
-            }
-        }
     }
 
     // ---- final state
+    if (vok) {
 #pragma unroll
-    for (int m = 0; m < Cf::SPW; ++m) {
-        const int id = wave + NW_ * m;
-        if (id < Cf::NS) {
-            const int tk = id / Cf::NVT, vj = id % Cf::NVT;
-            const int col = 16 * vj + lc;
-            if (col < vcols) {
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int dk = 16 * tk + lr + e;
-                    if (dk < Dk) sb[(size_t)dk * Dv + col] = accS[m][e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int dk = 16 * kt + lr + e;
+                if (dk < Dk) sb[(size_t)dk * Dv + vl] = accS[kt][e];
             }
-        }
     }
 }
 
 // ---------------------------------------------------------------- launch
 
-template <typename E, int C, int DK, int BV>
+template <typename E, int DK, int BV>
 static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream)
 {
-    constexpr int NW = 8;
+    using Cf = PipeCfg<E, 32, DK, BV>;
     const int nvt = (a.Dv + BV - 1) / BV;
     const long long blocks = (long long)nvt * a.Hv * a.B;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gdn_prefill_kernel<E, C, DK, BV, NW>), dim3((unsigned)blocks),
-                       dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((gdn_prefill_kernel<E, 32, DK, BV>), dim3((unsigned)blocks),
+                       dim3(Cf::THREADS), 0, stream,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, a.g_log, a.beta, a.scale,
                        a.state, (E*)a.out, a.Hk, a.Hv, a.S, a.Dk, a.Dv, nvt);
     return hipGetLastError();
@@ -494,26 +496,22 @@ static int pick_bv(const PrefillArgs& a, int max_bv)
     return 16;
 }
 
-template <typename E, int C, int DK>
+template <typename E, int DK>
 static hipError_t launch_dk(const PrefillArgs& a, int max_bv, hipStream_t stream)
 {
     switch (pick_bv(a, max_bv)) {
-        case 64: if constexpr (sizeof(E) == 2) return launch_cfg<E, C, DK, 64>(a, stream);
+        case 64: if constexpr (sizeof(E) == 2) return launch_cfg<E, DK, 64>(a, stream);
                  [[fallthrough]];
-        case 32: return launch_cfg<E, C, DK, 32>(a, stream);
-        default: return launch_cfg<E, C, DK, 16>(a, stream);
+        case 32: return launch_cfg<E, DK, 32>(a, stream);
+        default: return launch_cfg<E, DK, 16>(a, stream);
     }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, hipStream_t stream)
 {
-    if (dtype == 1) {   // bf16 operands: 64-token chunks
-        return a.Dk <= 64 ? launch_dk<bf16, 64, 64>(a, 64, stream)
-                          : launch_dk<bf16, 64, 128>(a, 64, stream);
-    }
-    // fp32 operands: 32-token chunks keep the fp32 tiles inside LDS
-    return a.Dk <= 64 ? launch_dk<float, 32, 64>(a, 32, stream)
-                      : launch_dk<float, 32, 128>(a, 32, stream);
+    if (dtype == 1)
+        return a.Dk <= 64 ? launch_dk<bf16, 64>(a, 64, stream) : launch_dk<bf16, 128>(a, 64, stream);
+    return a.Dk <= 64 ? launch_dk<float, 64>(a, 32, stream) : launch_dk<float, 128>(a, 32, stream);
 }
 
 }  // namespace gdn
