@@ -123,4 +123,13 @@ __device__ __forceinline__ f32x4 mma_f32_rm(f32x4 c, const float* A, int lda, in
                                                 0, 0, 0);
 }
 
+// As mma_f32_rm with A given transposed: A[r][k] = At[k][r].
+__device__ __forceinline__ f32x4 mma_f32_tm(f32x4 c, const float* At, int lda, int r0,
+                                            const float* B, int ldb, int n0, int k0) {
+    const int l = lane_id();
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(At[(k0 + (l >> 4)) * lda + r0 + (l & 15)],
+                                                B[(k0 + (l >> 4)) * ldb + n0 + (l & 15)], c,
+                                                0, 0, 0);
+}
+
 }  // namespace gdn

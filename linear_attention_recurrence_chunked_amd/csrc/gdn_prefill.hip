@@ -33,9 +33,9 @@
 //    16x16 diagonal blocks by forward substitution, one lane per column, then
 //    the merge T21 = -T22 (A21 T11) on fp32 MFMA);
 //  * the P wave builds P = Q K^T (.) Mincl for chunk i+1;
-//  * two stager waves move chunk i+2 from registers into LDS (with gamma and
-//    the per-token decay scalars) and prefetch chunk i+3 from HBM, so every
-//    HBM load has a chunk's worth of time to land.
+//  * two stager waves load chunk i+2 from HBM and store it into LDS (with
+//    gamma and the per-token decay scalars); the HBM latency is spent inside
+//    their own step, off the sequential path.
 //
 // LDS holds three input slots (chunks i, i+1, i+2) and two T/P buffers.
 // The state-independent work of a chunk therefore never sits on the
@@ -131,7 +131,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 
     __shared__ __attribute__((aligned(16))) char smem[Cf::LDS_BYTES];
 
-    const int wave = threadIdx.x >> 6;
+    // The wave index is uniform across a wave; readfirstlane makes that
+    // visible to the compiler so the role branches below are scalar branches
+    // (otherwise every wave would step through every role under exec masks).
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
     const int lc = l & 15;          // column of this lane in a 16x16 accumulator tile
     const int lr = 4 * (l >> 4);    // first of its 4 rows
@@ -158,7 +161,9 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 
     // ------------------------------------------------------------ stagers
     // Two stager waves split each chunk: half 0 moves K, g and beta, half 1
-    // moves Q and V. A chunk's loads are issued one chunk ahead of its store.
+    // moves Q and V, two chunks ahead of the consumers. Loads and stores of a
+    // chunk happen in the same step, so no staging registers stay live across
+    // the barrier (the register file is shared by all roles).
     const int half = wave - Cf::W_S;           // 0 or 1 on the stager waves
     VecE rk[Cf::NVK], rv[Cf::NVV];             // half 0: K rows; half 1: Q rows (rk) and V (rv)
     float rg = 0.f, rb = 0.f;
@@ -219,66 +224,110 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         if (l == 0) sc[Cf::SC_EGC] = __expf(gC);
     };
 
-    // ------------------------------------------------------------ inverse wave
+    // ------------------------------------------------------------ producers
+    // Per-lane gamma/beta for the rows (16 ti + lr + e) and columns (16 tj + lc)
+    // of the three lower 16x16 tiles of a chunk, read once.
+    struct TileScalars { float gr[2][4], br[2][4], gs[2]; };
+    auto tile_scalars = [&](const float* __restrict__ sc) {
+        TileScalars ts;
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            ts.gs[ti] = sc[Cf::SC_GAM + 16 * ti + lc];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ts.gr[ti][e] = sc[Cf::SC_GAM + 16 * ti + lr + e];
+                ts.br[ti][e] = sc[Cf::SC_B + 16 * ti + lr + e];
+            }
+        }
+        return ts;
+    };
+
+    // Inverse wave: A = diag(beta) (K K^T) (.) Mstrict and T = (I + A)^{-1}.
     auto build_T = [&](int c) {
         const char* slot = slot_ptr(c);
-        const E* sK = (const E*)(slot + Cf::OFF_SK);
-        const float* sc = (const float*)(slot + Cf::OFF_SSC);
-        float* sA = (float*)(smem + Cf::OFF_A);
-        float* sTf = (float*)(smem + Cf::OFF_TF);
-        float* sX = (float*)(smem + Cf::OFF_X);
-        E* Tp = (E*)(smem + Cf::OFF_T + (c & 1) * Cf::SZ_TP);
-        // A = diag(beta) (K K^T) (.) Mstrict on the three lower 16x16 tiles.
-        // Decay factors e^{gamma_r - gamma_s} are only used where s < r.
+        const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
+        float* __restrict__ sAt = (float*)(smem + Cf::OFF_A);   // A transposed: sAt[s][r] = A[r][s]
+        float* __restrict__ sTf = (float*)(smem + Cf::OFF_TF);
+        float* __restrict__ sX = (float*)(smem + Cf::OFF_X);
+        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c & 1) * Cf::SZ_TP);
+        const TileScalars ts = tile_scalars((const float*)(slot + Cf::OFF_SSC));
+        // K K^T on the three lower tiles; K fragments of both row tiles are
+        // loaded once and serve as both operands. A is stored transposed so
+        // that a column of A is a contiguous row. Decay factors
+        // e^{gamma_r - gamma_s} are only used where s < r.
+        F kf[2][NKS];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int m = 0; m < NKS; ++m) kf[t2][m] = O::lda(sK, LDK, 16 * t2, 32 * m);
 #pragma unroll
         for (int tt = 0; tt < 3; ++tt) {
             const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 0; m < NKS; ++m)
-                acc = O::mma(O::lda(sK, LDK, 16 * ti, 32 * m), O::lda(sK, LDK, 16 * tj, 32 * m), acc);
+            for (int m = 0; m < NKS; ++m) acc = O::mma(kf[ti][m], kf[tj][m], acc);
             const int s = 16 * tj + lc;
-            const float gs = sc[Cf::SC_GAM + s];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * ti + lr + e;
-                const float dec = __expf(sc[Cf::SC_GAM + r] - gs);
-                sA[r * LDF + s] = (s < r) ? sc[Cf::SC_B + r] * dec * acc[e] : 0.f;
+                const float dec = __expf(ts.gr[ti][e] - ts.gs[tj]);
+                sAt[s * LDF + r] = (s < r) ? ts.br[ti][e] * dec * acc[e] : 0.f;
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         wave_lds_fence();
         // Diagonal 16x16 blocks: lane (d, jc) solves column jc of block d by
-        // forward substitution, x_r = [r == jc] - sum_{s<r} A[r][s] x_s, in
-        // fp32, one row of A at a time (scheduling barriers keep the rows
-        // from all being loaded at once).
+        // forward substitution in fp32, x_r -= A[r][s] x_s for s < r, column
+        // by column (15 independent updates per step). Column s of A is row s
+        // of the transposed buffer (broadcast reads); columns are loaded two
+        // steps ahead of their use, and scheduling barriers keep the loads
+        // from being hoisted further (register pressure). The result goes to
+        // the fp32 buffer (for the merge) and to the operand buffer.
         if (l < 32) {
             const int d = l >> 4, jc = l & 15;
-            const float* Ad = sA + (16 * d) * LDF + 16 * d;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float a[16];
+            const float* Atd = sAt + (16 * d) * LDF + 16 * d;
+            auto col = [&](int s2, float* dst) {
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4) {
-                    const f32x4 w = *(const f32x4*)(Ad + r * LDF + 4 * c4);
-                    a[4 * c4] = w[0]; a[4 * c4 + 1] = w[1]; a[4 * c4 + 2] = w[2]; a[4 * c4 + 3] = w[3];
+                    const f32x4 w = *(const f32x4*)(Atd + s2 * LDF + 4 * c4);
+                    dst[4 * c4] = w[0]; dst[4 * c4 + 1] = w[1];
+                    dst[4 * c4 + 2] = w[2]; dst[4 * c4 + 3] = w[3];
                 }
-                float acc = (r == jc) ? 1.f : 0.f;
+            };
+            float x[16], c0v[16], c1v[16], c2v[16];
 #pragma unroll
-                for (int s2 = 0; s2 < r; ++s2) acc -= a[s2] * x[s2];
-                x[r] = acc;
+            for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
+            col(0, c0v);
+            col(1, c1v);
+#pragma unroll
+            for (int s2 = 0; s2 < 15; ++s2) {
+                if (s2 + 2 < 15) col(s2 + 2, c2v);
+                const float xs = x[s2];
+#pragma unroll
+                for (int r = s2 + 1; r < 16; ++r) x[r] -= c0v[r] * xs;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { c0v[r] = c1v[r]; c1v[r] = c2v[r]; }
                 __builtin_amdgcn_sched_barrier(0);
             }
             float* Td = sTf + (16 * d) * LDF + 16 * d;
+            E* Tpd = Tp + (16 * d) * LDP + 16 * d;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Td[r * LDF + jc] = x[r];
+            for (int r = 0; r < 16; ++r) {
+                Td[r * LDF + jc] = x[r];
+                store_pair<SP>(Tpd + r * LDP + jc, C, x[r]);
+            }
+        } else {
+            // the upper 16x16 block of T is zero
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const int id = (l - 32) + 32 * n;
+                store_pair<SP>(Tp + (id >> 4) * LDP + 16 + (id & 15), C, 0.f);
+            }
         }
         wave_lds_fence();
-        // Merge: T21 = -T22 (A21 T11)
+        // Merge: T21 = -T22 (A21 T11), with A21[r][k] read from the transposed buffer
         f32x4 acc = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < 16; k0 += 4) acc = mma_f32_rm(acc, sA, LDF, 16, sTf, LDF, 0, k0);
+        for (int k0 = 0; k0 < 16; k0 += 4) acc = mma_f32_tm(acc, sAt, LDF, 16, sTf, LDF, 0, k0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sX[(lr + e) * LDX + lc] = acc[e];
         wave_lds_fence();
@@ -286,39 +335,37 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
         for (int k0 = 0; k0 < 16; k0 += 4) acc = mma_f32_rm(acc, sTf + 16, LDF, 16, sX, LDX, 0, k0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sTf[(16 + lr + e) * LDF + lc] = -acc[e];
-        wave_lds_fence();
-        // T -> operand buffer (upper triangle zero)
-#pragma unroll
-        for (int n = 0; n < C * C / 64; ++n) {
-            const int id = l + 64 * n, r = id / C, s = id % C;
-            store_pair<SP>(Tp + r * LDP + s, C, (s <= r) ? sTf[r * LDF + s] : 0.f);
-        }
+        for (int e = 0; e < 4; ++e) store_pair<SP>(Tp + (16 + lr + e) * LDP + lc, C, -acc[e]);
     };
 
-    // ------------------------------------------------------------ P wave
+    // P wave: P = Q K^T (.) Mincl.
     auto build_P = [&](int c) {
         const char* slot = slot_ptr(c);
-        const E* sK = (const E*)(slot + Cf::OFF_SK);
-        const E* sQ = (const E*)(slot + Cf::OFF_SQ);
-        const float* sc = (const float*)(slot + Cf::OFF_SSC);
-        E* Pp = (E*)(smem + Cf::OFF_P + (c & 1) * Cf::SZ_TP);
+        const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
+        const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
+        E* __restrict__ Pp = (E*)(smem + Cf::OFF_P + (c & 1) * Cf::SZ_TP);
+        const TileScalars ts = tile_scalars((const float*)(slot + Cf::OFF_SSC));
+        F kf[2][NKS], qf[2][NKS];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int m = 0; m < NKS; ++m) {
+                kf[t2][m] = O::lda(sK, LDK, 16 * t2, 32 * m);
+                qf[t2][m] = O::lda(sQ, LDK, 16 * t2, 32 * m);
+            }
 #pragma unroll
         for (int tt = 0; tt < 3; ++tt) {
             const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 0; m < NKS; ++m)
-                acc = O::mma(O::lda(sQ, LDK, 16 * ti, 32 * m), O::lda(sK, LDK, 16 * tj, 32 * m), acc);
+            for (int m = 0; m < NKS; ++m) acc = O::mma(qf[ti][m], kf[tj][m], acc);
             const int s = 16 * tj + lc;
-            const float gs = sc[Cf::SC_GAM + s];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * ti + lr + e;
-                const float dec = __expf(sc[Cf::SC_GAM + r] - gs);
+                const float dec = __expf(ts.gr[ti][e] - ts.gs[tj]);
                 store_pair<SP>(Pp + r * LDP + s, C, (s <= r) ? dec * acc[e] : 0.f);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int n = 0; n < 4; ++n) {   // the upper 16x16 tile is zero
@@ -341,13 +388,27 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     }
     auto consume = [&](int i) {
         const char* slot = slot_ptr(i);
-        const E* sK = (const E*)(slot + Cf::OFF_SK);
-        const E* sQ = (const E*)(slot + Cf::OFF_SQ);
-        const E* sV = (const E*)(slot + Cf::OFF_SV);
-        const float* sc = (const float*)(slot + Cf::OFF_SSC);
-        const E* Tp = (const E*)(smem + Cf::OFF_T + (i & 1) * Cf::SZ_TP);
-        const E* Pp = (const E*)(smem + Cf::OFF_P + (i & 1) * Cf::SZ_TP);
+        const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
+        const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
+        const E* __restrict__ sV = (const E*)(slot + Cf::OFF_SV);
+        const float* __restrict__ sc = (const float*)(slot + Cf::OFF_SSC);
+        const E* __restrict__ Tp = (const E*)(smem + Cf::OFF_T + (i & 1) * Cf::SZ_TP);
+        const E* __restrict__ Pp = (const E*)(smem + Cf::OFF_P + (i & 1) * Cf::SZ_TP);
         const int c0 = i * C;
+        // per-row scalars and V values of this lane's rows t = 16 ti + lr + e, read once
+        float vv[NT][4], bt[NT][4], bk[NT][4], eg[NT][4], dl[NT][4];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * ti + lr + e;
+                vv[ti][e] = to_f32(sV[t * LDV + vl]);
+                bt[ti][e] = sc[Cf::SC_B + t];
+                bk[ti][e] = sc[Cf::SC_BK + t];
+                eg[ti][e] = sc[Cf::SC_EG + t];
+                dl[ti][e] = sc[Cf::SC_DL + t];
+            }
+        const float egC = sc[Cf::SC_EGC];
         // K S0 and Q S0 with S0 from registers
         f32x4 ks[NT], qs[NT];
 #pragma unroll
@@ -373,10 +434,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * ti + lr + e;
-                r[ti][e] = sc[Cf::SC_B + t] * to_f32(sV[t * LDV + vl]) - sc[Cf::SC_BK + t] * ks[ti][e];
-            }
+            for (int e = 0; e < 4; ++e) r[ti][e] = bt[ti][e] * vv[ti][e] - bk[ti][e] * ks[ti][e];
         F rh, rl;
         O::split(r[0], r[1], rh, rl);
         // U = T R
@@ -398,7 +456,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         for (int ti = 0; ti < NT; ++ti) {
             f32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = qs[ti][e] * sc[Cf::SC_EG + 16 * ti + lr + e];
+            for (int e = 0; e < 4; ++e) o[e] = qs[ti][e] * eg[ti][e];
             const F ph = O::lda(Pp, LDP, 16 * ti, 0);
             if constexpr (SP) {
                 o = O::mma(O::lda(Pp, LDP, 16 * ti, C), uh, o);
@@ -416,10 +474,9 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ud[ti][e] = u[ti][e] * sc[Cf::SC_DL + 16 * ti + lr + e];
+            for (int e = 0; e < 4; ++e) ud[ti][e] = u[ti][e] * dl[ti][e];
         F dh, dlo;
         O::split(ud[0], ud[1], dh, dlo);
-        const float egC = sc[Cf::SC_EGC];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
             const F ka = O::lda_t(sK, LDK, 16 * kt, 0);
@@ -431,12 +488,11 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     };
 
     // ------------------------------------------------------------ schedule
-    if (wave >= Cf::W_S) {                       // prologue: chunks 0, 1 stored, 2 loaded
+    if (wave >= Cf::W_S) {                       // prologue: chunks 0 and 1
         for (int c = 0; c < 2 && c < NC; ++c) {
             stage_load(c);
             stage_store(c);
         }
-        if (2 < NC) stage_load(2);
     }
     __syncthreads();
     if (wave == Cf::W_T && NC > 0) build_T(0);
@@ -451,8 +507,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         } else if (wave == Cf::W_P) {
             if (i + 1 < NC) build_P(i + 1);
         } else if (i + 2 < NC) {
+            stage_load(i + 2);
             stage_store(i + 2);
-            if (i + 3 < NC) stage_load(i + 3);
         }
         __syncthreads();
     }
