@@ -1,6 +1,7 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--only prefill|decode|copy]
 
 One step = one ``gdn_chunked_prefill`` call on the batched long prefill
 workload (B=4, Hk=16, Hv=32, Dk=Dv=128, S=8192, bf16 q/k/v, fp32 g/beta and
@@ -13,6 +14,10 @@ duration for the roofline.
 The decode path (B=256 single-token steps, 64 autoregressive steps with fresh
 inputs) is measured the same way in the same run and reported under
 "decode". Prints ONE JSON line.
+
+``--only copy`` runs a plain device-to-device copy of ``--copy-mib`` MiB
+(used to calibrate the HBM byte counters of rocprofv3 against a kernel of
+known traffic); ``--only prefill|decode`` runs one path alone.
 
 Roofline (per launch, algorithmic, see the workload docstrings below):
 * prefill: HBM bytes = tokens x (q + k + v + out + g + beta) + state in/out;
@@ -36,13 +41,14 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "GDN prefill tokens/s + MFMA util (S=8192); decode steps/s + HBM GB/s"
 
 
-def prefill_algorithmic(B, Hk, Hv, S, Dk, Dv, esize=2, chunk=64):
+def prefill_algorithmic(B, Hk, Hv, S, Dk, Dv, esize=2, chunk=32):
     """Algorithmic HBM bytes and MFMA flops of one prefill call.
 
     bytes: q, k [B,Hk,S,Dk] + v, out [B,Hv,S,Dv] in the operand type, g and
     beta fp32 [B,Hv,S], the fp32 state read once and written once.
     flops (per value head and chunk of C tokens; lower-triangular products
-    counted at half size; K K^T and Q K^T shared inside a GQA group):
+    counted at half size; K K^T and Q K^T shared inside a GQA group; C is the
+    kernel's chunk length, 32):
       W = T K and U~ = T V: C^2 (Dk + Dv); W S, Q S, K^T U: 3 x 2 C Dk Dv;
       P U: C^2 Dv; T: C^3 / 3; per key head: K K^T, Q K^T: 2 x C^2 Dk.
     """
@@ -61,6 +67,34 @@ def decode_algorithmic(B, Hk, Hv, Dk, Dv, esize=2):
     """HBM bytes of one decode step: fp32 state read + write, q, k, v, out, g, beta."""
     return float(2 * B * Hv * Dk * Dv * 4 + (2 * B * Hk * Dk + 2 * B * Hv * Dv) * esize
                  + B * Hv * 8)
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "gdn_prefill_kernel": "linear_attention_recurrence_chunked_amd/csrc/gdn_prefill.hip",
+    "gdn_decode_kernel": "linear_attention_recurrence_chunked_amd/csrc/gdn_decode.hip",
+}
+
+
+def source_digest(kernel):
+    import hashlib
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_digest(kernel):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def _events(torch, n):
@@ -139,6 +173,23 @@ def bench_decode(torch, gdn, inputs, reps, warmup):
     return w, steps, state0, ms_step, kern_ms, decode_algorithmic(w.B, w.Hk, w.Hv, w.Dk, w.Dv)
 
 
+def bench_copy(torch, mib, steps):
+    """Streaming elementwise kernel over ``mib`` MiB of fp32: b = -a reads and
+    writes that many bytes once (a same-dtype copy_ would be a DMA transfer,
+    which the shader counters do not see)."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    return {"copy_bytes_each_way": n * 4, "ms": dt * 1e3, "GB_s": 2 * n * 4 / dt / 1e9}
+
+
 def cpu_baseline_prefill(w, d):
     """The oracle on batch 0 of the prefill workload (1 x 8192 tokens x 32 heads)."""
     import oracle
@@ -172,6 +223,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the recurrence has no cross-GPU step in this "
@@ -187,9 +240,21 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.only == "copy":
+        print(json.dumps({"copy": bench_copy(torch, args.copy_mib, args.steps)}), flush=True)
+        return
+    if args.only == "decode":
+        dw, _, _, dms, dkern_ms, dbytes = bench_decode(torch, gdn, inputs, max(1, args.steps // 10), 1)
+        print(json.dumps({"decode_ms_per_step": dms, "kernel_ms": dkern_ms,
+                          "GB_s": dbytes / (dkern_ms / 1e3) / 1e9}), flush=True)
+        return
     w, d, ms_step, kern_ms, nbytes, flops = bench_prefill(torch, gdn, inputs, args.steps,
                                                           args.warmup)
     tokens = w.B * w.S
+    if args.only == "prefill":
+        print(json.dumps({"prefill_ms_per_step": ms_step, "kernel_ms": kern_ms,
+                          "tokens_per_s": tokens / (ms_step / 1e3)}), flush=True)
+        return
     dw, dsteps, dstate0, dms, dkern_ms, dbytes = bench_decode(torch, gdn, inputs,
                                                               max(1, args.steps // 10), 1)
     res = {
@@ -211,7 +276,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gdn_prefill_kernel",
                      "achieved": nbytes / (kern_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": nbytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None, "kernel_ms": kern_ms,
+                     "traffic": measured_traffic("gdn_prefill_kernel"), "kernel_ms": kern_ms,
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma_util": {"achieved_tflops": flops / (kern_ms / 1e3) / 1e12,
                       "peak_tflops": BF16_PEAK_TFLOPS,
@@ -224,7 +289,8 @@ def main():
                                 "achieved": dbytes / (dkern_ms / 1e3) / 1e9,
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": dbytes / (dkern_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                "traffic": None, "kernel_ms": dkern_ms,
+                                "traffic": measured_traffic("gdn_decode_kernel"),
+                                "kernel_ms": dkern_ms,
                                 "algorithmic_bytes_per_launch": dbytes}},
         "host": {"cpu": platform.processor() or platform.machine(),
                  "gpu": torch.cuda.get_device_name(0)},

@@ -139,8 +139,17 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     const int lc = l & 15;          // column of this lane in a 16x16 accumulator tile
     const int lr = 4 * (l >> 4);    // first of its 4 rows
 
-    // blockIdx -> (value slice, value head, batch)
+    // blockIdx -> (value slice, value head, batch). The workgroups that read
+    // the same key/query head (the Hv/Hk value heads of a GQA group times the
+    // nvt value slices) are placed on one XCD: consecutive workgroup ids go
+    // round-robin over the 8 XCDs, so id L runs on XCD L % 8, and the members
+    // of a group get ids L, L+8, L+16, ... That keeps q/k re-reads in one L2.
     int bid = blockIdx.x;
+    const int gu = (Hv / Hk) * nvt;             // workgroups per key-head group
+    if (gridDim.x % (8 * gu) == 0) {
+        const int slot = bid >> 3, grp = (bid & 7) + 8 * (slot / gu);
+        bid = grp * gu + slot % gu;
+    }
     const int vt = bid % nvt; bid /= nvt;
     const int h = bid % Hv;
     const int b = bid / Hv;
