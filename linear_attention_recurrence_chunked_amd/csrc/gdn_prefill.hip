@@ -29,15 +29,18 @@
 //    registers as the B operand), R, U = T R, O = e^gamma Q S0 + P U and the
 //    state update K^T (dl U) -- every intermediate stays in registers; LDS is
 //    only read for K, Q, V, T and P of the chunk;
-//  * the inverse wave builds A and T = (I + A)^{-1} for chunk i+1 (fp32:
-//    16x16 diagonal blocks by forward substitution, one lane per column, then
-//    the merge T21 = -T22 (A21 T11) on fp32 MFMA);
+//  * the inverse wave builds T = (I + A)^{-1} for chunk i+1 (fp32: 16x16
+//    diagonal blocks by forward substitution, one lane per column, then the
+//    merge T21 = -T22 (A21 T11) on fp32 MFMA);
 //  * the P wave builds P = Q K^T (.) Mincl for chunk i+1;
-//  * two stager waves load chunk i+2 from HBM and store it into LDS (with
+//  * two stager waves load chunk i+LEAD from HBM and store it into LDS (with
 //    gamma and the per-token decay scalars); the HBM latency is spent inside
-//    their own step, off the sequential path.
+//    their own step, off the sequential path. On the bf16 path the P wave
+//    also builds A = diag(beta) (K K^T) (.) Mstrict for chunk i+2 (on the
+//    fp32 path the inverse wave builds A).
 //
-// LDS holds three input slots (chunks i, i+1, i+2) and two T/P buffers.
+// LDS holds the input slots of chunks i .. i+LEAD (4 on the bf16 path, 3 on
+// the fp32 path, whose tiles are twice as large) and two T/P buffers.
 // The state-independent work of a chunk therefore never sits on the
 // sequential path. HBM traffic is the algorithmic minimum: q, k, v, g, beta
 // read once per slice, out written once, the state read and written once.
@@ -75,7 +78,13 @@ struct PipeCfg {
     static constexpr int W_S = NCW + 2;            // first of two stager waves
     static constexpr int NW = NCW + 4;
     static constexpr int THREADS = 64 * NW;
-    static constexpr int NSLOT = 3;
+    // AHEAD: the masked K K^T (A) of a chunk is built by the P wave one chunk
+    // before its inverse, so the inverse wave only solves. It costs a fourth
+    // input slot and a second A buffer, which fit LDS on the bf16 path.
+    static constexpr bool AHEAD = SP;
+    static constexpr int NSLOT = AHEAD ? 4 : 3;    // chunks i .. i+NSLOT-1 resident
+    static constexpr int LEAD = NSLOT - 1;         // the stagers write chunk i+LEAD
+    static constexpr int NABUF = AHEAD ? 2 : 1;
     static constexpr int PADE = SP ? 8 : 4;        // row padding (elements): 16-byte rows
     static constexpr int LDK = DK + PADE;          // K, Q rows [t][dk]
     static constexpr int LDV = BV + PADE;          // V rows [t][v]
@@ -99,7 +108,7 @@ struct PipeCfg {
     static constexpr int OFF_T = NSLOT * SZ_SLOT;
     static constexpr int OFF_P = OFF_T + 2 * SZ_TP;
     static constexpr int OFF_A = OFF_P + 2 * SZ_TP;
-    static constexpr int OFF_TF = OFF_A + SZ_F;
+    static constexpr int OFF_TF = OFF_A + NABUF * SZ_F;
     static constexpr int OFF_X = OFF_TF + SZ_F;
     static constexpr int LDS_BYTES = OFF_X + SZ_X;
     // scalar arrays inside a slot (floats): gamma, e^gamma, beta, beta e^gamma,
@@ -169,53 +178,43 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     auto slot_ptr = [&](int c) { return smem + (c % Cf::NSLOT) * Cf::SZ_SLOT; };
 
     // ------------------------------------------------------------ stagers
-    // Two stager waves split each chunk: half 0 moves K, g and beta, half 1
-    // moves Q and V, two chunks ahead of the consumers. Loads and stores of a
-    // chunk happen in the same step, so no staging registers stay live across
-    // the barrier (the register file is shared by all roles).
-    const int half = wave - Cf::W_S;           // 0 or 1 on the stager waves
-    VecE rk[Cf::NVK], rv[Cf::NVV];             // half 0: K rows; half 1: Q rows (rk) and V (rv)
-    float rg = 0.f, rb = 0.f;
-    auto stage_load = [&](int c) {
-        const int c0 = c * C;
-        const E* src = half == 0 ? kb : qb;
+    // Two stager waves split each chunk: the K stager (wave W_S) moves K, g
+    // and beta and computes gamma and the decay scalars; the QV stager (wave
+    // W_S + 1) moves Q and V. Loads and stores of a chunk happen in the same
+    // step, so no staging registers stay live across the barrier (the
+    // register file is shared by all roles).
+    // HBM loads are unconditional, from clamped (in-bounds) addresses, and
+    // out-of-range vectors are zeroed by selection: guarded loads would be
+    // issued one at a time, each waiting out the HBM latency.
+    auto load_rows = [&](VecE (&r)[Cf::NVK], const E* src, int c0) {
 #pragma unroll
         for (int n = 0; n < Cf::NVK; ++n) {
             const int id = l + 64 * n, t = id / (DK / VE), d0 = (id % (DK / VE)) * VE;
-            rk[n] = VecE{};
-            if (d0 < Dk) rk[n] = *(const VecE*)(src + (size_t)(c0 + t) * Dk + d0);
-        }
-        if (half == 0) {
-            if (l < C) { rg = gb[c0 + l]; rb = bb[c0 + l]; }
-        } else {
-#pragma unroll
-            for (int n = 0; n < Cf::NVV; ++n) {
-                const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
-                rv[n] = VecE{};
-                if (d0 < vcols) rv[n] = *(const VecE*)(vb + (size_t)(c0 + t) * Dv + d0);
-            }
+            const VecE x = *(const VecE*)(src + (size_t)(c0 + t) * Dk + min(d0, Dk - VE));
+            r[n] = d0 < Dk ? x : VecE{};
         }
     };
-    auto stage_store = [&](int c) {
-        char* slot = slot_ptr(c);
-        E* dst = (E*)(slot + (half == 0 ? Cf::OFF_SK : Cf::OFF_SQ));
+    auto store_rows = [&](const VecE (&r)[Cf::NVK], E* dst) {
 #pragma unroll
         for (int n = 0; n < Cf::NVK; ++n) {
             const int id = l + 64 * n, t = id / (DK / VE), d0 = (id % (DK / VE)) * VE;
-            *(VecE*)(dst + t * LDK + d0) = rk[n];
+            *(VecE*)(dst + t * LDK + d0) = r[n];
         }
-        if (half == 1) {
-            E* sV = (E*)(slot + Cf::OFF_SV);
-#pragma unroll
-            for (int n = 0; n < Cf::NVV; ++n) {
-                const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
-                *(VecE*)(sV + t * LDV + d0) = rv[n];
-            }
-            return;
-        }
+    };
+    struct KRegs { VecE k[Cf::NVK]; float g, b; };
+    auto stage_k_load = [&](int c, KRegs& R) {
+        load_rows(R.k, kb, c * C);
+        const float g = gb[c * C + min(l, C - 1)];
+        const float b2 = bb[c * C + min(l, C - 1)];
+        R.g = l < C ? g : 0.f;
+        R.b = l < C ? b2 : 0.f;
+    };
+    auto stage_k_store = [&](int c, const KRegs& R) {
+        char* slot = slot_ptr(c);
+        store_rows(R.k, (E*)(slot + Cf::OFF_SK));
         // gamma = inclusive cumulative sum of g over the chunk, and the scalars
         float* sc = (float*)(slot + Cf::OFF_SSC);
-        float x = (l < C) ? rg : 0.f;
+        float x = R.g;
 #pragma unroll
         for (int off = 1; off < C; off <<= 1) {
             const float y = __shfl_up(x, off);
@@ -226,11 +225,30 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             const float eg = __expf(x);
             sc[Cf::SC_GAM + l] = x;
             sc[Cf::SC_EG + l] = eg;
-            sc[Cf::SC_B + l] = rb;
-            sc[Cf::SC_BK + l] = rb * eg;
+            sc[Cf::SC_B + l] = R.b;
+            sc[Cf::SC_BK + l] = R.b * eg;
             sc[Cf::SC_DL + l] = __expf(gC - x);   // gC <= x: never overflows
         }
         if (l == 0) sc[Cf::SC_EGC] = __expf(gC);
+    };
+    auto stage_qv = [&](int c) {
+        VecE rq[Cf::NVK], rv[Cf::NVV];
+        const int c0 = c * C;
+        load_rows(rq, qb, c0);
+#pragma unroll
+        for (int n = 0; n < Cf::NVV; ++n) {
+            const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
+            const VecE x = *(const VecE*)(vb + (size_t)(c0 + t) * Dv + min(d0, vcols - VE));
+            rv[n] = d0 < vcols ? x : VecE{};
+        }
+        char* slot = slot_ptr(c);
+        store_rows(rq, (E*)(slot + Cf::OFF_SQ));
+        E* sV = (E*)(slot + Cf::OFF_SV);
+#pragma unroll
+        for (int n = 0; n < Cf::NVV; ++n) {
+            const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
+            *(VecE*)(sV + t * LDV + d0) = rv[n];
+        }
     };
 
     // ------------------------------------------------------------ producers
@@ -251,30 +269,29 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         return ts;
     };
 
-    // Inverse wave: A = diag(beta) (K K^T) (.) Mstrict and T = (I + A)^{-1}.
-    auto build_T = [&](int c) {
+    // A = diag(beta) (K K^T) (.) Mstrict of chunk c, into A buffer c % NABUF.
+    auto build_A = [&](int c) {
         const char* slot = slot_ptr(c);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
-        float* __restrict__ sAt = (float*)(smem + Cf::OFF_A);   // A transposed: sAt[s][r] = A[r][s]
-        float* __restrict__ sTf = (float*)(smem + Cf::OFF_TF);
-        float* __restrict__ sX = (float*)(smem + Cf::OFF_X);
-        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c & 1) * Cf::SZ_TP);
+        float* __restrict__ sAt = (float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
         const TileScalars ts = tile_scalars((const float*)(slot + Cf::OFF_SSC));
-        // K K^T on the three lower tiles; K fragments of both row tiles are
-        // loaded once and serve as both operands. A is stored transposed so
-        // that a column of A is a contiguous row. Decay factors
-        // e^{gamma_r - gamma_s} are only used where s < r.
-        F kf[2][NKS];
+        // K K^T on the three lower tiles; per 32-deep step the K fragments of
+        // both row tiles are loaded once and serve as both operands. A is
+        // stored transposed so that a column of A is a contiguous row. Decay
+        // factors e^{gamma_r - gamma_s} are only used where s < r.
+        f32x4 acc3[3] = {zero4(), zero4(), zero4()};
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-            for (int m = 0; m < NKS; ++m) kf[t2][m] = O::lda(sK, LDK, 16 * t2, 32 * m);
+        for (int m = 0; m < NKS; ++m) {
+            const F k0 = O::lda(sK, LDK, 0, 32 * m);
+            const F k1 = O::lda(sK, LDK, 16, 32 * m);
+            acc3[0] = O::mma(k0, k0, acc3[0]);
+            acc3[1] = O::mma(k1, k0, acc3[1]);
+            acc3[2] = O::mma(k1, k1, acc3[2]);
+        }
 #pragma unroll
         for (int tt = 0; tt < 3; ++tt) {
             const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int m = 0; m < NKS; ++m) acc = O::mma(kf[ti][m], kf[tj][m], acc);
+            const f32x4 acc = acc3[tt];
             const int s = 16 * tj + lc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -283,7 +300,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 sAt[s * LDF + r] = (s < r) ? ts.br[ti][e] * dec * acc[e] : 0.f;
             }
         }
-        wave_lds_fence();
+    };
+
+    // Inverse wave: T = (I + A)^{-1} of chunk c from A buffer c % NABUF.
+    auto build_T = [&](int c) {
+        const float* __restrict__ sAt = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
+        float* __restrict__ sTf = (float*)(smem + Cf::OFF_TF);
+        float* __restrict__ sX = (float*)(smem + Cf::OFF_X);
+        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c & 1) * Cf::SZ_TP);
         // Diagonal 16x16 blocks: lane (d, jc) solves column jc of block d by
         // forward substitution in fp32, x_r -= A[r][s] x_s for s < r, column
         // by column (15 independent updates per step). Column s of A is row s
@@ -497,27 +521,54 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     };
 
     // ------------------------------------------------------------ schedule
-    if (wave >= Cf::W_S) {                       // prologue: chunks 0 and 1
-        for (int c = 0; c < 2 && c < NC; ++c) {
-            stage_load(c);
-            stage_store(c);
+    // Per step i (one barrier): consumers take chunk i; the inverse and P
+    // waves build T and P of chunk i+1; the stagers write chunk i+LEAD. With
+    // AHEAD the P wave also builds A of chunk i+2; otherwise the inverse wave
+    // builds A itself.
+    if (wave == Cf::W_S) {                       // prologue: chunks 0 .. LEAD-1
+        for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
+            KRegs R;
+            stage_k_load(c, R);
+            stage_k_store(c, R);
         }
+    } else if (wave == Cf::W_S + 1) {
+        for (int c = 0; c < Cf::LEAD && c < NC; ++c) stage_qv(c);
     }
     __syncthreads();
-    if (wave == Cf::W_T && NC > 0) build_T(0);
-    if (wave == Cf::W_P && NC > 0) build_P(0);
+    if constexpr (Cf::AHEAD) {
+        if (wave == Cf::W_P) {
+            if (NC > 0) build_P(0);
+            for (int c = 0; c < 2 && c < NC; ++c) build_A(c);
+        }
+        __syncthreads();
+        if (wave == Cf::W_T && NC > 0) build_T(0);
+    } else {
+        if (wave == Cf::W_T && NC > 0) { build_A(0); wave_lds_fence(); build_T(0); }
+        if (wave == Cf::W_P && NC > 0) build_P(0);
+    }
     __syncthreads();
 
     for (int i = 0; i < NC; ++i) {
         if (wave < Cf::NCW) {
             consume(i);
         } else if (wave == Cf::W_T) {
-            if (i + 1 < NC) build_T(i + 1);
+            if (i + 1 < NC) {
+                if constexpr (!Cf::AHEAD) { build_A(i + 1); wave_lds_fence(); }
+                build_T(i + 1);
+            }
         } else if (wave == Cf::W_P) {
             if (i + 1 < NC) build_P(i + 1);
-        } else if (i + 2 < NC) {
-            stage_load(i + 2);
-            stage_store(i + 2);
+            if constexpr (Cf::AHEAD) {
+                if (i + 2 < NC) build_A(i + 2);
+            }
+        } else if (wave == Cf::W_S) {
+            if (i + Cf::LEAD < NC) {
+                KRegs R;
+                stage_k_load(i + Cf::LEAD, R);
+                stage_k_store(i + Cf::LEAD, R);
+            }
+        } else if (i + Cf::LEAD < NC) {
+            stage_qv(i + Cf::LEAD);
         }
         __syncthreads();
     }
