@@ -105,12 +105,17 @@ struct PipeCfg {
     static constexpr int SZ_TP = C * LDP * ES;
     static constexpr int SZ_F = C * LDF * 4;
     static constexpr int SZ_X = 16 * LDX * 4;
-    static constexpr int OFF_T = NSLOT * SZ_SLOT;
-    static constexpr int OFF_P = OFF_T + 2 * SZ_TP;
-    static constexpr int OFF_A = OFF_P + 2 * SZ_TP;
+    // The small T/P/A buffers sit at the bottom of LDS and the input slots
+    // above them, so that their fixed offsets fit the 16-bit immediate offset
+    // of LDS instructions (an address above 64 KiB costs an extra address
+    // register per access).
+    static constexpr int OFF_A = 0;
     static constexpr int OFF_TF = OFF_A + NABUF * SZ_F;
     static constexpr int OFF_X = OFF_TF + SZ_F;
-    static constexpr int LDS_BYTES = OFF_X + SZ_X;
+    static constexpr int OFF_T = OFF_X + SZ_X;
+    static constexpr int OFF_P = OFF_T + 2 * SZ_TP;
+    static constexpr int OFF_SLOTS = OFF_P + 2 * SZ_TP;
+    static constexpr int LDS_BYTES = OFF_SLOTS + NSLOT * SZ_SLOT;
     // scalar arrays inside a slot (floats): gamma, e^gamma, beta, beta e^gamma,
     // e^{gamma_C - gamma}, [0] = e^{gamma_C}
     static constexpr int SC_GAM = 0, SC_EG = C, SC_B = 2 * C, SC_BK = 3 * C, SC_DL = 4 * C,
@@ -175,7 +180,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     float* sb = state + bh * (size_t)Dk * Dv + v0;
     const int NC = S / C;
 
-    auto slot_ptr = [&](int c) { return smem + (c % Cf::NSLOT) * Cf::SZ_SLOT; };
+    auto slot_ptr = [&](int c) { return smem + Cf::OFF_SLOTS + (c % Cf::NSLOT) * Cf::SZ_SLOT; };
 
     // ------------------------------------------------------------ stagers
     // Two stager waves split each chunk: the K stager (wave W_S) moves K, g
@@ -311,34 +316,37 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         // Diagonal 16x16 blocks: lane (d, jc) solves column jc of block d by
         // forward substitution in fp32, x_r -= A[r][s] x_s for s < r, column
         // by column (15 independent updates per step). Column s of A is row s
-        // of the transposed buffer (broadcast reads); columns are loaded two
-        // steps ahead of their use, and scheduling barriers keep the loads
-        // from being hoisted further (register pressure). The result goes to
-        // the fp32 buffer (for the merge) and to the operand buffer.
+        // of the transposed buffer (broadcast reads); each column is loaded
+        // LA steps before its use, and a scheduling barrier per step keeps
+        // the loads from all being hoisted (register pressure).
         if (l < 32) {
+            constexpr int LA = 4;
             const int d = l >> 4, jc = l & 15;
             const float* Atd = sAt + (16 * d) * LDF + 16 * d;
-            auto col = [&](int s2, float* dst) {
+            f32x4 colv[LA + 1][4];
+            auto col = [&](int s2, f32x4* dst) {
 #pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    const f32x4 w = *(const f32x4*)(Atd + s2 * LDF + 4 * c4);
-                    dst[4 * c4] = w[0]; dst[4 * c4 + 1] = w[1];
-                    dst[4 * c4 + 2] = w[2]; dst[4 * c4 + 3] = w[3];
-                }
+                for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4)
+                    dst[c4] = *(const f32x4*)(Atd + s2 * LDF + 4 * c4);
             };
-            float x[16], c0v[16], c1v[16], c2v[16];
+            float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
-            col(0, c0v);
-            col(1, c1v);
+#pragma unroll
+            for (int s2 = 0; s2 < LA; ++s2) col(s2, colv[s2]);
 #pragma unroll
             for (int s2 = 0; s2 < 15; ++s2) {
-                if (s2 + 2 < 15) col(s2 + 2, c2v);
+                if (s2 + LA < 15) col(s2 + LA, colv[(s2 + LA) % (LA + 1)]);
                 const float xs = x[s2];
+                const f32x4* cv = colv[s2 % (LA + 1)];
 #pragma unroll
-                for (int r = s2 + 1; r < 16; ++r) x[r] -= c0v[r] * xs;
+                for (int r = s2 + 1; r < 16; ++r) x[r] -= cv[r >> 2][r & 3] * xs;
+                // Keep every element of the loaded vectors live up to here:
+                // otherwise an unused leading element lets the register
+                // allocator hand its register to another value while the load
+                // is in flight, and the write then waits for the load.
 #pragma unroll
-                for (int r = 0; r < 16; ++r) { c0v[r] = c1v[r]; c1v[r] = c2v[r]; }
+                for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4) asm volatile("" ::"v"(cv[c4]));
                 __builtin_amdgcn_sched_barrier(0);
             }
             float* Td = sTf + (16 * d) * LDF + 16 * d;
