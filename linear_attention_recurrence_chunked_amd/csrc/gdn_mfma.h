@@ -42,6 +42,22 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// hi/lo bf16 pair of two floats: hi = bf16(a), bf16(b) packed (round to
+// nearest even) and lo = bf16(a - hi_a), bf16(b - hi_b). The fp32 values of
+// the hi parts are read off the packed bits (a shift and a mask), so a pair
+// costs two conversions, two bit operations and two subtractions.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    const float ha = __builtin_bit_cast(float, h << 16);
+    const float hb = __builtin_bit_cast(float, h & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2));
+    hi = h;
+}
+
 template <typename E> struct Op;
 
 template <> struct Op<bf16> {
@@ -66,13 +82,13 @@ template <> struct Op<bf16> {
     }
     // B fragment from two accumulator tiles (k block 0 = x0 rows, block 1 = x1 rows).
     __device__ __forceinline__ static void split(f32x4 x0, f32x4 x1, F& hi, F& lo) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            hi[e] = (bf16)x0[e];
-            hi[4 + e] = (bf16)x1[e];
-            lo[e] = (bf16)(x0[e] - (float)hi[e]);
-            lo[4 + e] = (bf16)(x1[e] - (float)hi[4 + e]);
-        }
+        uint32_t h0, h1, h2, h3, w0, w1, w2, w3;
+        split2(x0[0], x0[1], h0, w0);
+        split2(x0[2], x0[3], h1, w1);
+        split2(x1[0], x1[1], h2, w2);
+        split2(x1[2], x1[3], h3, w3);
+        hi = __builtin_bit_cast(F, u32x4{h0, h1, h2, h3});
+        lo = __builtin_bit_cast(F, u32x4{w0, w1, w2, w3});
     }
     __device__ __forceinline__ static f32x4 mma(F a, F b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

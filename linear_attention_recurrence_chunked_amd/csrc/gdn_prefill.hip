@@ -188,15 +188,28 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // W_S + 1) moves Q and V. Loads and stores of a chunk happen in the same
     // step, so no staging registers stay live across the barrier (the
     // register file is shared by all roles).
-    // HBM loads are unconditional, from clamped (in-bounds) addresses, and
-    // out-of-range vectors are zeroed by selection: guarded loads would be
-    // issued one at a time, each waiting out the HBM latency.
+    // Global loads take a uniform row base (scalar registers) plus a 32-bit
+    // lane offset computed once, which maps onto the scalar-base form of the
+    // global load instructions. Full tiles load without further work; at a
+    // ragged edge (Dk < DK) the address is clamped in bounds and the vector
+    // zeroed by selection (guarded loads would be issued one at a time, each
+    // waiting out the HBM latency).
+    constexpr int KPR = DK / VE;                 // 16-byte vectors per K/Q row
+    constexpr int KRI = 64 / KPR;                // rows per load instruction
+    const bool kfull = Dk == DK;
+    const int kd0 = (l % KPR) * VE;
+    const uint32_t koff = (uint32_t)((l / KPR) * Dk + min(kd0, Dk - VE));
     auto load_rows = [&](VecE (&r)[Cf::NVK], const E* src, int c0) {
+        if (kfull) {
 #pragma unroll
-        for (int n = 0; n < Cf::NVK; ++n) {
-            const int id = l + 64 * n, t = id / (DK / VE), d0 = (id % (DK / VE)) * VE;
-            const VecE x = *(const VecE*)(src + (size_t)(c0 + t) * Dk + min(d0, Dk - VE));
-            r[n] = d0 < Dk ? x : VecE{};
+            for (int n = 0; n < Cf::NVK; ++n)
+                r[n] = *(const VecE*)(src + (size_t)(c0 + KRI * n) * Dk + koff);
+        } else {
+#pragma unroll
+            for (int n = 0; n < Cf::NVK; ++n) {
+                const VecE x = *(const VecE*)(src + (size_t)(c0 + KRI * n) * Dk + koff);
+                r[n] = kd0 < Dk ? x : VecE{};
+            }
         }
     };
     auto store_rows = [&](const VecE (&r)[Cf::NVK], E* dst) {
@@ -236,15 +249,25 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
         if (l == 0) sc[Cf::SC_EGC] = __expf(gC);
     };
+    constexpr int VPR = BV / VE;                 // 16-byte vectors per V row of the slice
+    constexpr int VRI = 64 / VPR;
+    const bool vfull = vcols == BV;
+    const int vd0 = (l % VPR) * VE;
+    const uint32_t voff = (uint32_t)((l / VPR) * Dv + min(vd0, vcols - VE));
     auto stage_qv = [&](int c) {
         VecE rq[Cf::NVK], rv[Cf::NVV];
         const int c0 = c * C;
         load_rows(rq, qb, c0);
+        if (vfull) {
 #pragma unroll
-        for (int n = 0; n < Cf::NVV; ++n) {
-            const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
-            const VecE x = *(const VecE*)(vb + (size_t)(c0 + t) * Dv + min(d0, vcols - VE));
-            rv[n] = d0 < vcols ? x : VecE{};
+            for (int n = 0; n < Cf::NVV; ++n)
+                rv[n] = *(const VecE*)(vb + (size_t)(c0 + VRI * n) * Dv + voff);
+        } else {
+#pragma unroll
+            for (int n = 0; n < Cf::NVV; ++n) {
+                const VecE x = *(const VecE*)(vb + (size_t)(c0 + VRI * n) * Dv + voff);
+                rv[n] = vd0 < vcols ? x : VecE{};
+            }
         }
         char* slot = slot_ptr(c);
         store_rows(rq, (E*)(slot + Cf::OFF_SQ));
@@ -356,13 +379,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 Td[r * LDF + jc] = x[r];
                 store_pair<SP>(Tpd + r * LDP + jc, C, x[r]);
             }
-        } else {
-            // the upper 16x16 block of T is zero
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const int id = (l - 32) + 32 * n;
-                store_pair<SP>(Tp + (id >> 4) * LDP + 16 + (id & 15), C, 0.f);
-            }
         }
         wave_lds_fence();
         // Merge: T21 = -T22 (A21 T11), with A21[r][k] read from the transposed buffer
@@ -407,11 +423,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 const float dec = __expf(ts.gr[ti][e] - ts.gs[tj]);
                 store_pair<SP>(Pp + r * LDP + s, C, (s <= r) ? dec * acc[e] : 0.f);
             }
-        }
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {   // the upper 16x16 tile is zero
-            const int id = l + 64 * n;
-            store_pair<SP>(Pp + (id >> 4) * LDP + 16 + (id & 15), C, 0.f);
         }
     };
 
@@ -533,6 +544,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // waves build T and P of chunk i+1; the stagers write chunk i+LEAD. With
     // AHEAD the P wave also builds A of chunk i+2; otherwise the inverse wave
     // builds A itself.
+    // The upper-right 16x16 blocks of T and P are zero for every chunk; they
+    // are written once, for both buffers of each.
+    for (int id = threadIdx.x; id < 4 * 256; id += Cf::THREADS) {
+        const int which = id >> 8, r = (id >> 4) & 15, col = 16 + (id & 15);
+        E* base = (E*)(smem + (which < 2 ? Cf::OFF_T + which * Cf::SZ_TP
+                                         : Cf::OFF_P + (which - 2) * Cf::SZ_TP));
+        store_pair<SP>(base + r * LDP + col, C, 0.f);
+    }
     if (wave == Cf::W_S) {                       // prologue: chunks 0 .. LEAD-1
         for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
             KRegs R;
