@@ -89,8 +89,7 @@ struct PipeCfg {
     static constexpr int LDK = DK + PADE;          // K, Q rows [t][dk]
     static constexpr int LDV = BV + PADE;          // V rows [t][v]
     static constexpr int LDP = (SP ? 2 : 1) * C + PADE;  // T, P rows [t][hi s | lo s]
-    static constexpr int LDF = C + 4;              // fp32 A, T rows
-    static constexpr int LDX = 16 + 4;             // fp32 merge scratch rows
+    static constexpr int ALD = 16 + 4;             // rows of the fp32 16x16 A blocks
     static constexpr int NT = C / 16;
     static constexpr int NKT = DK / 16;
     static constexpr int NKS = DK / 32;
@@ -103,16 +102,18 @@ struct PipeCfg {
     static constexpr int OFF_SK = 0, OFF_SQ = SZ_K, OFF_SV = 2 * SZ_K, OFF_SSC = 2 * SZ_K + SZ_V;
     static constexpr int SZ_SLOT = 2 * SZ_K + SZ_V + SZ_SC;
     static constexpr int SZ_TP = C * LDP * ES;
-    static constexpr int SZ_F = C * LDF * 4;
-    static constexpr int SZ_X = 16 * LDX * 4;
+    // A buffer: three 16 x ALD fp32 blocks, each in the layout its reader
+    // wants: A11 transposed, A22 reversed in both indices, A21 row-major.
+    static constexpr int SZ_F = 3 * 16 * ALD * 4;
+    static constexpr int AB_11T = 0, AB_22R = 16 * ALD, AB_21 = 32 * ALD;   // (floats)
+    static constexpr int SZ_I = 16 * 16 * 4;       // 16x16 identity (inverse start vectors)
     // The small T/P/A buffers sit at the bottom of LDS and the input slots
     // above them, so that their fixed offsets fit the 16-bit immediate offset
     // of LDS instructions (an address above 64 KiB costs an extra address
     // register per access).
     static constexpr int OFF_A = 0;
-    static constexpr int OFF_TF = OFF_A + NABUF * SZ_F;
-    static constexpr int OFF_X = OFF_TF + SZ_F;
-    static constexpr int OFF_T = OFF_X + SZ_X;
+    static constexpr int OFF_I = OFF_A + NABUF * SZ_F;
+    static constexpr int OFF_T = OFF_I + SZ_I;
     static constexpr int OFF_P = OFF_T + 2 * SZ_TP;
     static constexpr int OFF_SLOTS = OFF_P + 2 * SZ_TP;
     static constexpr int LDS_BYTES = OFF_SLOTS + NSLOT * SZ_SLOT;
@@ -124,7 +125,7 @@ struct PipeCfg {
     static_assert(C == 32, "the pipeline is laid out for 32-token chunks");
     static_assert(DK % 32 == 0 && BV % 16 == 0 && BV <= 64, "tile sizes");
     static_assert((C * DK / VE) % 64 == 0 && (C * BV / VE) % 64 == 0, "stager vector split");
-    static_assert((SZ_K | SZ_V | SZ_SC | SZ_TP | SZ_F | SZ_X) % 16 == 0, "16-byte LDS alignment");
+    static_assert((SZ_K | SZ_V | SZ_SC | SZ_TP | SZ_F | SZ_I) % 16 == 0, "16-byte LDS alignment");
     static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KiB LDS of a CU");
 };
 
@@ -140,8 +141,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     using F = typename O::F;
     using VecE = typename Vec16<E>::type;
     constexpr bool SP = Cf::SP;
-    constexpr int VE = Cf::VE, LDK = Cf::LDK, LDV = Cf::LDV, LDP = Cf::LDP, LDF = Cf::LDF;
-    constexpr int LDX = Cf::LDX, NT = Cf::NT, NKT = Cf::NKT, NKS = Cf::NKS;
+    constexpr int VE = Cf::VE, LDK = Cf::LDK, LDV = Cf::LDV, LDP = Cf::LDP, ALD = Cf::ALD;
+    constexpr int NT = Cf::NT, NKT = Cf::NKT, NKS = Cf::NKS;
 
     __shared__ __attribute__((aligned(16))) char smem[Cf::LDS_BYTES];
 
@@ -220,14 +221,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
     };
     struct KRegs { VecE k[Cf::NVK]; float g, b; };
-    auto stage_k_load = [&](int c, KRegs& R) {
+    auto stage_k_load = [&](int c, KRegs& R) __attribute__((always_inline)) {
         load_rows(R.k, kb, c * C);
         const float g = gb[c * C + min(l, C - 1)];
         const float b2 = bb[c * C + min(l, C - 1)];
         R.g = l < C ? g : 0.f;
         R.b = l < C ? b2 : 0.f;
     };
-    auto stage_k_store = [&](int c, const KRegs& R) {
+    auto stage_k_store = [&](int c, const KRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
         store_rows(R.k, (E*)(slot + Cf::OFF_SK));
         // gamma = inclusive cumulative sum of g over the chunk, and the scalars
@@ -254,7 +255,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     const bool vfull = vcols == BV;
     const int vd0 = (l % VPR) * VE;
     const uint32_t voff = (uint32_t)((l / VPR) * Dv + min(vd0, vcols - VE));
-    auto stage_qv = [&](int c) {
+    auto stage_qv = [&](int c) __attribute__((always_inline)) {
         VecE rq[Cf::NVK], rv[Cf::NVV];
         const int c0 = c * C;
         load_rows(rq, qb, c0);
@@ -283,7 +284,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // Per-lane gamma/beta for the rows (16 ti + lr + e) and columns (16 tj + lc)
     // of the three lower 16x16 tiles of a chunk, read once.
     struct TileScalars { float gr[2][4], br[2][4], gs[2]; };
-    auto tile_scalars = [&](const float* __restrict__ sc) {
+    auto tile_scalars = [&](const float* __restrict__ sc) __attribute__((always_inline)) {
         TileScalars ts;
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
@@ -298,14 +299,13 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     };
 
     // A = diag(beta) (K K^T) (.) Mstrict of chunk c, into A buffer c % NABUF.
-    auto build_A = [&](int c) {
+    auto build_A = [&](int c) __attribute__((always_inline)) {
         const char* slot = slot_ptr(c);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
-        float* __restrict__ sAt = (float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
+        float* __restrict__ sA = (float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
         const TileScalars ts = tile_scalars((const float*)(slot + Cf::OFF_SSC));
         // K K^T on the three lower tiles; per 32-deep step the K fragments of
-        // both row tiles are loaded once and serve as both operands. A is
-        // stored transposed so that a column of A is a contiguous row. Decay
+        // both row tiles are loaded once and serve as both operands. Decay
         // factors e^{gamma_r - gamma_s} are only used where s < r.
         f32x4 acc3[3] = {zero4(), zero4(), zero4()};
 #pragma unroll
@@ -316,87 +316,151 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             acc3[1] = O::mma(k1, k0, acc3[1]);
             acc3[2] = O::mma(k1, k1, acc3[2]);
         }
+        // lane (lr/4, lc) holds rows r = lr + e, column s = lc of each tile
+        f32x4 w;
 #pragma unroll
-        for (int tt = 0; tt < 3; ++tt) {
-            const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
-            const f32x4 acc = acc3[tt];
-            const int s = 16 * tj + lc;
+        for (int e = 0; e < 4; ++e) {   // A11, stored transposed: [s][r], one vector per lane
+            const float dec = __expf(ts.gr[0][e] - ts.gs[0]);
+            w[e] = (lc < lr + e) ? ts.br[0][e] * dec * acc3[0][e] : 0.f;
+        }
+        *(f32x4*)(sA + Cf::AB_11T + lc * ALD + lr) = w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * ti + lr + e;
-                const float dec = __expf(ts.gr[ti][e] - ts.gs[tj]);
-                sAt[s * LDF + r] = (s < r) ? ts.br[ti][e] * dec * acc[e] : 0.f;
-            }
+        for (int e = 0; e < 4; ++e) {
+            // A21 row-major: [r][s]
+            const float d21 = __expf(ts.gr[1][e] - ts.gs[0]);
+            sA[Cf::AB_21 + (lr + e) * ALD + lc] = ts.br[1][e] * d21 * acc3[1][e];
+            // A22 reversed: entry [15 - r][15 - s]
+            const float d22 = __expf(ts.gr[1][e] - ts.gs[1]);
+            sA[Cf::AB_22R + (15 - lr - e) * ALD + 15 - lc] =
+                (lc < lr + e) ? ts.br[1][e] * d22 * acc3[2][e] : 0.f;
         }
     };
 
     // Inverse wave: T = (I + A)^{-1} of chunk c from A buffer c % NABUF.
-    auto build_T = [&](int c) {
-        const float* __restrict__ sAt = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
-        float* __restrict__ sTf = (float*)(smem + Cf::OFF_TF);
-        float* __restrict__ sX = (float*)(smem + Cf::OFF_X);
+    //
+    // Diagonal blocks: forward substitution in fp32, both blocks in the same
+    // instructions. Lane (g, n) of half 0 (g = 0, 1) computes column n of
+    // T11 = (I + A11)^{-1}:  x_r = [r = n] - sum_{s<r} A11[r][s] x_s.
+    // Lane (g, n) of half 1 (g = 2, 3) computes row n of T22 in reverse order,
+    // x_r = T22[n][15 - r]; from x^T (I + A22) = e_n^T this obeys
+    //   x_r = [r = 15 - n] - sum_{s<r} A22[15 - s][15 - r] x_s,
+    // the same recurrence with the coefficient block M[s][r] = A22[15-s][15-r]
+    // in place of M[s][r] = A11[r][s]. Row s of M is read as broadcast
+    // vectors, LA steps ahead of its use.
+    //
+    // Merge: T21 = -T22 (A21 T11) on fp32 MFMA (16x16x4, four steps). The
+    // contraction index of step s for lane group g is 4g + s, so the B operand
+    // of X = A21 T11 is T11[4g+s][n] (column n, which half 0 holds) and the A
+    // operand of T22 X is T22[n][4g+s] (row n, which half 1 holds). The two
+    // halves swap the values the other needs with one lane shuffle per step.
+    auto build_T = [&](int c) __attribute__((always_inline)) {
+        const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
+        const float* __restrict__ sI = (const float*)(smem + Cf::OFF_I);
         E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c & 1) * Cf::SZ_TP);
-        // Diagonal 16x16 blocks: lane (d, jc) solves column jc of block d by
-        // forward substitution in fp32, x_r -= A[r][s] x_s for s < r, column
-        // by column (15 independent updates per step). Column s of A is row s
-        // of the transposed buffer (broadcast reads); each column is loaded
-        // LA steps before its use, and a scheduling barrier per step keeps
-        // the loads from all being hoisted (register pressure).
-        if (l < 32) {
-            constexpr int LA = 4;
-            const int d = l >> 4, jc = l & 15;
-            const float* Atd = sAt + (16 * d) * LDF + 16 * d;
-            f32x4 colv[LA + 1][4];
-            auto col = [&](int s2, f32x4* dst) {
+        const int g = l >> 4, n = l & 15, half = l >> 5, godd = g & 1;
+        const float* M = sA + (half ? Cf::AB_22R : Cf::AB_11T);
+        constexpr int LA = 4;
+        f32x4 colv[LA + 1][4];
+        auto col = [&](int s2, f32x4* dst) {
 #pragma unroll
-                for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4)
-                    dst[c4] = *(const f32x4*)(Atd + s2 * LDF + 4 * c4);
-            };
-            float x[16];
+            for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4) dst[c4] = *(const f32x4*)(M + s2 * ALD + 4 * c4);
+        };
+        float x[16];
+        {
+            const float* e0 = sI + (half ? 15 - n : n) * 16;   // unit start vector
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
-#pragma unroll
-            for (int s2 = 0; s2 < LA; ++s2) col(s2, colv[s2]);
-#pragma unroll
-            for (int s2 = 0; s2 < 15; ++s2) {
-                if (s2 + LA < 15) col(s2 + LA, colv[(s2 + LA) % (LA + 1)]);
-                const float xs = x[s2];
-                const f32x4* cv = colv[s2 % (LA + 1)];
-#pragma unroll
-                for (int r = s2 + 1; r < 16; ++r) x[r] -= cv[r >> 2][r & 3] * xs;
-                // Keep every element of the loaded vectors live up to here:
-                // otherwise an unused leading element lets the register
-                // allocator hand its register to another value while the load
-                // is in flight, and the write then waits for the load.
-#pragma unroll
-                for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4) asm volatile("" ::"v"(cv[c4]));
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            float* Td = sTf + (16 * d) * LDF + 16 * d;
-            E* Tpd = Tp + (16 * d) * LDP + 16 * d;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                Td[r * LDF + jc] = x[r];
-                store_pair<SP>(Tpd + r * LDP + jc, C, x[r]);
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 w = *(const f32x4*)(e0 + 4 * q);
+                x[4 * q] = w[0]; x[4 * q + 1] = w[1]; x[4 * q + 2] = w[2]; x[4 * q + 3] = w[3];
             }
         }
-        wave_lds_fence();
-        // Merge: T21 = -T22 (A21 T11), with A21[r][k] read from the transposed buffer
-        f32x4 acc = zero4();
+        const f32x4 a21 = *(const f32x4*)(sA + Cf::AB_21 + n * ALD + 4 * g);   // A21[n][4g..4g+3]
 #pragma unroll
-        for (int k0 = 0; k0 < 16; k0 += 4) acc = mma_f32_tm(acc, sAt, LDF, 16, sTf, LDF, 0, k0);
+        for (int s2 = 0; s2 < LA; ++s2) col(s2, colv[s2]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sX[(lr + e) * LDX + lc] = acc[e];
-        wave_lds_fence();
-        acc = zero4();
+        for (int s2 = 0; s2 < 15; ++s2) {
+            if (s2 + LA < 15) col(s2 + LA, colv[(s2 + LA) % (LA + 1)]);
+            const float xs = x[s2];
+            const f32x4* cv = colv[s2 % (LA + 1)];
 #pragma unroll
-        for (int k0 = 0; k0 < 16; k0 += 4) acc = mma_f32_rm(acc, sTf + 16, LDF, 16, sX, LDX, 0, k0);
+            for (int r = s2 + 1; r < 16; ++r) x[r] -= cv[r >> 2][r & 3] * xs;
+            // Keep every element of the loaded vectors live up to here:
+            // otherwise an unused leading element lets the register allocator
+            // hand its register to another value while the load is in flight,
+            // and the write then waits for the load.
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store_pair<SP>(Tp + (16 + lr + e) * LDP + lc, C, -acc[e]);
+            for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4) asm volatile("" ::"v"(cv[c4]));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Merge operands: half 0 sends T11[8+4g+s][n] (for lane group g+2),
+        // half 1 sends T22[n][4(g-2)+s] (for lane group g-2).
+        float b11[4], a22[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const float send = half ? (godd ? x[11 - s2] : x[15 - s2]) : (godd ? x[12 + s2] : x[8 + s2]);
+            const float recv = __shfl_xor(send, 32);
+            b11[s2] = half ? recv : (godd ? x[4 + s2] : x[s2]);
+            a22[s2] = half ? (godd ? x[3 - s2] : x[7 - s2]) : recv;
+        }
+        f32x4 X = zero4();
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) X = __builtin_amdgcn_mfma_f32_16x16x4f32(a21[s2], b11[s2], X, 0, 0, 0);
+        f32x4 Y = zero4();
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a22[s2], X[s2], Y, 0, 0, 0);
+        // Stores into the T buffer ([t][hi s | lo s] rows; fp32: [t][s]).
+        if constexpr (SP) {
+            uint32_t h[8], w2[8];
+            if (half == 0) {
+                // column n of T11: lane group 0 writes the hi parts, group 1 the lo parts
+#pragma unroll
+                for (int i = 0; i < 8; ++i) split2(x[2 * i], x[2 * i + 1], h[i], w2[i]);
+                uint16_t* p = (uint16_t*)(Tp + n + (godd ? C : 0));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t u = godd ? w2[i] : h[i];
+                    p[(2 * i) * LDP] = (uint16_t)u;
+                    p[(2 * i + 1) * LDP] = (uint16_t)(u >> 16);
+                }
+            } else {
+                // row n of T22: T[16+n][16+j] = x[15-j]; group 2 writes hi, group 3 lo
+#pragma unroll
+                for (int i = 0; i < 8; ++i) split2(x[15 - 2 * i], x[14 - 2 * i], h[i], w2[i]);
+                u32x4* p = (u32x4*)(Tp + (16 + n) * LDP + 16 + (godd ? C : 0));
+                p[0] = godd ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{h[0], h[1], h[2], h[3]};
+                p[1] = godd ? u32x4{w2[4], w2[5], w2[6], w2[7]} : u32x4{h[4], h[5], h[6], h[7]};
+            }
+            // T21 rows 16 + 4g + e, column n
+            uint32_t th[2], tl[2];
+            split2(-Y[0], -Y[1], th[0], tl[0]);
+            split2(-Y[2], -Y[3], th[1], tl[1]);
+            uint16_t* q = (uint16_t*)(Tp + (16 + 4 * g) * LDP + n);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                q[(2 * i) * LDP] = (uint16_t)th[i];
+                q[(2 * i + 1) * LDP] = (uint16_t)(th[i] >> 16);
+                q[(2 * i) * LDP + C] = (uint16_t)tl[i];
+                q[(2 * i + 1) * LDP + C] = (uint16_t)(tl[i] >> 16);
+            }
+        } else {
+            if (half == 0) {
+                if (!godd) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) Tp[r * LDP + n] = x[r];
+                }
+            } else {
+                f32x4* p = (f32x4*)(Tp + (16 + n) * LDP + 16 + (godd ? 8 : 0));
+                const int o = godd ? 7 : 15;   // x[o], x[o-1], ...
+                p[0] = f32x4{x[o], x[o - 1], x[o - 2], x[o - 3]};
+                p[1] = f32x4{x[o - 4], x[o - 5], x[o - 6], x[o - 7]};
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Tp[(16 + 4 * g + e) * LDP + n] = -Y[e];
+        }
     };
 
     // P wave: P = Q K^T (.) Mincl.
-    auto build_P = [&](int c) {
+    auto build_P = [&](int c) __attribute__((always_inline)) {
         const char* slot = slot_ptr(c);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
         const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
@@ -438,7 +502,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             accS[kt][e] = (vok && dk < Dk) ? sb[(size_t)dk * Dv + vl] : 0.f;
         }
     }
-    auto consume = [&](int i) {
+    auto consume = [&](int i) __attribute__((always_inline)) {
         const char* slot = slot_ptr(i);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
         const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
@@ -552,6 +616,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                                          : Cf::OFF_P + (which - 2) * Cf::SZ_TP));
         store_pair<SP>(base + r * LDP + col, C, 0.f);
     }
+    for (int id = threadIdx.x; id < 256; id += Cf::THREADS)
+        ((float*)(smem + Cf::OFF_I))[id] = (id >> 4) == (id & 15) ? 1.f : 0.f;
     if (wave == Cf::W_S) {                       // prologue: chunks 0 .. LEAD-1
         for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
             KRegs R;
