@@ -117,7 +117,7 @@ struct PipeCfg {
     static constexpr int OFF_P = OFF_T + 2 * SZ_TP;
     static constexpr int OFF_SLOTS = OFF_P + 2 * SZ_TP;
     static constexpr int LDS_BYTES = OFF_SLOTS + NSLOT * SZ_SLOT;
-    // scalar arrays inside a slot (floats): gamma, e^gamma, beta, beta e^gamma,
+    // scalar arrays inside a slot (floats): gamma, scale e^gamma, beta, beta e^gamma,
     // e^{gamma_C - gamma}, [0] = e^{gamma_C}
     static constexpr int SC_GAM = 0, SC_EG = C, SC_B = 2 * C, SC_BK = 3 * C, SC_DL = 4 * C,
                          SC_EGC = 5 * C;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         if (l < C) {
             const float eg = __expf(x);
             sc[Cf::SC_GAM + l] = x;
-            sc[Cf::SC_EG + l] = eg;
+            sc[Cf::SC_EG + l] = scale * eg;
             sc[Cf::SC_B + l] = R.b;
             sc[Cf::SC_BK + l] = R.b * eg;
             sc[Cf::SC_DL + l] = __expf(gC - x);   // gC <= x: never overflows
@@ -459,7 +459,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
     };
 
-    // P wave: P = Q K^T (.) Mincl.
+    // P wave: P = scale (Q K^T (.) Mincl).
     auto build_P = [&](int c) __attribute__((always_inline)) {
         const char* slot = slot_ptr(c);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
@@ -485,7 +485,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * ti + lr + e;
                 const float dec = __expf(ts.gr[ti][e] - ts.gs[tj]);
-                store_pair<SP>(Pp + r * LDP + s, C, (s <= r) ? dec * acc[e] : 0.f);
+                store_pair<SP>(Pp + r * LDP + s, C, (s <= r) ? scale * dec * acc[e] : 0.f);
             }
         }
     };
@@ -493,16 +493,9 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // ------------------------------------------------------------ consumers
     const int vl = 16 * wave + lc;             // column of this lane within the slice
     const bool vok = wave < Cf::NCW && vl < vcols;
-    f32x4 accS[NKT];                           // state rows 16 kt + lr + e, column vl
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int dk = 16 * kt + lr + e;
-            accS[kt][e] = (vok && dk < Dk) ? sb[(size_t)dk * Dv + vl] : 0.f;
-        }
-    }
-    auto consume = [&](int i) __attribute__((always_inline)) {
+    const bool wok = wave < Cf::NCW && 16 * wave < vcols;   // this wave's 16 output columns exist
+    // accS[kt]: state rows 16 kt + lr + e, column vl, held for the whole sequence
+    auto consume = [&](int i, f32x4 (&accS)[NKT]) __attribute__((always_inline)) {
         const char* slot = slot_ptr(i);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
         const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
@@ -512,20 +505,22 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         const E* __restrict__ Pp = (const E*)(smem + Cf::OFF_P + (i & 1) * Cf::SZ_TP);
         const int c0 = i * C;
         // per-row scalars and V values of this lane's rows t = 16 ti + lr + e, read once
-        float vv[NT][4], bt[NT][4], bk[NT][4], eg[NT][4], dl[NT][4];
+        float vv[NT][4], bt[NT][4], bk[NT][4], dl[NT][4], egt[NT];
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti)
+        for (int ti = 0; ti < NT; ++ti) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * ti + lr + e;
                 vv[ti][e] = to_f32(sV[t * LDV + vl]);
                 bt[ti][e] = sc[Cf::SC_B + t];
                 bk[ti][e] = sc[Cf::SC_BK + t];
-                eg[ti][e] = sc[Cf::SC_EG + t];
                 dl[ti][e] = sc[Cf::SC_DL + t];
             }
+            egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];   // scale e^gamma of token 16 ti + lc
+        }
         const float egC = sc[Cf::SC_EGC];
-        // K S0 and Q S0 with S0 from registers
+        // K S0 ([token][value column] tiles) and (Q S0)^T ([value column][token]
+        // tiles: the same fragments with the operands swapped), S0 from registers
         f32x4 ks[NT], qs[NT];
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) { ks[ti] = zero4(); qs[ti] = zero4(); }
@@ -539,10 +534,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 const F qa = O::lda(sQ, LDK, 16 * ti, 32 * m);
                 if constexpr (SP) {
                     ks[ti] = O::mma(ka, sl, ks[ti]);
-                    qs[ti] = O::mma(qa, sl, qs[ti]);
+                    qs[ti] = O::mma(sl, qa, qs[ti]);
                 }
                 ks[ti] = O::mma(ka, sh, ks[ti]);
-                qs[ti] = O::mma(qa, sh, qs[ti]);
+                qs[ti] = O::mma(sh, qa, qs[ti]);
             }
         }
         // R = beta V - beta e^gamma (K S0)
@@ -565,26 +560,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             }
             u[ti] = O::mma(th, rh, u[ti]);
         }
-        // O = scale (e^gamma Q S0 + P U)
-        F uh, ul;
-        O::split(u[0], u[1], uh, ul);
-#pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
-            f32x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = qs[ti][e] * eg[ti][e];
-            const F ph = O::lda(Pp, LDP, 16 * ti, 0);
-            if constexpr (SP) {
-                o = O::mma(O::lda(Pp, LDP, 16 * ti, C), uh, o);
-                o = O::mma(ph, ul, o);
-            }
-            o = O::mma(ph, uh, o);
-            if (vok) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ob[(size_t)(c0 + 16 * ti + lr + e) * Dv + vl] = from_f32<E>(scale * o[e]);
-            }
-        }
         // S = e^{gamma_C} S0 + K^T diag(e^{gamma_C - gamma}) U
         f32x4 ud[NT];
 #pragma unroll
@@ -600,6 +575,31 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             for (int e = 0; e < 4; ++e) accS[kt][e] *= egC;
             if constexpr (SP) accS[kt] = O::mma(ka, dlo, accS[kt]);
             accS[kt] = O::mma(ka, dh, accS[kt]);
+        }
+        // O^T = (Q S0)^T diag(scale e^gamma) + U^T P^T (P carries the scale):
+        // lane (g, n) holds 4 consecutive value columns 4g.. of token 16 ti + n,
+        // stored as one vector.
+        F uh, ul;
+        O::split(u[0], u[1], uh, ul);
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = qs[ti][e] * egt[ti];
+            const F ph = O::lda(Pp, LDP, 16 * ti, 0);
+            if constexpr (SP) {
+                o = O::mma(uh, O::lda(Pp, LDP, 16 * ti, C), o);
+                o = O::mma(ul, ph, o);
+            }
+            o = O::mma(uh, ph, o);
+            if (wok) {
+                E* dst = ob + (size_t)(c0 + 16 * ti + lc) * Dv + 16 * wave + lr;
+                if constexpr (SP) {
+                    *(bf16x4*)dst = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+                } else {
+                    *(f32x4*)dst = o;
+                }
+            }
         }
     };
 
@@ -641,40 +641,62 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     }
     __syncthreads();
 
-    for (int i = 0; i < NC; ++i) {
-        if (wave < Cf::NCW) {
-            consume(i);
-        } else if (wave == Cf::W_T) {
+    // Each role runs its own loop over the chunks with one barrier per step,
+    // so values a role carries from step to step occupy registers only in
+    // that role's code.
+    if (wave < Cf::NCW) {
+        f32x4 accS[NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int dk = 16 * kt + lr + e;
+                accS[kt][e] = (vok && dk < Dk) ? sb[(size_t)dk * Dv + vl] : 0.f;
+            }
+        }
+        for (int i = 0; i < NC; ++i) {
+            consume(i, accS);
+            __syncthreads();
+        }
+        if (vok) {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int dk = 16 * kt + lr + e;
+                    if (dk < Dk) sb[(size_t)dk * Dv + vl] = accS[kt][e];
+                }
+        }
+    } else if (wave == Cf::W_T) {
+        for (int i = 0; i < NC; ++i) {
             if (i + 1 < NC) {
                 if constexpr (!Cf::AHEAD) { build_A(i + 1); wave_lds_fence(); }
                 build_T(i + 1);
             }
-        } else if (wave == Cf::W_P) {
+            __syncthreads();
+        }
+    } else if (wave == Cf::W_P) {
+        for (int i = 0; i < NC; ++i) {
             if (i + 1 < NC) build_P(i + 1);
             if constexpr (Cf::AHEAD) {
                 if (i + 2 < NC) build_A(i + 2);
             }
-        } else if (wave == Cf::W_S) {
+            __syncthreads();
+        }
+    } else if (wave == Cf::W_S) {
+        for (int i = 0; i < NC; ++i) {
             if (i + Cf::LEAD < NC) {
                 KRegs R;
                 stage_k_load(i + Cf::LEAD, R);
                 stage_k_store(i + Cf::LEAD, R);
             }
-        } else if (i + Cf::LEAD < NC) {
-            stage_qv(i + Cf::LEAD);
+            __syncthreads();
         }
-        __syncthreads();
-    }
-
-    // ---- final state
-    if (vok) {
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int dk = 16 * kt + lr + e;
-                if (dk < Dk) sb[(size_t)dk * Dv + vl] = accS[kt][e];
-            }
+    } else {
+        for (int i = 0; i < NC; ++i) {
+            if (i + Cf::LEAD < NC) stage_qv(i + Cf::LEAD);
+            __syncthreads();
+        }
     }
 }
 
