@@ -255,28 +255,30 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     const bool vfull = vcols == BV;
     const int vd0 = (l % VPR) * VE;
     const uint32_t voff = (uint32_t)((l / VPR) * Dv + min(vd0, vcols - VE));
-    auto stage_qv = [&](int c) __attribute__((always_inline)) {
-        VecE rq[Cf::NVK], rv[Cf::NVV];
+    struct QVRegs { VecE q[Cf::NVK], v[Cf::NVV]; };
+    auto stage_qv_load = [&](int c, QVRegs& R) __attribute__((always_inline)) {
         const int c0 = c * C;
-        load_rows(rq, qb, c0);
+        load_rows(R.q, qb, c0);
         if (vfull) {
 #pragma unroll
             for (int n = 0; n < Cf::NVV; ++n)
-                rv[n] = *(const VecE*)(vb + (size_t)(c0 + VRI * n) * Dv + voff);
+                R.v[n] = *(const VecE*)(vb + (size_t)(c0 + VRI * n) * Dv + voff);
         } else {
 #pragma unroll
             for (int n = 0; n < Cf::NVV; ++n) {
                 const VecE x = *(const VecE*)(vb + (size_t)(c0 + VRI * n) * Dv + voff);
-                rv[n] = vd0 < vcols ? x : VecE{};
+                R.v[n] = vd0 < vcols ? x : VecE{};
             }
         }
+    };
+    auto stage_qv_store = [&](int c, const QVRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
-        store_rows(rq, (E*)(slot + Cf::OFF_SQ));
+        store_rows(R.q, (E*)(slot + Cf::OFF_SQ));
         E* sV = (E*)(slot + Cf::OFF_SV);
 #pragma unroll
         for (int n = 0; n < Cf::NVV; ++n) {
             const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
-            *(VecE*)(sV + t * LDV + d0) = rv[n];
+            *(VecE*)(sV + t * LDV + d0) = R.v[n];
         }
     };
 
@@ -625,7 +627,11 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             stage_k_store(c, R);
         }
     } else if (wave == Cf::W_S + 1) {
-        for (int c = 0; c < Cf::LEAD && c < NC; ++c) stage_qv(c);
+        for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
+            QVRegs R;
+            stage_qv_load(c, R);
+            stage_qv_store(c, R);
+        }
     }
     __syncthreads();
     if constexpr (Cf::AHEAD) {
@@ -684,18 +690,35 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             __syncthreads();
         }
     } else if (wave == Cf::W_S) {
-        for (int i = 0; i < NC; ++i) {
-            if (i + Cf::LEAD < NC) {
-                KRegs R;
-                stage_k_load(i + Cf::LEAD, R);
-                stage_k_store(i + Cf::LEAD, R);
-            }
+        // Loads are issued a full step before their data is stored: at step i
+        // the loads of chunk i + LEAD + 1 go out first, then chunk i + LEAD
+        // (loaded during step i - 1) is stored. Two register sets alternate
+        // (the loop is unrolled by two), so the HBM latency passes during the
+        // rest of the step and the barrier instead of inside the store.
+        KRegs Ra, Rb;
+        if (Cf::LEAD < NC) stage_k_load(Cf::LEAD, Ra);
+        for (int i = 0; i < NC; i += 2) {
+            if (i + Cf::LEAD + 1 < NC) stage_k_load(i + Cf::LEAD + 1, Rb);
+            if (i + Cf::LEAD < NC) stage_k_store(i + Cf::LEAD, Ra);
             __syncthreads();
+            if (i + 1 < NC) {
+                if (i + Cf::LEAD + 2 < NC) stage_k_load(i + Cf::LEAD + 2, Ra);
+                if (i + Cf::LEAD + 1 < NC) stage_k_store(i + Cf::LEAD + 1, Rb);
+                __syncthreads();
+            }
         }
     } else {
-        for (int i = 0; i < NC; ++i) {
-            if (i + Cf::LEAD < NC) stage_qv(i + Cf::LEAD);
+        QVRegs Ra, Rb;
+        if (Cf::LEAD < NC) stage_qv_load(Cf::LEAD, Ra);
+        for (int i = 0; i < NC; i += 2) {
+            if (i + Cf::LEAD + 1 < NC) stage_qv_load(i + Cf::LEAD + 1, Rb);
+            if (i + Cf::LEAD < NC) stage_qv_store(i + Cf::LEAD, Ra);
             __syncthreads();
+            if (i + 1 < NC) {
+                if (i + Cf::LEAD + 2 < NC) stage_qv_load(i + Cf::LEAD + 2, Ra);
+                if (i + Cf::LEAD + 1 < NC) stage_qv_store(i + Cf::LEAD + 1, Rb);
+                __syncthreads();
+            }
         }
     }
 }
