@@ -52,6 +52,9 @@
 
 namespace gdn {
 
+// Fourth word of a raw buffer resource (32-bit data format; no swizzle).
+constexpr int kBufDword3 = 0x00020000;
+
 template <typename E> struct Vec16;  // one 16-byte vector of E
 template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int N = 8; };
 template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
@@ -73,18 +76,22 @@ struct PipeCfg {
     static constexpr int ES = (int)sizeof(E);
     static constexpr int VE = Vec16<E>::N;
     static constexpr int NCW = BV / 16;            // consumer waves (16 value columns each)
-    static constexpr int W_T = NCW;                // inverse wave
-    static constexpr int W_P = NCW + 1;            // P wave
-    static constexpr int W_S = NCW + 2;            // first of two stager waves
-    static constexpr int NW = NCW + 4;
+    // SPREAD (bf16 path): two inverse waves take alternate chunks and spread
+    // the inverse of a chunk over two steps (substitution, then merge and
+    // stores), and an A wave builds A three chunks ahead. Without SPREAD
+    // (fp32 path, whose tiles are twice as large) one inverse wave builds A
+    // and T of a chunk in one step.
+    static constexpr bool SPREAD = SP;
+    static constexpr int NTW = SPREAD ? 2 : 1;     // inverse waves
+    static constexpr int W_T = NCW;                // first inverse wave
+    static constexpr int W_P = W_T + NTW;          // P wave
+    static constexpr int W_A = SPREAD ? W_P + 1 : -1;   // A wave
+    static constexpr int W_S = SPREAD ? W_P + 2 : W_P + 1;   // first of two stager waves
+    static constexpr int NW = W_S + 2;
     static constexpr int THREADS = 64 * NW;
-    // AHEAD: the masked K K^T (A) of a chunk is built by the P wave one chunk
-    // before its inverse, so the inverse wave only solves. It costs a fourth
-    // input slot and a second A buffer, which fit LDS on the bf16 path.
-    static constexpr bool AHEAD = SP;
-    static constexpr int NSLOT = AHEAD ? 4 : 3;    // chunks i .. i+NSLOT-1 resident
+    static constexpr int NSLOT = SPREAD ? 5 : 3;   // chunks i .. i+NSLOT-1 resident
     static constexpr int LEAD = NSLOT - 1;         // the stagers write chunk i+LEAD
-    static constexpr int NABUF = AHEAD ? 2 : 1;
+    static constexpr int NABUF = SPREAD ? 3 : 1;   // A of chunks i+1 .. i+3
     static constexpr int PADE = SP ? 8 : 4;        // row padding (elements): 16-byte rows
     static constexpr int LDK = DK + PADE;          // K, Q rows [t][dk]
     static constexpr int LDV = BV + PADE;          // V rows [t][v]
@@ -189,51 +196,48 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // W_S + 1) moves Q and V. Loads and stores of a chunk happen in the same
     // step, so no staging registers stay live across the barrier (the
     // register file is shared by all roles).
-    // Global loads take a uniform row base (scalar registers) plus a 32-bit
-    // lane offset computed once, which maps onto the scalar-base form of the
-    // global load instructions. Full tiles load without further work; at a
-    // ragged edge (Dk < DK) the address is clamped in bounds and the vector
-    // zeroed by selection (guarded loads would be issued one at a time, each
-    // waiting out the HBM latency).
+    // Global loads are buffer loads: a buffer resource per stream (scalar
+    // registers), a uniform row offset (scalar) and a 32-bit lane offset
+    // computed once, clamped in bounds (Dk < DK). No per-load address
+    // registers, no branches: the store that follows a step later waits only
+    // for its own loads. Vectors past a ragged edge are zeroed when stored.
     constexpr int KPR = DK / VE;                 // 16-byte vectors per K/Q row
     constexpr int KRI = 64 / KPR;                // rows per load instruction
     const bool kfull = Dk == DK;
     const int kd0 = (l % KPR) * VE;
-    const uint32_t koff = (uint32_t)((l / KPR) * Dk + min(kd0, Dk - VE));
-    auto load_rows = [&](VecE (&r)[Cf::NVK], const E* src, int c0) {
-        if (kfull) {
+    const uint32_t koff = (uint32_t)(((l / KPR) * Dk + min(kd0, Dk - VE)) * Cf::ES);
+    const int nrec_k = S * Dk * Cf::ES;
+    const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, nrec_k, kBufDword3);
+    const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, nrec_k, kBufDword3);
+    auto load_rows = [&](VecE (&r)[Cf::NVK], __amdgpu_buffer_rsrc_t rs, int c0) __attribute__((always_inline)) {
 #pragma unroll
-            for (int n = 0; n < Cf::NVK; ++n)
-                r[n] = *(const VecE*)(src + (size_t)(c0 + KRI * n) * Dk + koff);
-        } else {
-#pragma unroll
-            for (int n = 0; n < Cf::NVK; ++n) {
-                const VecE x = *(const VecE*)(src + (size_t)(c0 + KRI * n) * Dk + koff);
-                r[n] = kd0 < Dk ? x : VecE{};
-            }
-        }
+        for (int n = 0; n < Cf::NVK; ++n)
+            r[n] = __builtin_bit_cast(VecE, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rs, koff, (c0 + KRI * n) * Dk * Cf::ES, 0));
     };
-    auto store_rows = [&](const VecE (&r)[Cf::NVK], E* dst) {
+    auto store_rows = [&](const VecE (&r)[Cf::NVK], E* dst) __attribute__((always_inline)) {
+        const bool z = !kfull && kd0 >= Dk;
 #pragma unroll
         for (int n = 0; n < Cf::NVK; ++n) {
             const int id = l + 64 * n, t = id / (DK / VE), d0 = (id % (DK / VE)) * VE;
-            *(VecE*)(dst + t * LDK + d0) = r[n];
+            *(VecE*)(dst + t * LDK + d0) = z ? VecE{} : r[n];
         }
     };
     struct KRegs { VecE k[Cf::NVK]; float g, b; };
+    const uint32_t goff = (uint32_t)min(l, C - 1) * 4;
+    const __amdgpu_buffer_rsrc_t rs_g = __builtin_amdgcn_make_buffer_rsrc((void*)gb, (short)0, S * 4, kBufDword3);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)bb, (short)0, S * 4, kBufDword3);
     auto stage_k_load = [&](int c, KRegs& R) __attribute__((always_inline)) {
-        load_rows(R.k, kb, c * C);
-        const float g = gb[c * C + min(l, C - 1)];
-        const float b2 = bb[c * C + min(l, C - 1)];
-        R.g = l < C ? g : 0.f;
-        R.b = l < C ? b2 : 0.f;
+        load_rows(R.k, rs_k, c * C);
+        R.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_g, goff, c * C * 4, 0));
+        R.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_b, goff, c * C * 4, 0));
     };
     auto stage_k_store = [&](int c, const KRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
         store_rows(R.k, (E*)(slot + Cf::OFF_SK));
         // gamma = inclusive cumulative sum of g over the chunk, and the scalars
         float* sc = (float*)(slot + Cf::OFF_SSC);
-        float x = R.g;
+        float x = l < C ? R.g : 0.f;
 #pragma unroll
         for (int off = 1; off < C; off <<= 1) {
             const float y = __shfl_up(x, off);
@@ -254,31 +258,27 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     constexpr int VRI = 64 / VPR;
     const bool vfull = vcols == BV;
     const int vd0 = (l % VPR) * VE;
-    const uint32_t voff = (uint32_t)((l / VPR) * Dv + min(vd0, vcols - VE));
+    const uint32_t voff = (uint32_t)(((l / VPR) * Dv + min(vd0, vcols - VE)) * Cf::ES);
+    const __amdgpu_buffer_rsrc_t rs_v =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, (S * Dv - v0) * Cf::ES, kBufDword3);
     struct QVRegs { VecE q[Cf::NVK], v[Cf::NVV]; };
     auto stage_qv_load = [&](int c, QVRegs& R) __attribute__((always_inline)) {
         const int c0 = c * C;
-        load_rows(R.q, qb, c0);
-        if (vfull) {
+        load_rows(R.q, rs_q, c0);
 #pragma unroll
-            for (int n = 0; n < Cf::NVV; ++n)
-                R.v[n] = *(const VecE*)(vb + (size_t)(c0 + VRI * n) * Dv + voff);
-        } else {
-#pragma unroll
-            for (int n = 0; n < Cf::NVV; ++n) {
-                const VecE x = *(const VecE*)(vb + (size_t)(c0 + VRI * n) * Dv + voff);
-                R.v[n] = vd0 < vcols ? x : VecE{};
-            }
-        }
+        for (int n = 0; n < Cf::NVV; ++n)
+            R.v[n] = __builtin_bit_cast(VecE, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs_v, voff, (c0 + VRI * n) * Dv * Cf::ES, 0));
     };
     auto stage_qv_store = [&](int c, const QVRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
         store_rows(R.q, (E*)(slot + Cf::OFF_SQ));
         E* sV = (E*)(slot + Cf::OFF_SV);
+        const bool z = !vfull && vd0 >= vcols;
 #pragma unroll
         for (int n = 0; n < Cf::NVV; ++n) {
             const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
-            *(VecE*)(sV + t * LDV + d0) = R.v[n];
+            *(VecE*)(sV + t * LDV + d0) = z ? VecE{} : R.v[n];
         }
     };
 
@@ -355,11 +355,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // of X = A21 T11 is T11[4g+s][n] (column n, which half 0 holds) and the A
     // operand of T22 X is T22[n][4g+s] (row n, which half 1 holds). The two
     // halves swap the values the other needs with one lane shuffle per step.
-    auto build_T = [&](int c) __attribute__((always_inline)) {
+    const int g = l >> 4, n = l & 15, half = l >> 5, godd = g & 1;   // inverse-wave lane roles
+    auto t_solve = [&](int c, float (&x)[16]) __attribute__((always_inline)) {
         const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
         const float* __restrict__ sI = (const float*)(smem + Cf::OFF_I);
-        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c & 1) * Cf::SZ_TP);
-        const int g = l >> 4, n = l & 15, half = l >> 5, godd = g & 1;
         const float* M = sA + (half ? Cf::AB_22R : Cf::AB_11T);
         constexpr int LA = 4;
         f32x4 colv[LA + 1][4];
@@ -367,7 +366,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
             for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4) dst[c4] = *(const f32x4*)(M + s2 * ALD + 4 * c4);
         };
-        float x[16];
         {
             const float* e0 = sI + (half ? 15 - n : n) * 16;   // unit start vector
 #pragma unroll
@@ -376,7 +374,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 x[4 * q] = w[0]; x[4 * q + 1] = w[1]; x[4 * q + 2] = w[2]; x[4 * q + 3] = w[3];
             }
         }
-        const f32x4 a21 = *(const f32x4*)(sA + Cf::AB_21 + n * ALD + 4 * g);   // A21[n][4g..4g+3]
 #pragma unroll
         for (int s2 = 0; s2 < LA; ++s2) col(s2, colv[s2]);
 #pragma unroll
@@ -394,15 +391,28 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4) asm volatile("" ::"v"(cv[c4]));
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+    auto t_merge = [&](int c, const float (&x)[16]) __attribute__((always_inline)) {
+        const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
+        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c & 1) * Cf::SZ_TP);
+        const f32x4 a21 = *(const f32x4*)(sA + Cf::AB_21 + n * ALD + 4 * g);   // A21[n][4g..4g+3]
         // Merge operands: half 0 sends T11[8+4g+s][n] (for lane group g+2),
         // half 1 sends T22[n][4(g-2)+s] (for lane group g-2).
         float b11[4], a22[4];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-            const float send = half ? (godd ? x[11 - s2] : x[15 - s2]) : (godd ? x[12 + s2] : x[8 + s2]);
+            // The candidates are pinned to registers first: a lane-dependent
+            // choice between array elements would otherwise become a choice
+            // of address and push x out to scratch memory.
+            float v[8] = {x[s2], x[4 + s2], x[8 + s2], x[12 + s2],
+                          x[15 - s2], x[11 - s2], x[7 - s2], x[3 - s2]};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) asm("" : "+v"(v[q]));
+            const float send = half ? (godd ? v[5] : v[4]) : (godd ? v[3] : v[2]);
             const float recv = __shfl_xor(send, 32);
-            b11[s2] = half ? recv : (godd ? x[4 + s2] : x[s2]);
-            a22[s2] = half ? (godd ? x[3 - s2] : x[7 - s2]) : recv;
+            b11[s2] = half ? recv : (godd ? v[1] : v[0]);
+            a22[s2] = half ? (godd ? v[7] : v[6]) : recv;
         }
         f32x4 X = zero4();
 #pragma unroll
@@ -606,12 +616,20 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     };
 
     // ------------------------------------------------------------ schedule
-    // Per step i (one barrier): consumers take chunk i; the inverse and P
-    // waves build T and P of chunk i+1; the stagers write chunk i+LEAD. With
-    // AHEAD the P wave also builds A of chunk i+2; otherwise the inverse wave
-    // builds A itself.
+    // Each role runs its own program: three prologue barriers, then one
+    // barrier per step i = 0 .. NC-1. Values a role carries from step to step
+    // occupy registers only in that role's code.
+    //   consumers         chunk i
+    //   P wave            P of chunk i+1
+    //   stagers           store chunk i+LEAD (loaded during step i-1), load chunk i+LEAD+1
+    //  SPREAD:
+    //   A wave            A of chunk i+3
+    //   inverse wave i%2  substitution for chunk i+2 (result kept in registers)
+    //   other inverse     merge and T stores for chunk i+1
+    //  otherwise:
+    //   inverse wave      A, substitution, merge and T stores for chunk i+1
     // The upper-right 16x16 blocks of T and P are zero for every chunk; they
-    // are written once, for both buffers of each.
+    // are written once, for both buffers of each; so is the identity table.
     for (int id = threadIdx.x; id < 4 * 256; id += Cf::THREADS) {
         const int which = id >> 8, r = (id >> 4) & 15, col = 16 + (id & 15);
         E* base = (E*)(smem + (which < 2 ? Cf::OFF_T + which * Cf::SZ_TP
@@ -620,36 +638,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     }
     for (int id = threadIdx.x; id < 256; id += Cf::THREADS)
         ((float*)(smem + Cf::OFF_I))[id] = (id >> 4) == (id & 15) ? 1.f : 0.f;
-    if (wave == Cf::W_S) {                       // prologue: chunks 0 .. LEAD-1
-        for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
-            KRegs R;
-            stage_k_load(c, R);
-            stage_k_store(c, R);
-        }
-    } else if (wave == Cf::W_S + 1) {
-        for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
-            QVRegs R;
-            stage_qv_load(c, R);
-            stage_qv_store(c, R);
-        }
-    }
-    __syncthreads();
-    if constexpr (Cf::AHEAD) {
-        if (wave == Cf::W_P) {
-            if (NC > 0) build_P(0);
-            for (int c = 0; c < 2 && c < NC; ++c) build_A(c);
-        }
-        __syncthreads();
-        if (wave == Cf::W_T && NC > 0) build_T(0);
-    } else {
-        if (wave == Cf::W_T && NC > 0) { build_A(0); wave_lds_fence(); build_T(0); }
-        if (wave == Cf::W_P && NC > 0) build_P(0);
-    }
-    __syncthreads();
 
-    // Each role runs its own loop over the chunks with one barrier per step,
-    // so values a role carries from step to step occupy registers only in
-    // that role's code.
     if (wave < Cf::NCW) {
         f32x4 accS[NKT];
 #pragma unroll
@@ -660,6 +649,9 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 accS[kt][e] = (vok && dk < Dk) ? sb[(size_t)dk * Dv + vl] : 0.f;
             }
         }
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
         for (int i = 0; i < NC; ++i) {
             consume(i, accS);
             __syncthreads();
@@ -673,20 +665,47 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                     if (dk < Dk) sb[(size_t)dk * Dv + vl] = accS[kt][e];
                 }
         }
-    } else if (wave == Cf::W_T) {
+    } else if (wave < Cf::W_T + Cf::NTW) {
+        const int pw = wave - Cf::W_T;
+        float x[16];
+        __syncthreads();
+        if constexpr (!Cf::SPREAD) {
+            if (NC > 0) { build_A(0); wave_lds_fence(); t_solve(0, x); t_merge(0, x); }
+        }
+        __syncthreads();
+        if constexpr (Cf::SPREAD) {
+            if (pw == 0 && NC > 0) { t_solve(0, x); t_merge(0, x); }
+            if (pw == 1 && NC > 1) t_solve(1, x);
+        }
+        __syncthreads();
         for (int i = 0; i < NC; ++i) {
-            if (i + 1 < NC) {
-                if constexpr (!Cf::AHEAD) { build_A(i + 1); wave_lds_fence(); }
-                build_T(i + 1);
+            if constexpr (Cf::SPREAD) {
+                if ((i & 1) == pw) {
+                    if (i + 2 < NC) t_solve(i + 2, x);
+                } else {
+                    if (i + 1 < NC) t_merge(i + 1, x);
+                }
+            } else {
+                if (i + 1 < NC) { build_A(i + 1); wave_lds_fence(); t_solve(i + 1, x); t_merge(i + 1, x); }
             }
             __syncthreads();
         }
     } else if (wave == Cf::W_P) {
+        __syncthreads();
+        if (NC > 0) build_P(0);
+        __syncthreads();
+        __syncthreads();
         for (int i = 0; i < NC; ++i) {
             if (i + 1 < NC) build_P(i + 1);
-            if constexpr (Cf::AHEAD) {
-                if (i + 2 < NC) build_A(i + 2);
-            }
+            __syncthreads();
+        }
+    } else if (wave == Cf::W_A) {
+        __syncthreads();
+        for (int c = 0; c < 3 && c < NC; ++c) build_A(c);
+        __syncthreads();
+        __syncthreads();
+        for (int i = 0; i < NC; ++i) {
+            if (i + 3 < NC) build_A(i + 3);
             __syncthreads();
         }
     } else if (wave == Cf::W_S) {
@@ -695,27 +714,43 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         // (loaded during step i - 1) is stored. Two register sets alternate
         // (the loop is unrolled by two), so the HBM latency passes during the
         // rest of the step and the barrier instead of inside the store.
+        for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
+            KRegs R;
+            stage_k_load(c, R);
+            stage_k_store(c, R);
+        }
         KRegs Ra, Rb;
-        if (Cf::LEAD < NC) stage_k_load(Cf::LEAD, Ra);
+        stage_k_load(min(Cf::LEAD, NC - 1), Ra);
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
         for (int i = 0; i < NC; i += 2) {
-            if (i + Cf::LEAD + 1 < NC) stage_k_load(i + Cf::LEAD + 1, Rb);
+            stage_k_load(min(i + Cf::LEAD + 1, NC - 1), Rb);   // past the end: a harmless reload
             if (i + Cf::LEAD < NC) stage_k_store(i + Cf::LEAD, Ra);
             __syncthreads();
             if (i + 1 < NC) {
-                if (i + Cf::LEAD + 2 < NC) stage_k_load(i + Cf::LEAD + 2, Ra);
+                stage_k_load(min(i + Cf::LEAD + 2, NC - 1), Ra);
                 if (i + Cf::LEAD + 1 < NC) stage_k_store(i + Cf::LEAD + 1, Rb);
                 __syncthreads();
             }
         }
     } else {
+        for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
+            QVRegs R;
+            stage_qv_load(c, R);
+            stage_qv_store(c, R);
+        }
         QVRegs Ra, Rb;
-        if (Cf::LEAD < NC) stage_qv_load(Cf::LEAD, Ra);
+        stage_qv_load(min(Cf::LEAD, NC - 1), Ra);
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
         for (int i = 0; i < NC; i += 2) {
-            if (i + Cf::LEAD + 1 < NC) stage_qv_load(i + Cf::LEAD + 1, Rb);
+            stage_qv_load(min(i + Cf::LEAD + 1, NC - 1), Rb);   // past the end: a harmless reload
             if (i + Cf::LEAD < NC) stage_qv_store(i + Cf::LEAD, Ra);
             __syncthreads();
             if (i + 1 < NC) {
-                if (i + Cf::LEAD + 2 < NC) stage_qv_load(i + Cf::LEAD + 2, Ra);
+                stage_qv_load(min(i + Cf::LEAD + 2, NC - 1), Ra);
                 if (i + Cf::LEAD + 1 < NC) stage_qv_store(i + Cf::LEAD + 1, Rb);
                 __syncthreads();
             }
