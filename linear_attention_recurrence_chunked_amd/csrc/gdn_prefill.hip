@@ -52,6 +52,10 @@
 
 namespace gdn {
 
+// Scheduling-barrier mask that lets ALU, VALU, SALU and MFMA instructions
+// move across it while memory instructions stay on their side.
+constexpr int kComputeMayCross = 0x000F;
+
 // Fourth word of a raw buffer resource (32-bit data format; no swizzle).
 constexpr int kBufDword3 = 0x00020000;
 
@@ -531,27 +535,56 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];   // scale e^gamma of token 16 ti + lc
         }
         const float egC = sc[Cf::SC_EGC];
+        // LDS operands are read one stage ahead of the products that use them
+        // (the next 32-deep slice of K and Q, then T, then the transposed K
+        // tiles and P); a scheduling barrier after each batch of reads keeps
+        // the compiler from sinking them back next to their use, while
+        // arithmetic is still free to move across it.
         // K S0 ([token][value column] tiles) and (Q S0)^T ([value column][token]
         // tiles: the same fragments with the operands swapped), S0 from registers
         f32x4 ks[NT], qs[NT];
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) { ks[ti] = zero4(); qs[ti] = zero4(); }
+        F kf[2][NT], qf[2][NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            kf[0][ti] = O::lda(sK, LDK, 16 * ti, 0);
+            qf[0][ti] = O::lda(sQ, LDK, 16 * ti, 0);
+        }
+        F tf[NT][2];
 #pragma unroll
         for (int m = 0; m < NKS; ++m) {
+            const int cb = m & 1, nb = cb ^ 1;
+            if (m + 1 < NKS) {
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti) {
+                    kf[nb][ti] = O::lda(sK, LDK, 16 * ti, 32 * (m + 1));
+                    qf[nb][ti] = O::lda(sQ, LDK, 16 * ti, 32 * (m + 1));
+                }
+            } else {
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti) {
+                    tf[ti][0] = O::lda(Tp, LDP, 16 * ti, 0);
+                    if constexpr (SP) tf[ti][1] = O::lda(Tp, LDP, 16 * ti, C);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(kComputeMayCross);
             F sh, sl;
             O::split(accS[2 * m], accS[2 * m + 1], sh, sl);
 #pragma unroll
             for (int ti = 0; ti < NT; ++ti) {
-                const F ka = O::lda(sK, LDK, 16 * ti, 32 * m);
-                const F qa = O::lda(sQ, LDK, 16 * ti, 32 * m);
                 if constexpr (SP) {
-                    ks[ti] = O::mma(ka, sl, ks[ti]);
-                    qs[ti] = O::mma(sl, qa, qs[ti]);
+                    ks[ti] = O::mma(kf[cb][ti], sl, ks[ti]);
+                    qs[ti] = O::mma(sl, qf[cb][ti], qs[ti]);
                 }
-                ks[ti] = O::mma(ka, sh, ks[ti]);
-                qs[ti] = O::mma(sh, qa, qs[ti]);
+                ks[ti] = O::mma(kf[cb][ti], sh, ks[ti]);
+                qs[ti] = O::mma(sh, qf[cb][ti], qs[ti]);
             }
         }
+        // first transposed K tile of the state update
+        F kt_f[2];
+        kt_f[0] = O::lda_t(sK, LDK, 0, 0);
+        __builtin_amdgcn_sched_barrier(kComputeMayCross);
         // R = beta V - beta e^gamma (K S0)
         f32x4 r[NT];
 #pragma unroll
@@ -564,13 +597,12 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         f32x4 u[NT];
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) {
-            const F th = O::lda(Tp, LDP, 16 * ti, 0);
             u[ti] = zero4();
             if constexpr (SP) {
-                u[ti] = O::mma(O::lda(Tp, LDP, 16 * ti, C), rh, u[ti]);
-                u[ti] = O::mma(th, rl, u[ti]);
+                u[ti] = O::mma(tf[ti][1], rh, u[ti]);
+                u[ti] = O::mma(tf[ti][0], rl, u[ti]);
             }
-            u[ti] = O::mma(th, rh, u[ti]);
+            u[ti] = O::mma(tf[ti][0], rh, u[ti]);
         }
         // S = e^{gamma_C} S0 + K^T diag(e^{gamma_C - gamma}) U
         f32x4 ud[NT];
@@ -580,13 +612,23 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             for (int e = 0; e < 4; ++e) ud[ti][e] = u[ti][e] * dl[ti][e];
         F dh, dlo;
         O::split(ud[0], ud[1], dh, dlo);
+        F pf[NT][2];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
-            const F ka = O::lda_t(sK, LDK, 16 * kt, 0);
+            if (kt + 1 < NKT) {
+                kt_f[(kt + 1) & 1] = O::lda_t(sK, LDK, 16 * (kt + 1), 0);
+            } else {
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti) {
+                    pf[ti][0] = O::lda(Pp, LDP, 16 * ti, 0);
+                    if constexpr (SP) pf[ti][1] = O::lda(Pp, LDP, 16 * ti, C);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(kComputeMayCross);
 #pragma unroll
             for (int e = 0; e < 4; ++e) accS[kt][e] *= egC;
-            if constexpr (SP) accS[kt] = O::mma(ka, dlo, accS[kt]);
-            accS[kt] = O::mma(ka, dh, accS[kt]);
+            if constexpr (SP) accS[kt] = O::mma(kt_f[kt & 1], dlo, accS[kt]);
+            accS[kt] = O::mma(kt_f[kt & 1], dh, accS[kt]);
         }
         // O^T = (Q S0)^T diag(scale e^gamma) + U^T P^T (P carries the scale):
         // lane (g, n) holds 4 consecutive value columns 4g.. of token 16 ti + n,
@@ -598,12 +640,11 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             f32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = qs[ti][e] * egt[ti];
-            const F ph = O::lda(Pp, LDP, 16 * ti, 0);
             if constexpr (SP) {
-                o = O::mma(uh, O::lda(Pp, LDP, 16 * ti, C), o);
-                o = O::mma(ul, ph, o);
+                o = O::mma(uh, pf[ti][1], o);
+                o = O::mma(ul, pf[ti][0], o);
             }
-            o = O::mma(uh, ph, o);
+            o = O::mma(uh, pf[ti][0], o);
             if (wok) {
                 E* dst = ob + (size_t)(c0 + 16 * ti + lc) * Dv + 16 * wave + lr;
                 if constexpr (SP) {
