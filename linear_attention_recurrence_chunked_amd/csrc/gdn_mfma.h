@@ -1,15 +1,25 @@
 // gdn_mfma.h -- matrix-core (MFMA) operand helpers for gfx950.
 //
-// All products are built from 16x16 fp32 output tiles contracted 32 deep.
-// The contraction index of a 32-deep step is split into two 16-blocks, and
-// lane l (group g = l/16) supplies the k values {4g .. 4g+3} of block 0 and
-// {16+4g .. 16+4g+3} of block 1. That is exactly the row set a lane holds in
-// the 16x16 fp32 accumulator layout (rows 4g + e, e = 0..3, column l%16), so
-// an accumulator tile pair can be fed back as the B operand of the next
-// product straight from registers, with no LDS round trip. A operands are
-// read from LDS with the same k mapping, either from a row-major [m][k]
-// buffer (two 8-byte reads per lane) or transposed from a row-major [k][m]
-// buffer (gfx950 LDS transpose reads).
+// All products are built from 16x16 fp32 output tiles contracted 32 deep. In
+// a 32-deep step lane l (group g = l/16) supplies eight contraction indices,
+// and any assignment works as long as both operands use the same one. Two
+// assignments are used:
+//
+//  * token contractions (T R, P U, K^T U): lane group g supplies k =
+//    {4g .. 4g+3} and {16+4g .. 16+4g+3}, exactly the rows a lane holds in
+//    a pair of 16x16 accumulator tiles (rows 4g + e, e = 0..3, column l%16),
+//    so computed tiles feed the next product straight from registers. The
+//    LDS side (T, P) is stored with its columns permuted (tpos) so that the
+//    eight values a lane needs are contiguous: one 16-byte read.
+//  * key-dimension contractions (K S, Q S, K K^T, Q K^T): lane group g
+//    supplies k = 8g .. 8g+7 of the 32-deep step, a contiguous 16-byte piece
+//    of a K or Q row. The state tiles kept in registers are produced with
+//    their rows permuted (spos) so that a pair of them supplies exactly those
+//    rows as the state operand.
+//
+// 16-byte fragment reads replace pairs of 8-byte reads: the compiler would
+// merge such a pair into one ds_read2_b64, which runs about four times slower
+// than two plain reads on gfx950 for these lane patterns.
 //
 // bf16: one v_mfma_f32_16x16x32_bf16 per step; computed operands are carried
 //       as a pair hi = bf16(x), lo = bf16(x - hi) and a product of pairs is
@@ -25,6 +35,15 @@
 namespace gdn {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Stored column of token s (0..31) in a T or P row: the values lane group g
+// needs, s = 4g..4g+3 and 16+4g..16+4g+3, sit at columns 8g .. 8g+7.
+__host__ __device__ constexpr int tpos(int s) { return 8 * ((s & 15) >> 2) + 4 * (s >> 4) + (s & 3); }
+
+// Key row held by element e of lane group g in state tile kt: the tile pair
+// (2m, 2m+1) holds rows 32m + 8g + 0..7, the contiguous slice lane group g
+// supplies in key-dimension contractions.
+__host__ __device__ constexpr int spos(int kt, int g, int e) { return 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + e; }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -64,18 +83,19 @@ template <> struct Op<bf16> {
     static constexpr bool SPLIT = true;
     typedef bf16x8 F;   // one 32-deep operand fragment
 
-    // A[r0 + l%16][k0 + {4g..4g+3, 16+4g..16+4g+3}] from row-major A.
-    __device__ __forceinline__ static F lda(const bf16* A, int ld, int r0, int k0) {
+    // A[r0 + l%16][k0 + 8g .. k0 + 8g + 7]: one 16-byte read from row-major A.
+    __device__ __forceinline__ static F ldc(const bf16* A, int ld, int r0, int k0) {
         const int l = lane_id();
-        const bf16* p = A + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
-        const bf16x4 a = *(const bf16x4*)p;
-        const bf16x4 b = *(const bf16x4*)(p + 16);
-        return F{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        return *(const F*)(A + (r0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
     }
-    // (X^T)[m0 + l%16][k0 + ...] for row-major X[k][m], via transposed reads.
-    __device__ __forceinline__ static F lda_t(const bf16* X, int ld, int m0, int k0) {
+    // Transposed state-update operand for state tile kt: row i of the result
+    // is key index spos(kt, i/4, i%4) = 32(kt/2) + 8(i/4) + 4(kt%2) + i%4,
+    // contraction over the tokens k0 + {4g.., 16+4g..} of row-major X[t][dk].
+    // Lane j of a 16-lane group points the transpose read at row 4g + j/4,
+    // key columns 32(kt/2) + 8(j%4) + 4(kt%2) .. +3.
+    __device__ __forceinline__ static F ldt(const bf16* X, int ld, int kt, int k0) {
         const int l = lane_id(), g = l >> 4, j = l & 15;
-        const bf16* p = X + (k0 + 4 * g + (j >> 2)) * ld + m0 + 4 * (j & 3);
+        const bf16* p = X + (k0 + 4 * g + (j >> 2)) * ld + 32 * (kt >> 1) + 4 * (kt & 1) + 8 * (j & 3);
         const bf16x4 a = lds_read_tr(p);
         const bf16x4 b = lds_read_tr(p + 16 * ld);
         return F{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -101,17 +121,18 @@ template <> struct Op<float> {
     static constexpr bool SPLIT = false;
     typedef F8 F;
 
-    __device__ __forceinline__ static F lda(const float* A, int ld, int r0, int k0) {
+    __device__ __forceinline__ static F ldc(const float* A, int ld, int r0, int k0) {
         const int l = lane_id();
-        const float* p = A + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
-        F a;
+        const float* p = A + (r0 + (l & 15)) * ld + k0 + 8 * (l >> 4);
+        const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+        F r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { a.v[e] = p[e]; a.v[4 + e] = p[16 + e]; }
-        return a;
+        for (int e = 0; e < 4; ++e) { r.v[e] = a[e]; r.v[4 + e] = b[e]; }
+        return r;
     }
-    __device__ __forceinline__ static F lda_t(const float* X, int ld, int m0, int k0) {
-        const int l = lane_id();
-        const float* p = X + (k0 + 4 * (l >> 4)) * ld + m0 + (l & 15);
+    __device__ __forceinline__ static F ldt(const float* X, int ld, int kt, int k0) {
+        const int l = lane_id(), j = l & 15;
+        const float* p = X + (k0 + 4 * (l >> 4)) * ld + 32 * (kt >> 1) + 8 * (j >> 2) + 4 * (kt & 1) + (j & 3);
         F a;
 #pragma unroll
         for (int e = 0; e < 4; ++e) { a.v[e] = p[e * ld]; a.v[4 + e] = p[(16 + e) * ld]; }

@@ -96,10 +96,13 @@ struct PipeCfg {
     static constexpr int NSLOT = SPREAD ? 5 : 3;   // chunks i .. i+NSLOT-1 resident
     static constexpr int LEAD = NSLOT - 1;         // the stagers write chunk i+LEAD
     static constexpr int NABUF = SPREAD ? 3 : 1;   // A of chunks i+1 .. i+3
-    static constexpr int PADE = SP ? 8 : 4;        // row padding (elements): 16-byte rows
-    static constexpr int LDK = DK + PADE;          // K, Q rows [t][dk]
+    // Row strides (elements), chosen so that the 16-byte fragment reads and
+    // the transpose reads of each buffer spread over the LDS banks (on the
+    // bf16 path: K/Q rows of 72 dwords, T/P rows of 40 dwords).
+    static constexpr int PADE = SP ? 8 : 4;
+    static constexpr int LDK = DK + (SP ? 16 : 4); // K, Q rows [t][dk]
     static constexpr int LDV = BV + PADE;          // V rows [t][v]
-    static constexpr int LDP = (SP ? 2 : 1) * C + PADE;  // T, P rows [t][hi s | lo s]
+    static constexpr int LDP = SP ? 2 * C + 16 : C + 4;  // T, P rows [t][hi tpos(s) | lo tpos(s)]
     static constexpr int ALD = 16 + 4;             // rows of the fp32 16x16 A blocks
     static constexpr int NT = C / 16;
     static constexpr int NKT = DK / 16;
@@ -316,8 +319,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         f32x4 acc3[3] = {zero4(), zero4(), zero4()};
 #pragma unroll
         for (int m = 0; m < NKS; ++m) {
-            const F k0 = O::lda(sK, LDK, 0, 32 * m);
-            const F k1 = O::lda(sK, LDK, 16, 32 * m);
+            const F k0 = O::ldc(sK, LDK, 0, 32 * m);
+            const F k1 = O::ldc(sK, LDK, 16, 32 * m);
             acc3[0] = O::mma(k0, k0, acc3[0]);
             acc3[1] = O::mma(k1, k0, acc3[1]);
             acc3[2] = O::mma(k1, k1, acc3[2]);
@@ -424,54 +427,62 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         f32x4 Y = zero4();
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a22[s2], X[s2], Y, 0, 0, 0);
-        // Stores into the T buffer ([t][hi s | lo s] rows; fp32: [t][s]).
+        // Stores into the T buffer: rows [t][hi tpos(s) | lo tpos(s)] (fp32: [t][tpos(s)]).
         if constexpr (SP) {
-            uint32_t h[8], w2[8];
             if (half == 0) {
                 // column n of T11: lane group 0 writes the hi parts, group 1 the lo parts
+                uint32_t h[8], w2[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) split2(x[2 * i], x[2 * i + 1], h[i], w2[i]);
-                uint16_t* p = (uint16_t*)(Tp + n + (godd ? C : 0));
+                for (int i2 = 0; i2 < 8; ++i2) split2(x[2 * i2], x[2 * i2 + 1], h[i2], w2[i2]);
+                uint16_t* p = (uint16_t*)(Tp + tpos(n) + (godd ? C : 0));
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t u = godd ? w2[i] : h[i];
-                    p[(2 * i) * LDP] = (uint16_t)u;
-                    p[(2 * i + 1) * LDP] = (uint16_t)(u >> 16);
+                for (int i2 = 0; i2 < 8; ++i2) {
+                    const uint32_t u = godd ? w2[i2] : h[i2];
+                    p[(2 * i2) * LDP] = (uint16_t)u;
+                    p[(2 * i2 + 1) * LDP] = (uint16_t)(u >> 16);
                 }
             } else {
-                // row n of T22: T[16+n][16+j] = x[15-j]; group 2 writes hi, group 3 lo
+                // row n of T22: T[16+n][16+4a+b] = x[15-4a-b], stored at column 8a+4+b;
+                // group 2 writes hi, group 3 lo
+                E* p = Tp + (16 + n) * LDP + 4 + (godd ? C : 0);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) split2(x[15 - 2 * i], x[14 - 2 * i], h[i], w2[i]);
-                u32x4* p = (u32x4*)(Tp + (16 + n) * LDP + 16 + (godd ? C : 0));
-                p[0] = godd ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{h[0], h[1], h[2], h[3]};
-                p[1] = godd ? u32x4{w2[4], w2[5], w2[6], w2[7]} : u32x4{h[4], h[5], h[6], h[7]};
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    uint32_t h0, l0, h1, l1;
+                    split2(x[15 - 4 * a4], x[14 - 4 * a4], h0, l0);
+                    split2(x[13 - 4 * a4], x[12 - 4 * a4], h1, l1);
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    *(u32x2*)(p + 8 * a4) = godd ? u32x2{l0, l1} : u32x2{h0, h1};
+                }
             }
             // T21 rows 16 + 4g + e, column n
             uint32_t th[2], tl[2];
             split2(-Y[0], -Y[1], th[0], tl[0]);
             split2(-Y[2], -Y[3], th[1], tl[1]);
-            uint16_t* q = (uint16_t*)(Tp + (16 + 4 * g) * LDP + n);
+            uint16_t* q = (uint16_t*)(Tp + (16 + 4 * g) * LDP + tpos(n));
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                q[(2 * i) * LDP] = (uint16_t)th[i];
-                q[(2 * i + 1) * LDP] = (uint16_t)(th[i] >> 16);
-                q[(2 * i) * LDP + C] = (uint16_t)tl[i];
-                q[(2 * i + 1) * LDP + C] = (uint16_t)(tl[i] >> 16);
+            for (int i2 = 0; i2 < 2; ++i2) {
+                q[(2 * i2) * LDP] = (uint16_t)th[i2];
+                q[(2 * i2 + 1) * LDP] = (uint16_t)(th[i2] >> 16);
+                q[(2 * i2) * LDP + C] = (uint16_t)tl[i2];
+                q[(2 * i2 + 1) * LDP + C] = (uint16_t)(tl[i2] >> 16);
             }
         } else {
             if (half == 0) {
                 if (!godd) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) Tp[r * LDP + n] = x[r];
+                    for (int r = 0; r < 16; ++r) Tp[r * LDP + tpos(n)] = x[r];
                 }
             } else {
-                f32x4* p = (f32x4*)(Tp + (16 + n) * LDP + 16 + (godd ? 8 : 0));
-                const int o = godd ? 7 : 15;   // x[o], x[o-1], ...
-                p[0] = f32x4{x[o], x[o - 1], x[o - 2], x[o - 3]};
-                p[1] = f32x4{x[o - 4], x[o - 5], x[o - 6], x[o - 7]};
+                // row n of T22: columns 8a+4 .. 8a+7 hold T22[n][4a .. 4a+3] = x[15-4a], ..;
+                // group 2 writes a = 0, 1, group 3 a = 2, 3
+#pragma unroll
+                for (int a2 = 0; a2 < 2; ++a2) {
+                    const int a4 = 2 * godd + a2, o = 15 - 4 * a4;
+                    *(f32x4*)(Tp + (16 + n) * LDP + 8 * a4 + 4) = f32x4{x[o], x[o - 1], x[o - 2], x[o - 3]};
+                }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Tp[(16 + 4 * g + e) * LDP + n] = -Y[e];
+            for (int e = 0; e < 4; ++e) Tp[(16 + 4 * g + e) * LDP + tpos(n)] = -Y[e];
         }
     };
 
@@ -487,8 +498,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-                kf[t2][m] = O::lda(sK, LDK, 16 * t2, 32 * m);
-                qf[t2][m] = O::lda(sQ, LDK, 16 * t2, 32 * m);
+                kf[t2][m] = O::ldc(sK, LDK, 16 * t2, 32 * m);
+                qf[t2][m] = O::ldc(sQ, LDK, 16 * t2, 32 * m);
             }
 #pragma unroll
         for (int tt = 0; tt < 3; ++tt) {
@@ -501,7 +512,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * ti + lr + e;
                 const float dec = __expf(ts.gr[ti][e] - ts.gs[tj]);
-                store_pair<SP>(Pp + r * LDP + s, C, (s <= r) ? scale * dec * acc[e] : 0.f);
+                store_pair<SP>(Pp + r * LDP + tpos(s), C, (s <= r) ? scale * dec * acc[e] : 0.f);
             }
         }
     };
@@ -510,7 +521,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     const int vl = 16 * wave + lc;             // column of this lane within the slice
     const bool vok = wave < Cf::NCW && vl < vcols;
     const bool wok = wave < Cf::NCW && 16 * wave < vcols;   // this wave's 16 output columns exist
-    // accS[kt]: state rows 16 kt + lr + e, column vl, held for the whole sequence
+    // accS[kt]: state rows spos(kt, lr/4, e), column vl, held for the whole sequence
     auto consume = [&](int i, f32x4 (&accS)[NKT]) __attribute__((always_inline)) {
         const char* slot = slot_ptr(i);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
@@ -548,8 +559,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         F kf[2][NT], qf[2][NT];
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) {
-            kf[0][ti] = O::lda(sK, LDK, 16 * ti, 0);
-            qf[0][ti] = O::lda(sQ, LDK, 16 * ti, 0);
+            kf[0][ti] = O::ldc(sK, LDK, 16 * ti, 0);
+            qf[0][ti] = O::ldc(sQ, LDK, 16 * ti, 0);
         }
         F tf[NT][2];
 #pragma unroll
@@ -558,14 +569,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             if (m + 1 < NKS) {
 #pragma unroll
                 for (int ti = 0; ti < NT; ++ti) {
-                    kf[nb][ti] = O::lda(sK, LDK, 16 * ti, 32 * (m + 1));
-                    qf[nb][ti] = O::lda(sQ, LDK, 16 * ti, 32 * (m + 1));
+                    kf[nb][ti] = O::ldc(sK, LDK, 16 * ti, 32 * (m + 1));
+                    qf[nb][ti] = O::ldc(sQ, LDK, 16 * ti, 32 * (m + 1));
                 }
             } else {
 #pragma unroll
                 for (int ti = 0; ti < NT; ++ti) {
-                    tf[ti][0] = O::lda(Tp, LDP, 16 * ti, 0);
-                    if constexpr (SP) tf[ti][1] = O::lda(Tp, LDP, 16 * ti, C);
+                    tf[ti][0] = O::ldc(Tp, LDP, 16 * ti, 0);
+                    if constexpr (SP) tf[ti][1] = O::ldc(Tp, LDP, 16 * ti, C);
                 }
             }
             __builtin_amdgcn_sched_barrier(kComputeMayCross);
@@ -583,7 +594,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
         // first transposed K tile of the state update
         F kt_f[2];
-        kt_f[0] = O::lda_t(sK, LDK, 0, 0);
+        kt_f[0] = O::ldt(sK, LDK, 0, 0);
         __builtin_amdgcn_sched_barrier(kComputeMayCross);
         // R = beta V - beta e^gamma (K S0)
         f32x4 r[NT];
@@ -616,12 +627,12 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
             if (kt + 1 < NKT) {
-                kt_f[(kt + 1) & 1] = O::lda_t(sK, LDK, 16 * (kt + 1), 0);
+                kt_f[(kt + 1) & 1] = O::ldt(sK, LDK, kt + 1, 0);
             } else {
 #pragma unroll
                 for (int ti = 0; ti < NT; ++ti) {
-                    pf[ti][0] = O::lda(Pp, LDP, 16 * ti, 0);
-                    if constexpr (SP) pf[ti][1] = O::lda(Pp, LDP, 16 * ti, C);
+                    pf[ti][0] = O::ldc(Pp, LDP, 16 * ti, 0);
+                    if constexpr (SP) pf[ti][1] = O::ldc(Pp, LDP, 16 * ti, C);
                 }
             }
             __builtin_amdgcn_sched_barrier(kComputeMayCross);
@@ -672,7 +683,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // The upper-right 16x16 blocks of T and P are zero for every chunk; they
     // are written once, for both buffers of each; so is the identity table.
     for (int id = threadIdx.x; id < 4 * 256; id += Cf::THREADS) {
-        const int which = id >> 8, r = (id >> 4) & 15, col = 16 + (id & 15);
+        const int which = id >> 8, r = (id >> 4) & 15, col = tpos(16 + (id & 15));
         E* base = (E*)(smem + (which < 2 ? Cf::OFF_T + which * Cf::SZ_TP
                                          : Cf::OFF_P + (which - 2) * Cf::SZ_TP));
         store_pair<SP>(base + r * LDP + col, C, 0.f);
@@ -686,7 +697,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int dk = 16 * kt + lr + e;
+                const int dk = spos(kt, lr >> 2, e);
                 accS[kt][e] = (vok && dk < Dk) ? sb[(size_t)dk * Dv + vl] : 0.f;
             }
         }
@@ -702,7 +713,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int dk = 16 * kt + lr + e;
+                    const int dk = spos(kt, lr >> 2, e);
                     if (dk < Dk) sb[(size_t)dk * Dv + vl] = accS[kt][e];
                 }
         }
