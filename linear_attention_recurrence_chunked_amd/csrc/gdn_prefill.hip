@@ -128,7 +128,8 @@ struct PipeCfg {
     static constexpr int OFF_A = 0;
     static constexpr int OFF_I = OFF_A + NABUF * SZ_F;
     static constexpr int OFF_T = OFF_I + SZ_I;
-    static constexpr int OFF_P = OFF_T + 2 * SZ_TP;
+    static constexpr int NTBUF = SPREAD ? 3 : 2;   // T of chunks i .. i+NTBUF-1
+    static constexpr int OFF_P = OFF_T + NTBUF * SZ_TP;
     static constexpr int OFF_SLOTS = OFF_P + 2 * SZ_TP;
     static constexpr int LDS_BYTES = OFF_SLOTS + NSLOT * SZ_SLOT;
     // scalar arrays inside a slot (floats): gamma, scale e^gamma, beta, beta e^gamma,
@@ -398,36 +399,9 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4) asm volatile("" ::"v"(cv[c4]));
             __builtin_amdgcn_sched_barrier(0);
         }
-    };
-
-    auto t_merge = [&](int c, const float (&x)[16]) __attribute__((always_inline)) {
-        const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
-        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c & 1) * Cf::SZ_TP);
-        const f32x4 a21 = *(const f32x4*)(sA + Cf::AB_21 + n * ALD + 4 * g);   // A21[n][4g..4g+3]
-        // Merge operands: half 0 sends T11[8+4g+s][n] (for lane group g+2),
-        // half 1 sends T22[n][4(g-2)+s] (for lane group g-2).
-        float b11[4], a22[4];
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-            // The candidates are pinned to registers first: a lane-dependent
-            // choice between array elements would otherwise become a choice
-            // of address and push x out to scratch memory.
-            float v[8] = {x[s2], x[4 + s2], x[8 + s2], x[12 + s2],
-                          x[15 - s2], x[11 - s2], x[7 - s2], x[3 - s2]};
-#pragma unroll
-            for (int q = 0; q < 8; ++q) asm("" : "+v"(v[q]));
-            const float send = half ? (godd ? v[5] : v[4]) : (godd ? v[3] : v[2]);
-            const float recv = __shfl_xor(send, 32);
-            b11[s2] = half ? recv : (godd ? v[1] : v[0]);
-            a22[s2] = half ? (godd ? v[7] : v[6]) : recv;
-        }
-        f32x4 X = zero4();
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) X = __builtin_amdgcn_mfma_f32_16x16x4f32(a21[s2], b11[s2], X, 0, 0, 0);
-        f32x4 Y = zero4();
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a22[s2], X[s2], Y, 0, 0, 0);
-        // Stores into the T buffer: rows [t][hi tpos(s) | lo tpos(s)] (fp32: [t][tpos(s)]).
+        // Diagonal blocks into the T buffer: rows [t][hi tpos(s) | lo tpos(s)]
+        // (fp32: [t][tpos(s)]).
+        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c % Cf::NTBUF) * Cf::SZ_TP);
         if constexpr (SP) {
             if (half == 0) {
                 // column n of T11: lane group 0 writes the hi parts, group 1 the lo parts
@@ -454,18 +428,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                     *(u32x2*)(p + 8 * a4) = godd ? u32x2{l0, l1} : u32x2{h0, h1};
                 }
             }
-            // T21 rows 16 + 4g + e, column n
-            uint32_t th[2], tl[2];
-            split2(-Y[0], -Y[1], th[0], tl[0]);
-            split2(-Y[2], -Y[3], th[1], tl[1]);
-            uint16_t* q = (uint16_t*)(Tp + (16 + 4 * g) * LDP + tpos(n));
-#pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2) {
-                q[(2 * i2) * LDP] = (uint16_t)th[i2];
-                q[(2 * i2 + 1) * LDP] = (uint16_t)(th[i2] >> 16);
-                q[(2 * i2) * LDP + C] = (uint16_t)tl[i2];
-                q[(2 * i2 + 1) * LDP + C] = (uint16_t)(tl[i2] >> 16);
-            }
         } else {
             if (half == 0) {
                 if (!godd) {
@@ -481,6 +443,51 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                     *(f32x4*)(Tp + (16 + n) * LDP + 8 * a4 + 4) = f32x4{x[o], x[o - 1], x[o - 2], x[o - 3]};
                 }
             }
+        }
+    };
+
+    auto t_merge = [&](int c, const float (&x)[16]) __attribute__((always_inline)) {
+        const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
+        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c % Cf::NTBUF) * Cf::SZ_TP);
+        const f32x4 a21 = *(const f32x4*)(sA + Cf::AB_21 + n * ALD + 4 * g);   // A21[n][4g..4g+3]
+        // Merge operands: half 0 sends T11[8+4g+s][n] (for lane group g+2),
+        // half 1 sends T22[n][4(g-2)+s] (for lane group g-2).
+        float b11[4], a22[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            // The candidates are pinned to registers first: a lane-dependent
+            // choice between array elements would otherwise become a choice
+            // of address and push x out to scratch memory.
+            float v[8] = {x[s2], x[4 + s2], x[8 + s2], x[12 + s2],
+                          x[15 - s2], x[11 - s2], x[7 - s2], x[3 - s2]};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) asm("" : "+v"(v[q]));
+            const float send = half ? (godd ? v[5] : v[4]) : (godd ? v[3] : v[2]);
+            const float recv = __shfl_xor(send, 32);
+            b11[s2] = half ? recv : (godd ? v[1] : v[0]);
+            a22[s2] = half ? (godd ? v[7] : v[6]) : recv;
+        }
+        f32x4 X = zero4();
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) X = __builtin_amdgcn_mfma_f32_16x16x4f32(a21[s2], b11[s2], X, 0, 0, 0);
+        f32x4 Y = zero4();
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a22[s2], X[s2], Y, 0, 0, 0);
+        // T21 into the T buffer
+        if constexpr (SP) {
+            // T21 rows 16 + 4g + e, column n
+            uint32_t th[2], tl[2];
+            split2(-Y[0], -Y[1], th[0], tl[0]);
+            split2(-Y[2], -Y[3], th[1], tl[1]);
+            uint16_t* q = (uint16_t*)(Tp + (16 + 4 * g) * LDP + tpos(n));
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+                q[(2 * i2) * LDP] = (uint16_t)th[i2];
+                q[(2 * i2 + 1) * LDP] = (uint16_t)(th[i2] >> 16);
+                q[(2 * i2) * LDP + C] = (uint16_t)tl[i2];
+                q[(2 * i2 + 1) * LDP + C] = (uint16_t)(tl[i2] >> 16);
+            }
+        } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) Tp[(16 + 4 * g + e) * LDP + tpos(n)] = -Y[e];
         }
@@ -528,7 +535,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
         const E* __restrict__ sV = (const E*)(slot + Cf::OFF_SV);
         const float* __restrict__ sc = (const float*)(slot + Cf::OFF_SSC);
-        const E* __restrict__ Tp = (const E*)(smem + Cf::OFF_T + (i & 1) * Cf::SZ_TP);
+        const E* __restrict__ Tp = (const E*)(smem + Cf::OFF_T + (i % Cf::NTBUF) * Cf::SZ_TP);
         const E* __restrict__ Pp = (const E*)(smem + Cf::OFF_P + (i & 1) * Cf::SZ_TP);
         const int c0 = i * C;
         // per-row scalars and V values of this lane's rows t = 16 ti + lr + e, read once
@@ -682,10 +689,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     //   inverse wave      A, substitution, merge and T stores for chunk i+1
     // The upper-right 16x16 blocks of T and P are zero for every chunk; they
     // are written once, for both buffers of each; so is the identity table.
-    for (int id = threadIdx.x; id < 4 * 256; id += Cf::THREADS) {
+    for (int id = threadIdx.x; id < (Cf::NTBUF + 2) * 256; id += Cf::THREADS) {
         const int which = id >> 8, r = (id >> 4) & 15, col = tpos(16 + (id & 15));
-        E* base = (E*)(smem + (which < 2 ? Cf::OFF_T + which * Cf::SZ_TP
-                                         : Cf::OFF_P + (which - 2) * Cf::SZ_TP));
+        E* base = (E*)(smem + (which < Cf::NTBUF ? Cf::OFF_T + which * Cf::SZ_TP
+                                                 : Cf::OFF_P + (which - Cf::NTBUF) * Cf::SZ_TP));
         store_pair<SP>(base + r * LDP + col, C, 0.f);
     }
     for (int id = threadIdx.x; id < 256; id += Cf::THREADS)
