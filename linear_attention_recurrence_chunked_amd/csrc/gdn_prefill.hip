@@ -86,11 +86,14 @@ struct PipeCfg {
     // (fp32 path, whose tiles are twice as large) one inverse wave builds A
     // and T of a chunk in one step.
     static constexpr bool SPREAD = SP;
+    // Wave w runs on SIMD w % 4 (waves are placed round-robin): with four
+    // consumers, P and A share SIMDs 0 and 1 with the two stagers, and the
+    // inverse waves (the heaviest helpers) get SIMDs 2 and 3 to themselves.
     static constexpr int NTW = SPREAD ? 2 : 1;     // inverse waves
-    static constexpr int W_T = NCW;                // first inverse wave
-    static constexpr int W_P = W_T + NTW;          // P wave
-    static constexpr int W_A = SPREAD ? W_P + 1 : -1;   // A wave
-    static constexpr int W_S = SPREAD ? W_P + 2 : W_P + 1;   // first of two stager waves
+    static constexpr int W_P = NCW;                // P wave
+    static constexpr int W_A = SPREAD ? NCW + 1 : -1;   // A wave
+    static constexpr int W_T = SPREAD ? NCW + 2 : NCW + 1;   // first inverse wave
+    static constexpr int W_S = W_T + NTW;          // first of two stager waves
     static constexpr int NW = W_S + 2;
     static constexpr int THREADS = 64 * NW;
     static constexpr int NSLOT = SPREAD ? 5 : 3;   // chunks i .. i+NSLOT-1 resident
@@ -223,12 +226,15 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             r[n] = __builtin_bit_cast(VecE, __builtin_amdgcn_raw_buffer_load_b128(
                                                 rs, koff, (c0 + KRI * n) * Dk * Cf::ES, 0));
     };
-    auto store_rows = [&](const VecE (&r)[Cf::NVK], E* dst) __attribute__((always_inline)) {
-        const bool z = !kfull && kd0 >= Dk;
+    auto store_rows = [&](VecE (&r)[Cf::NVK], E* dst) __attribute__((always_inline)) {
+        if (!kfull) {                            // uniform: only with a ragged key dimension
+#pragma unroll
+            for (int n = 0; n < Cf::NVK; ++n) r[n] = kd0 < Dk ? r[n] : VecE{};
+        }
 #pragma unroll
         for (int n = 0; n < Cf::NVK; ++n) {
             const int id = l + 64 * n, t = id / (DK / VE), d0 = (id % (DK / VE)) * VE;
-            *(VecE*)(dst + t * LDK + d0) = z ? VecE{} : r[n];
+            *(VecE*)(dst + t * LDK + d0) = r[n];
         }
     };
     struct KRegs { VecE k[Cf::NVK]; float g, b; };
@@ -240,7 +246,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         R.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_g, goff, c * C * 4, 0));
         R.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_b, goff, c * C * 4, 0));
     };
-    auto stage_k_store = [&](int c, const KRegs& R) __attribute__((always_inline)) {
+    auto stage_k_store = [&](int c, KRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
         store_rows(R.k, (E*)(slot + Cf::OFF_SK));
         // gamma = inclusive cumulative sum of g over the chunk, and the scalars
@@ -278,15 +284,18 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             R.v[n] = __builtin_bit_cast(VecE, __builtin_amdgcn_raw_buffer_load_b128(
                                                   rs_v, voff, (c0 + VRI * n) * Dv * Cf::ES, 0));
     };
-    auto stage_qv_store = [&](int c, const QVRegs& R) __attribute__((always_inline)) {
+    auto stage_qv_store = [&](int c, QVRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
         store_rows(R.q, (E*)(slot + Cf::OFF_SQ));
         E* sV = (E*)(slot + Cf::OFF_SV);
-        const bool z = !vfull && vd0 >= vcols;
+        if (!vfull) {                            // uniform: only with a ragged value slice
+#pragma unroll
+            for (int n = 0; n < Cf::NVV; ++n) R.v[n] = vd0 < vcols ? R.v[n] : VecE{};
+        }
 #pragma unroll
         for (int n = 0; n < Cf::NVV; ++n) {
             const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
-            *(VecE*)(sV + t * LDV + d0) = z ? VecE{} : R.v[n];
+            *(VecE*)(sV + t * LDV + d0) = R.v[n];
         }
     };
 
@@ -724,7 +733,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                     if (dk < Dk) sb[(size_t)dk * Dv + vl] = accS[kt][e];
                 }
         }
-    } else if (wave < Cf::W_T + Cf::NTW) {
+    } else if (wave >= Cf::W_T && wave < Cf::W_T + Cf::NTW) {
         const int pw = wave - Cf::W_T;
         float x[16];
         __syncthreads();
