@@ -25,6 +25,13 @@ Then per call, from ``rng([workload_id, variant, step])``, in this order:
 For bf16 workloads q, k and v are rounded to bf16 (round to nearest even)
 after normalisation; the arrays returned here are float32 holding exactly those
 bf16 values, so the oracle sees precisely what the GPU sees.
+
+With ``raw=True`` the draw also returns the quantities before step 2's
+normalisation and step 4's gate functions, for the entry points that take the
+prologue on the device: ``q_raw``, ``k_raw`` (the N(0, 1) draws of step 2,
+rounded to bf16 for bf16 workloads), ``a``, ``b`` (step 4, float32) and
+``A_log``, ``dt_bias`` (step 1, float32). They come from the same random
+stream, so raw and derived inputs describe the same tokens.
 """
 from dataclasses import dataclass, field
 
@@ -92,18 +99,20 @@ def _head_params(decay, Hv, seed):
 
 
 def draw_prefill(B, Hk, Hv, S, Dk, Dv, dtype="bf16", state="zero", decay="std",
-                 seed=(0, 0, 0)):
+                 seed=(0, 0, 0), raw=False):
     """Draw one prefill batch. Returns a dict of float32 numpy arrays:
     q, k [B,Hk,S,Dk]; v [B,Hv,S,Dv]; g_log, beta [B,Hv,S]; state [B,Hv,Dk,Dv]
-    (zeros for ``state="zero"``, None for ``state="none"``).
+    (zeros for ``state="zero"``, None for ``state="none"``); with ``raw`` also
+    q_raw, k_raw, a, b, A_log, dt_bias (see the module docstring).
     ``seed`` is (workload_id, variant, step); the per-head gate parameters
     come from (workload_id, variant) alone."""
     if dtype not in ("bf16", "f32"):
         raise ValueError("dtype must be 'bf16' or 'f32'")
     A_log, dt_bias = _head_params(decay, Hv, seed[:2])
     rng = np.random.default_rng(list(seed))
-    q = _l2norm(rng.standard_normal((B, Hk, S, Dk), dtype=np.float32))
-    k = _l2norm(rng.standard_normal((B, Hk, S, Dk), dtype=np.float32))
+    q_raw = rng.standard_normal((B, Hk, S, Dk), dtype=np.float32)
+    k_raw = rng.standard_normal((B, Hk, S, Dk), dtype=np.float32)
+    q, k = _l2norm(q_raw), _l2norm(k_raw)
     v = rng.standard_normal((B, Hv, S, Dv), dtype=np.float32)
     a = rng.standard_normal((B, Hv, S))
     b = rng.standard_normal((B, Hv, S))
@@ -121,7 +130,13 @@ def draw_prefill(B, Hk, Hv, S, Dk, Dv, dtype="bf16", state="zero", decay="std",
         raise ValueError("state must be 'zero', 'normal' or 'none'")
     if dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
-    return {"q": q, "k": k, "v": v, "g_log": g_log, "beta": beta, "state": st}
+    d = {"q": q, "k": k, "v": v, "g_log": g_log, "beta": beta, "state": st}
+    if raw:
+        if dtype == "bf16":
+            q_raw, k_raw = bf16_round(q_raw), bf16_round(k_raw)
+        d.update(q_raw=q_raw, k_raw=k_raw, a=a.astype(np.float32), b=b.astype(np.float32),
+                 A_log=A_log.astype(np.float32), dt_bias=dt_bias.astype(np.float32))
+    return d
 
 
 def draw_workload(w, variant="std", step=0, state=None, **overrides):

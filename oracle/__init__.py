@@ -8,6 +8,11 @@ shares no code with it.
   ``gdn_serial.c``), S_t = e^{g_t} S_{t-1} + beta_t k_t (v_t - e^{g_t} S_{t-1}^T k_t)^T,
   o_t = scale S_t^T q_t, with value head h reading key head h // (Hv/Hk)
   (page "GDN CTE Kernel API Reference", Notes).
+* :func:`gdn_serial_gated` -- the same recurrence behind the decode block's
+  prologue: g_log = -exp(A_log[h]) softplus(a + dt_bias[h]), beta = sigmoid(b),
+  q and k L2-normalised with an epsilon (page "GDN Block TKG Kernel API
+  Reference", introduction and Parameters A_log, dt_bias).
+* :func:`gdn_gates`, :func:`l2_normalize` -- those two prologue steps alone.
 * :mod:`oracle.chunked` -- an independent chunk-parallel (WY) derivation in
   numpy fp64, used only as a cross-check of :func:`gdn_serial`.
 """
@@ -18,7 +23,7 @@ import numpy as np
 
 from . import build as _build
 
-__all__ = ["gdn_serial", "default_threads"]
+__all__ = ["gdn_serial", "gdn_serial_gated", "gdn_gates", "l2_normalize", "default_threads"]
 
 _LIB = None
 
@@ -36,6 +41,18 @@ def _lib():
             ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
             ctypes.c_long, ctypes.c_int]
+        lib.oracle_gdn_serial_gated.restype = ctypes.c_int
+        lib.oracle_gdn_serial_gated.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+            ctypes.c_long, ctypes.c_int]
+        lib.oracle_gdn_gates.restype = ctypes.c_int
+        lib.oracle_gdn_gates.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_long] * 3
+        lib.oracle_l2norm.restype = ctypes.c_int
+        lib.oracle_l2norm.argtypes = [ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
+                                      ctypes.c_long, ctypes.c_long]
         _LIB = lib
     return _LIB
 
@@ -50,6 +67,20 @@ def default_threads() -> int:
 
 def _f32(x):
     return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _state_arg(state, shape, inplace):
+    if state is None:
+        return np.zeros(shape, dtype=np.float64)
+    if inplace:
+        if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+                and state.flags.c_contiguous and state.shape == shape):
+            raise ValueError("oracle: inplace needs a C-contiguous float64 state of the right shape")
+        return state
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    if st.shape != shape:
+        raise ValueError("oracle: bad state shape")
+    return st
 
 
 def gdn_serial(q, k, v, g_log, beta, scale, state=None, nthreads=None, inplace=False):
@@ -70,17 +101,7 @@ def gdn_serial(q, k, v, g_log, beta, scale, state=None, nthreads=None, inplace=F
         raise ValueError("oracle: inconsistent shapes")
     if Hv % Hk:
         raise ValueError("oracle: Hv must be a multiple of Hk")
-    if state is None:
-        st = np.zeros((B, Hv, Dk, Dv), dtype=np.float64)
-    elif inplace:
-        st = state
-        if not (isinstance(st, np.ndarray) and st.dtype == np.float64
-                and st.flags.c_contiguous and st.shape == (B, Hv, Dk, Dv)):
-            raise ValueError("oracle: inplace needs a C-contiguous float64 state of the right shape")
-    else:
-        st = np.array(state, dtype=np.float64, order="C", copy=True)
-        if st.shape != (B, Hv, Dk, Dv):
-            raise ValueError("oracle: bad state shape")
+    st = _state_arg(state, (B, Hv, Dk, Dv), inplace)
     out = np.empty((B, Hv, S, Dv), dtype=np.float64)
     n = default_threads() if nthreads is None else int(nthreads)
     rc = _lib().oracle_gdn_serial(
@@ -89,3 +110,61 @@ def gdn_serial(q, k, v, g_log, beta, scale, state=None, nthreads=None, inplace=F
     if rc != 0:
         raise RuntimeError("oracle_gdn_serial failed with code %d" % rc)
     return out, st
+
+
+def gdn_serial_gated(q, k, v, a, b, A_log, dt_bias, scale, eps, state=None, nthreads=None,
+                     inplace=False):
+    """Token-serial fp64 gated delta rule from the raw prologue inputs.
+
+    Shapes: q, k [B,Hk,S,Dk] (not normalised); v [B,Hv,S,Dv]; a, b [B,Hv,S];
+    A_log, dt_bias [Hv]; state [B,Hv,Dk,Dv] or None. Per token
+    g_log = -exp(A_log[h]) softplus(a + dt_bias[h]), beta = sigmoid(b),
+    q and k divided by sqrt(sum of squares + eps), all in fp64; then the
+    recurrence of :func:`gdn_serial`. Returns (out, final state), float64.
+    """
+    q, k, v, a, b, A_log, dt_bias = (_f32(x) for x in (q, k, v, a, b, A_log, dt_bias))
+    B, Hk, S, Dk = q.shape
+    Bv, Hv, Sv, Dv = v.shape
+    if k.shape != q.shape or (Bv, Sv) != (B, S) or a.shape != (B, Hv, S) \
+            or b.shape != (B, Hv, S) or A_log.shape != (Hv,) or dt_bias.shape != (Hv,):
+        raise ValueError("oracle: inconsistent shapes")
+    if Hv % Hk:
+        raise ValueError("oracle: Hv must be a multiple of Hk")
+    st = _state_arg(state, (B, Hv, Dk, Dv), inplace)
+    out = np.empty((B, Hv, S, Dv), dtype=np.float64)
+    n = default_threads() if nthreads is None else int(nthreads)
+    rc = _lib().oracle_gdn_serial_gated(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, a.ctypes.data, b.ctypes.data,
+        A_log.ctypes.data, dt_bias.ctypes.data, float(eps), float(scale),
+        st.ctypes.data, out.ctypes.data, B, Hk, Hv, S, Dk, Dv, n)
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_serial_gated failed with code %d" % rc)
+    return out, st
+
+
+def gdn_gates(a, b, A_log, dt_bias):
+    """g_log = -exp(A_log[h]) softplus(a + dt_bias[h]) and beta = sigmoid(b),
+    fp64, for a, b [B,Hv,S] and A_log, dt_bias [Hv]."""
+    a, b, A_log, dt_bias = (_f32(x) for x in (a, b, A_log, dt_bias))
+    if a.ndim != 3 or b.shape != a.shape or A_log.shape != (a.shape[1],) \
+            or dt_bias.shape != A_log.shape:
+        raise ValueError("oracle: inconsistent gate shapes")
+    B, Hv, S = a.shape
+    g = np.empty(a.shape, np.float64)
+    be = np.empty(a.shape, np.float64)
+    rc = _lib().oracle_gdn_gates(a.ctypes.data, b.ctypes.data, A_log.ctypes.data,
+                                 dt_bias.ctypes.data, g.ctypes.data, be.ctypes.data, B, Hv, S)
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_gates failed with code %d" % rc)
+    return g, be
+
+
+def l2_normalize(x, eps):
+    """x / sqrt(sum over the last axis of x^2 + eps), fp64."""
+    x = _f32(x)
+    D = x.shape[-1]
+    y = np.empty(x.shape, np.float64)
+    rc = _lib().oracle_l2norm(x.ctypes.data, float(eps), y.ctypes.data, x.size // D if D else 0, D)
+    if rc != 0:
+        raise RuntimeError("oracle_l2norm failed with code %d" % rc)
+    return y

@@ -24,13 +24,30 @@
  *   which is S_t = e^{g_t} S_{t-1} + beta_t k_t (v_t - e^{g_t} S_{t-1}^T k_t)^T,
  *   o_t = scale S_t^T q_t.
  *
+ * The gated entry (oracle_gdn_serial_gated) first derives the recurrence's
+ * inputs from the decode block's raw quantities ("GDN Block TKG Kernel API
+ * Reference": introduction, "l2norm/beta/g" ahead of the recurrence;
+ * Parameters A_log, a per-value-head log decay, and dt_bias, a per-value-head
+ * bias inside a softplus), per token:
+ *
+ *     g_log = -exp(A_log[h]) * softplus(a[b,h,t] + dt_bias[h]),
+ *             softplus(x) = ln(1 + e^x)
+ *     beta  = sigmoid(b[b,h,t]) = 1 / (1 + e^{-b})
+ *     k     = k_raw / sqrt(sum_i k_raw[i]^2 + eps), q likewise
+ *             (q and k must be L2-normalised: "GDN CTE Kernel API
+ *             Reference", Parameters query/key and Notes; the pages give no
+ *             epsilon, so it is an argument)
+ *
+ * and then runs the same token step.
+ *
  * Precision: inputs arrive as float (bf16 operands are widened exactly by the
  * caller); every product and sum is in double. The state is double in and out
  * so that chained calls (iterated decode) keep full precision.
  *
  * Layouts (row-major, contiguous):
  *   q, k  [B][Hk][S][Dk]     v, out [B][Hv][S][Dv]
- *   g_log, beta [B][Hv][S]   state  [B][Hv][Dk][Dv]  (in/out)
+ *   g_log, beta, a, b [B][Hv][S]   A_log, dt_bias [Hv]
+ *   state [B][Hv][Dk][Dv]  (in/out)
  *
  * Parallelism: the (b, h) pairs are independent; they are spread over
  * nthreads OpenMP threads. Each pair runs the loop above exactly as written,
@@ -44,11 +61,76 @@
 #include <omp.h>
 #endif
 
-int oracle_gdn_serial(const float* q, const float* k, const float* v,
-                      const float* g_log, const float* beta, double scale,
-                      double* state, double* out,
-                      long B, long Hk, long Hv, long S, long Dk, long Dv,
-                      int nthreads)
+/* ln(1 + e^x), evaluated without overflow for large x */
+static double softplus(double x)
+{
+    return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+}
+
+static double sigmoid(double x)
+{
+    return 1.0 / (1.0 + exp(-x));
+}
+
+/* y = x / sqrt(sum x^2 + eps) over one vector of length D */
+static void l2norm_row(const float* x, double eps, double* y, long D)
+{
+    double ss = 0.0;
+    for (long i = 0; i < D; ++i) ss += (double)x[i] * (double)x[i];
+    const double r = 1.0 / sqrt(ss + eps);
+    for (long i = 0; i < D; ++i) y[i] = (double)x[i] * r;
+}
+
+/* g_log and beta of token t of value head h */
+static void gates(double a, double b, double A_log_h, double dt_bias_h, double* g, double* be)
+{
+    *g = -exp(A_log_h) * softplus(a + dt_bias_h);
+    *be = sigmoid(b);
+}
+
+/*
+ * One token of the recurrence on the [Dk][Dv] state St, with decay factor
+ * a = e^{g}, write strength be, key kt, query qt (length Dk), value vt
+ * (length Dv); u is scratch of length Dv, ot receives the output row.
+ */
+static void gdn_token(double* St, const double* kt, const double* qt, const double* vt,
+                      double a, double be, double scale, double* u, double* ot,
+                      long Dk, long Dv)
+{
+    /* S = a * S */
+    for (long i = 0; i < Dk; ++i)
+        for (long c = 0; c < Dv; ++c)
+            St[i * Dv + c] *= a;
+
+    /* u = beta * (v - S^T k) */
+    for (long c = 0; c < Dv; ++c) {
+        double x = 0.0;
+        for (long i = 0; i < Dk; ++i) x += St[i * Dv + c] * kt[i];
+        u[c] = be * (vt[c] - x);
+    }
+
+    /* S = S + k u^T */
+    for (long i = 0; i < Dk; ++i)
+        for (long c = 0; c < Dv; ++c)
+            St[i * Dv + c] += kt[i] * u[c];
+
+    /* o = scale * S^T q */
+    for (long c = 0; c < Dv; ++c) {
+        double y = 0.0;
+        for (long i = 0; i < Dk; ++i) y += St[i * Dv + c] * qt[i];
+        ot[c] = scale * y;
+    }
+}
+
+/*
+ * Both entries share this driver. Without gates (A_log == NULL) g_log and
+ * beta are the per-token decay and write strength and q, k are used as given;
+ * with gates, gl/bt hold the raw a and b and q, k are normalised with eps.
+ */
+static int serial(const float* q, const float* k, const float* v,
+                  const float* gl, const float* bt, const float* A_log, const float* dt_bias,
+                  double eps, double scale, double* state, double* out,
+                  long B, long Hk, long Hv, long S, long Dk, long Dv, int nthreads)
 {
     if (B < 0 || Hk <= 0 || Hv <= 0 || S < 0 || Dk <= 0 || Dv <= 0) return 1;
     if (Hv % Hk != 0) return 1;
@@ -62,45 +144,82 @@ int oracle_gdn_serial(const float* q, const float* k, const float* v,
         const long h = bh % Hv;
         const long j = h / G;                      /* GQA: contiguous groups */
         double* St = state + bh * Dk * Dv;         /* S[i][c] = St[i*Dv + c] */
-        double* u = (double*)malloc((size_t)Dv * sizeof(double));
-        if (!u) {
+        double* buf = (double*)malloc((size_t)(3 * Dk + 2 * Dv) * sizeof(double));
+        if (!buf) {
 #pragma omp atomic write
             failed = 1;
             continue;
         }
+        double* kd = buf;
+        double* qd = buf + Dk;
+        double* vd = buf + 2 * Dk;
+        double* u = buf + 2 * Dk + Dv;
         for (long t = 0; t < S; ++t) {
             const float* kt = k + ((b * Hk + j) * S + t) * Dk;
             const float* qt = q + ((b * Hk + j) * S + t) * Dk;
             const float* vt = v + ((b * Hv + h) * S + t) * Dv;
-            const double a = exp((double)g_log[bh * S + t]);
-            const double be = (double)beta[bh * S + t];
-            double* ot = out + (bh * S + t) * Dv;
-
-            /* S = a * S */
-            for (long i = 0; i < Dk; ++i)
-                for (long c = 0; c < Dv; ++c)
-                    St[i * Dv + c] *= a;
-
-            /* u = beta * (v - S^T k) */
-            for (long c = 0; c < Dv; ++c) {
-                double x = 0.0;
-                for (long i = 0; i < Dk; ++i) x += St[i * Dv + c] * (double)kt[i];
-                u[c] = be * ((double)vt[c] - x);
+            double g, be;
+            if (A_log) {
+                gates((double)gl[bh * S + t], (double)bt[bh * S + t], (double)A_log[h],
+                      (double)dt_bias[h], &g, &be);
+                l2norm_row(kt, eps, kd, Dk);
+                l2norm_row(qt, eps, qd, Dk);
+            } else {
+                g = (double)gl[bh * S + t];
+                be = (double)bt[bh * S + t];
+                for (long i = 0; i < Dk; ++i) {
+                    kd[i] = (double)kt[i];
+                    qd[i] = (double)qt[i];
+                }
             }
-
-            /* S = S + k u^T */
-            for (long i = 0; i < Dk; ++i)
-                for (long c = 0; c < Dv; ++c)
-                    St[i * Dv + c] += (double)kt[i] * u[c];
-
-            /* o = scale * S^T q */
-            for (long c = 0; c < Dv; ++c) {
-                double y = 0.0;
-                for (long i = 0; i < Dk; ++i) y += St[i * Dv + c] * (double)qt[i];
-                ot[c] = scale * y;
-            }
+            for (long c = 0; c < Dv; ++c) vd[c] = (double)vt[c];
+            gdn_token(St, kd, qd, vd, exp(g), be, scale, u, out + (bh * S + t) * Dv, Dk, Dv);
         }
-        free(u);
+        free(buf);
     }
     return failed ? 2 : 0;
+}
+
+int oracle_gdn_serial(const float* q, const float* k, const float* v,
+                      const float* g_log, const float* beta, double scale,
+                      double* state, double* out,
+                      long B, long Hk, long Hv, long S, long Dk, long Dv,
+                      int nthreads)
+{
+    return serial(q, k, v, g_log, beta, NULL, NULL, 0.0, scale, state, out,
+                  B, Hk, Hv, S, Dk, Dv, nthreads);
+}
+
+int oracle_gdn_serial_gated(const float* q, const float* k, const float* v,
+                            const float* a, const float* b,
+                            const float* A_log, const float* dt_bias,
+                            double eps, double scale, double* state, double* out,
+                            long B, long Hk, long Hv, long S, long Dk, long Dv,
+                            int nthreads)
+{
+    if (!A_log || !dt_bias) return 1;
+    return serial(q, k, v, a, b, A_log, dt_bias, eps, scale, state, out,
+                  B, Hk, Hv, S, Dk, Dv, nthreads);
+}
+
+/* The gates alone: g_log, beta [B][Hv][S] (double) from a, b [B][Hv][S] and
+ * A_log, dt_bias [Hv]. */
+int oracle_gdn_gates(const float* a, const float* b, const float* A_log, const float* dt_bias,
+                     double* g_log, double* beta, long B, long Hv, long S)
+{
+    if (B < 0 || Hv <= 0 || S < 0) return 1;
+    for (long bh = 0; bh < B * Hv; ++bh)
+        for (long t = 0; t < S; ++t)
+            gates((double)a[bh * S + t], (double)b[bh * S + t], (double)A_log[bh % Hv],
+                  (double)dt_bias[bh % Hv], &g_log[bh * S + t], &beta[bh * S + t]);
+    return 0;
+}
+
+/* The normalisation alone: y = x / sqrt(sum x^2 + eps) for each of `rows`
+ * vectors of length D. */
+int oracle_l2norm(const float* x, double eps, double* y, long rows, long D)
+{
+    if (rows < 0 || D <= 0) return 1;
+    for (long r = 0; r < rows; ++r) l2norm_row(x + r * D, eps, y + r * D, D);
+    return 0;
 }

@@ -273,3 +273,163 @@ ALL_PINS = [
     pin_gqa_equals_repeat, pin_columns_independent, pin_linear_in_values_and_state,
     pin_scale, pin_split_carry, pin_permutation,
 ]
+
+
+# ------------------------------------------------- gate + normalisation prologue
+#
+# The decode block computes the recurrence's inputs from raw quantities
+# ("GDN Block TKG Kernel API Reference": introduction, "l2norm/beta/g";
+# Parameters A_log, a per-value-head log decay, and dt_bias, a per-value-head
+# softplus bias); q and k must reach the recurrence L2-normalised ("GDN CTE
+# Kernel API Reference", Notes). Read here as, per token,
+#     g_log = -exp(A_log[h]) softplus(a + dt_bias[h]),  beta = sigmoid(b),
+#     k = k_raw / sqrt(|k_raw|^2 + eps), q likewise.
+# Every ``gpin_*`` takes a namespace ``o`` with
+#     o.gated(q, k, v, a, b, A_log, dt_bias, scale, eps, state) -> (out, state)
+#     o.gates(a, b, A_log, dt_bias) -> (g_log, beta)
+#     o.l2norm(x, eps) -> x normalised over its last axis
+# and checks them against library routines (scipy's logistic function),
+# closed forms and a hand-worked example.
+
+def _expit(x):
+    from scipy.special import expit
+    return expit(np.asarray(x, np.float64))
+
+
+def raw_case(seed, B=1, Hk=1, Hv=1, S=8, Dk=4, Dv=3, state=True):
+    """Small random raw prologue inputs: un-normalised q, k (norms spread over
+    [0.2, 5]), v, gate pre-activations a, b and per-head A_log, dt_bias."""
+    r = _rng(seed)
+    q = (r.standard_normal((B, Hk, S, Dk)) * r.uniform(0.2, 5.0, (B, Hk, S, 1))).astype(np.float32)
+    k = (r.standard_normal((B, Hk, S, Dk)) * r.uniform(0.2, 5.0, (B, Hk, S, 1))).astype(np.float32)
+    v = r.standard_normal((B, Hv, S, Dv)).astype(np.float32)
+    a = r.standard_normal((B, Hv, S)).astype(np.float32)
+    b = r.standard_normal((B, Hv, S)).astype(np.float32)
+    A_log = r.uniform(np.log(1.0), np.log(16.0), Hv).astype(np.float32)
+    dt_bias = r.uniform(-1.0, 1.0, Hv).astype(np.float32)
+    s0 = (0.5 * r.standard_normal((B, Hv, Dk, Dv))).astype(np.float32) if state else None
+    return q, k, v, a, b, A_log, dt_bias, s0
+
+
+def _decay_by_library(a, A_log, dt_bias):
+    """e^{g} = exp(-e^{A} softplus(x)) = (1 / (1 + e^{x}))^{e^{A}} = expit(-x)^{e^{A}}."""
+    x = a.astype(np.float64) + dt_bias.astype(np.float64)[None, :, None]
+    return _expit(-x) ** np.exp(A_log.astype(np.float64))[None, :, None]
+
+
+def gpin_gates_match_library(o):
+    """e^{g} equals expit(-(a + dt_bias))^{exp(A_log)} and beta equals expit(b),
+    with A_log and dt_bias varying per value head; extreme pre-activations stay
+    finite and follow the asymptotes of softplus."""
+    _, _, _, a, b, A_log, dt_bias, _ = raw_case(30, B=2, Hv=3, S=7)
+    g, beta = o.gates(a, b, A_log, dt_bias)
+    _close(np.exp(g), _decay_by_library(a, A_log, dt_bias), 1e-12, "gates: decay")
+    _close(beta, _expit(b), 1e-14, "gates: beta")
+    assert np.all(g < 0), "gates: g_log must be negative"
+    # asymptotes: softplus(x) -> x for large x, -> e^x for very negative x
+    a2 = np.array([[[60.0, -60.0, 0.0]]], np.float32)
+    b2 = np.array([[[60.0, -60.0, 0.0]]], np.float32)
+    g2, be2 = o.gates(a2, b2, np.array([np.log(2.0)], np.float32), np.zeros(1, np.float32))
+    e2 = np.exp(float(np.float32(np.log(2.0))))
+    assert np.all(np.isfinite(g2)) and np.all(np.isfinite(be2)), "gates: not finite"
+    _close(g2[0, 0, 0] / (-e2 * 60.0), 1.0, 1e-14, "gates: large x")
+    _close(g2[0, 0, 1] / (-e2 * np.exp(-60.0)), 1.0, 1e-12, "gates: small x")
+    _close(g2[0, 0, 2], -e2 * np.log(2.0), 1e-15, "gates: x = 0")
+    _close(be2[0, 0], [1.0, np.exp(-60.0), 0.5], 1e-15, "gates: beta limits")
+
+
+def gpin_l2norm_closed_forms(o):
+    """(3, 4) -> (0.6, 0.8); with eps = 11 the divisor is sqrt(25 + 11) = 6;
+    a zero vector stays zero; random rows get unit norm and keep direction."""
+    _close(o.l2norm(np.array([[3.0, 4.0]], np.float32), 0.0), [[0.6, 0.8]], 1e-15, "l2 (3,4)")
+    _close(o.l2norm(np.array([[3.0, 4.0]], np.float32), 11.0), [[0.5, 4.0 / 6.0]], 1e-15,
+           "l2 eps")
+    z = o.l2norm(np.zeros((2, 5), np.float32), 1e-6)
+    assert np.all(z == 0.0), "l2: zero vector"
+    x = _rng(31).standard_normal((3, 4, 7)).astype(np.float32) * 3.0
+    y = o.l2norm(x, 0.0)
+    _close(np.linalg.norm(y, axis=-1), np.ones((3, 4)), 1e-14, "l2: unit norm")
+    _close(y * np.linalg.norm(x.astype(np.float64), axis=-1, keepdims=True),
+           x.astype(np.float64), 1e-13, "l2: direction")
+
+
+def gpin_gated_golden(o):
+    """Hand-worked Dk = 2 example (tests/golden/gated_gdn.json)."""
+    d = _golden("gated_gdn.json")
+    n = len(d["v"])
+    f = lambda x, *s: np.asarray(x, np.float32).reshape(*s)
+    out, st = o.gated(f(d["q"], 1, 1, n, 2), f(d["k"], 1, 1, n, 2), f(d["v"], 1, 1, n, 1),
+                      f(d["a"], 1, 1, n), f(d["b"], 1, 1, n), f([d["A_log"]], 1),
+                      f([d["dt_bias"]], 1), d["scale"], d["eps"], f(d["state0"], 1, 1, 2, 1))
+    # the logarithms are stored as float32: e^{g} is exact to ~1e-7 relative
+    _close(out.reshape(n), d["out"], 1e-6, "gated golden out")
+    _close(st.reshape(2), d["state"], 1e-6, "gated golden state")
+
+
+def gpin_gated_pure_decay(o):
+    """b = -60 makes beta ~ 1e-26: no write, S_T = prod e^{g_t} S_0 and
+    o_t = scale (prod_{tau<=t} e^{g_tau}) S_0^T q_t / |q_t|, with e^{g} from the
+    logistic function (library)."""
+    q, k, v, a, b, A_log, dt_bias, s0 = raw_case(32, B=1, Hk=1, Hv=2, S=6, Dk=4, Dv=3)
+    b[:] = -60.0
+    out, st = o.gated(q, k, v, a, b, A_log, dt_bias, 0.8, 0.0, s0)
+    dec = np.cumprod(_decay_by_library(a, A_log, dt_bias), axis=-1)
+    qn = q.astype(np.float64) / np.linalg.norm(q.astype(np.float64), axis=-1, keepdims=True)
+    for h in range(2):
+        S0 = s0[0, h].astype(np.float64)
+        for t in range(6):
+            _close(out[0, h, t], 0.8 * dec[0, h, t] * (S0.T @ qn[0, 0, t]), 1e-12, "decay out")
+        _close(st[0, h], dec[0, h, -1] * S0, 1e-12, "decay state")
+
+
+def gpin_gated_equals_normalised_serial(o):
+    """The prologue followed by the recurrence equals the (separately pinned)
+    serial recurrence fed with q, k normalised by numpy and g_log, beta from
+    the logistic function, with GQA (Hk = 2, Hv = 4) and per-head parameters."""
+    import oracle
+    q, k, v, a, b, A_log, dt_bias, s0 = raw_case(33, B=2, Hk=2, Hv=4, S=9, Dk=5, Dv=3)
+    eps = 1e-3
+    out, st = o.gated(q, k, v, a, b, A_log, dt_bias, 0.6, eps, s0)
+    nq = lambda x: x.astype(np.float64) / np.sqrt(
+        np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True) + eps)
+    g = np.log(_decay_by_library(a, A_log, dt_bias))
+    ref_o, ref_s = oracle.gdn_serial(nq(q), nq(k), v, g, _expit(b), 0.6, s0)
+    # the serial oracle takes float32 inputs: agreement to float32 rounding
+    _close(out, ref_o, 2e-6, "gated vs serial out")
+    _close(st, ref_s, 2e-6, "gated vs serial state")
+
+
+def gpin_gated_norm_invariance(o):
+    """With eps = 0 the result does not depend on the length of each q_t and
+    k_t: rescaling every token's q and k by its own positive factor changes
+    nothing."""
+    q, k, v, a, b, A_log, dt_bias, s0 = raw_case(34, B=1, Hk=1, Hv=2, S=10, Dk=6, Dv=4)
+    o1, s1 = o.gated(q, k, v, a, b, A_log, dt_bias, 1.1, 0.0, s0)
+    r = _rng(35)
+    # powers of two keep the rescaled float32 inputs exact
+    fq = (2.0 ** r.integers(-4, 5, (1, 1, 10, 1))).astype(np.float32)
+    fk = (2.0 ** r.integers(-4, 5, (1, 1, 10, 1))).astype(np.float32)
+    o2, s2 = o.gated(q * fq, k * fk, v, a, b, A_log, dt_bias, 1.1, 0.0, s0)
+    _close(o2, o1, 1e-13, "norm invariance out")
+    _close(s2, s1, 1e-13, "norm invariance state")
+
+
+def gpin_gated_heads_independent(o):
+    """Each value head uses its own A_log[h], dt_bias[h]: a GQA call equals
+    one single-head call per value head (with that head's key head)."""
+    q, k, v, a, b, A_log, dt_bias, s0 = raw_case(36, B=1, Hk=2, Hv=4, S=7, Dk=4, Dv=3)
+    out, st = o.gated(q, k, v, a, b, A_log, dt_bias, 0.9, 1e-6, s0)
+    for h in range(4):
+        j = h // 2
+        sl = slice(h, h + 1)
+        oh, sh = o.gated(q[:, j:j + 1], k[:, j:j + 1], v[:, sl], a[:, sl], b[:, sl],
+                         A_log[sl], dt_bias[sl], 0.9, 1e-6, s0[:, sl])
+        _close(out[:, sl], oh, 1e-14, "heads out")
+        _close(st[:, sl], sh, 1e-14, "heads state")
+
+
+GATED_PINS = [
+    gpin_gates_match_library, gpin_l2norm_closed_forms, gpin_gated_golden,
+    gpin_gated_pure_decay, gpin_gated_equals_normalised_serial, gpin_gated_norm_invariance,
+    gpin_gated_heads_independent,
+]

@@ -66,3 +66,10 @@ def test_workload_inputs_are_seeded_and_normalised():
     x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 1.00390625], np.float32)
     r = inputs.bf16_round(x)
     assert list(r) == [1.0, 1.0 + 4 * 2.0 ** -8, -2.5, 1.0]
+
+
+@pytest.mark.parametrize("pin", P.GATED_PINS, ids=lambda f: f.__name__)
+def test_gated_pin(pin):
+    from types import SimpleNamespace
+    pin(SimpleNamespace(gated=oracle.gdn_serial_gated, gates=oracle.gdn_gates,
+                        l2norm=oracle.l2_normalize))

@@ -6,6 +6,7 @@ import ctypes
 import os
 import subprocess
 import tempfile
+from types import SimpleNamespace
 
 import numpy as np
 import pytest
@@ -18,16 +19,31 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn_serial.c")
 MUTANTS = {
     "no_decay": ("St[i * Dv + c] *= a;", "St[i * Dv + c] *= 1.0;"),
     "decay_twice": ("St[i * Dv + c] *= a;", "St[i * Dv + c] *= a * a;"),
-    "delta_sign": ("u[c] = be * ((double)vt[c] - x);", "u[c] = be * ((double)vt[c] + x);"),
-    "no_beta": ("u[c] = be * ((double)vt[c] - x);", "u[c] = ((double)vt[c] - x);"),
-    "no_delta": ("u[c] = be * ((double)vt[c] - x);", "u[c] = be * (double)vt[c];"),
+    "delta_sign": ("u[c] = be * (vt[c] - x);", "u[c] = be * (vt[c] + x);"),
+    "no_beta": ("u[c] = be * (vt[c] - x);", "u[c] = (vt[c] - x);"),
+    "no_delta": ("u[c] = be * (vt[c] - x);", "u[c] = be * vt[c];"),
     "gqa_modulo": ("const long j = h / G;", "const long j = h % Hk;"),
-    "transposed_read": ("x += St[i * Dv + c] * (double)kt[i];",
-                        "x += St[(c % Dk) * Dv + (i % Dv)] * (double)kt[i];"),
-    "out_reads_k": ("y += St[i * Dv + c] * (double)qt[i];", "y += St[i * Dv + c] * (double)kt[i];"),
+    "transposed_read": ("x += St[i * Dv + c] * kt[i];",
+                        "x += St[(c % Dk) * Dv + (i % Dv)] * kt[i];"),
+    "out_reads_k": ("y += St[i * Dv + c] * qt[i];", "y += St[i * Dv + c] * kt[i];"),
     "no_scale": ("ot[c] = scale * y;", "ot[c] = y;"),
-    "write_with_q": ("St[i * Dv + c] += (double)kt[i] * u[c];",
-                     "St[i * Dv + c] += (double)qt[i] * u[c];"),
+    "write_with_q": ("St[i * Dv + c] += kt[i] * u[c];", "St[i * Dv + c] += qt[i] * u[c];"),
+    # the gate and normalisation prologue
+    "softplus_sign": (": log1p(exp(x));", ": log1p(exp(-x));"),
+    "softplus_no_shift": ("x + log1p(exp(-x))", "log1p(exp(-x))"),
+    "gate_no_dt_bias": ("softplus(a + dt_bias_h)", "softplus(a)"),
+    "gate_no_exp": ("*g = -exp(A_log_h) *", "*g = -A_log_h *"),
+    "gate_sign": ("*g = -exp(A_log_h) *", "*g = exp(A_log_h) *"),
+    "sigmoid_sign": ("1.0 / (1.0 + exp(-x));", "1.0 / (1.0 + exp(x));"),
+    "norm_no_sqrt": ("1.0 / sqrt(ss + eps);", "1.0 / (ss + eps);"),
+    "norm_eps_outside": ("1.0 / sqrt(ss + eps);", "1.0 / (sqrt(ss) + eps);"),
+    "q_not_normalised": ("l2norm_row(qt, eps, qd, Dk);",
+                         "for (long i = 0; i < Dk; ++i) qd[i] = (double)qt[i];"),
+    "k_not_normalised": ("l2norm_row(kt, eps, kd, Dk);",
+                         "for (long i = 0; i < Dk; ++i) kd[i] = (double)kt[i];"),
+    "gate_key_head": ("(double)A_log[h],", "(double)A_log[j],"),
+    "gates_swapped": ("gates((double)gl[bh * S + t], (double)bt[bh * S + t],",
+                      "gates((double)bt[bh * S + t], (double)gl[bh * S + t],"),
 }
 
 
@@ -45,34 +61,71 @@ def _build_mutant(name, tmpdir):
 
 
 def _wrap(libpath):
+    """The mutant's three entries, marshalled like the real oracle's."""
     lib = ctypes.CDLL(libpath)
-    f = lib.oracle_gdn_serial
-    f.restype = ctypes.c_int
-    f.argtypes = oracle._lib().oracle_gdn_serial.argtypes
+    real = oracle._lib()
+    for name in ("oracle_gdn_serial", "oracle_gdn_serial_gated", "oracle_gdn_gates",
+                 "oracle_l2norm"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = getattr(real, name).argtypes
+    f32 = lambda *xs: [np.ascontiguousarray(np.asarray(x, np.float32)) for x in xs]
+
+    def state_of(state, B, Hv, Dk, Dv):
+        return (np.zeros((B, Hv, Dk, Dv)) if state is None
+                else np.array(state, dtype=np.float64, order="C", copy=True))
 
     def fn(q, k, v, g, beta, scale, state=None):
-        q, k, v, g, beta = (np.ascontiguousarray(np.asarray(a, np.float32))
-                            for a in (q, k, v, g, beta))
+        q, k, v, g, beta = f32(q, k, v, g, beta)
         B, Hk, S, Dk = q.shape
         Hv, Dv = v.shape[1], v.shape[3]
-        st = (np.zeros((B, Hv, Dk, Dv)) if state is None
-              else np.array(state, dtype=np.float64, order="C", copy=True))
+        st = state_of(state, B, Hv, Dk, Dv)
         out = np.empty((B, Hv, S, Dv))
-        rc = f(q.ctypes.data, k.ctypes.data, v.ctypes.data, g.ctypes.data, beta.ctypes.data,
-               float(scale), st.ctypes.data, out.ctypes.data, B, Hk, Hv, S, Dk, Dv, 1)
+        rc = lib.oracle_gdn_serial(q.ctypes.data, k.ctypes.data, v.ctypes.data, g.ctypes.data,
+                                   beta.ctypes.data, float(scale), st.ctypes.data,
+                                   out.ctypes.data, B, Hk, Hv, S, Dk, Dv, 1)
         assert rc == 0
         return out, st
-    return fn
+
+    def gated(q, k, v, a, b, A_log, dt_bias, scale, eps, state=None):
+        q, k, v, a, b, A_log, dt_bias = f32(q, k, v, a, b, A_log, dt_bias)
+        B, Hk, S, Dk = q.shape
+        Hv, Dv = v.shape[1], v.shape[3]
+        st = state_of(state, B, Hv, Dk, Dv)
+        out = np.empty((B, Hv, S, Dv))
+        rc = lib.oracle_gdn_serial_gated(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, a.ctypes.data, b.ctypes.data,
+            A_log.ctypes.data, dt_bias.ctypes.data, float(eps), float(scale), st.ctypes.data,
+            out.ctypes.data, B, Hk, Hv, S, Dk, Dv, 1)
+        assert rc == 0
+        return out, st
+
+    def gates(a, b, A_log, dt_bias):
+        a, b, A_log, dt_bias = f32(a, b, A_log, dt_bias)
+        g = np.empty(a.shape)
+        be = np.empty(a.shape)
+        assert lib.oracle_gdn_gates(a.ctypes.data, b.ctypes.data, A_log.ctypes.data,
+                                    dt_bias.ctypes.data, g.ctypes.data, be.ctypes.data,
+                                    *a.shape) == 0
+        return g, be
+
+    def l2norm(x, eps):
+        (x,) = f32(x)
+        y = np.empty(x.shape)
+        assert lib.oracle_l2norm(x.ctypes.data, float(eps), y.ctypes.data,
+                                 x.size // x.shape[-1], x.shape[-1]) == 0
+        return y
+
+    return fn, SimpleNamespace(gated=gated, gates=gates, l2norm=l2norm)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name):
     with tempfile.TemporaryDirectory() as d:
-        fn = _wrap(_build_mutant(name, d))
+        fn, ns = _wrap(_build_mutant(name, d))
         caught = []
-        for pin in P.ALL_PINS:
+        for pin, arg in [(p, fn) for p in P.ALL_PINS] + [(p, ns) for p in P.GATED_PINS]:
             try:
-                pin(fn)
+                pin(arg)
             except AssertionError:
                 caught.append(pin.__name__)
         assert caught, "planted mistake %r passed every pin" % name
