@@ -1,7 +1,7 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|copy]
+                    [--only prefill|decode|prefill_gated|decode_gated|copy]
 
 One step = one ``gdn_chunked_prefill`` call on the batched long prefill
 workload (B=4, Hk=16, Hv=32, Dk=Dv=128, S=8192, bf16 q/k/v, fp32 g/beta and
@@ -17,6 +17,10 @@ steps after W/10 warm-up passes -- and reported under "decode". It runs
 first: the GPU takes ~100 ms under load to reach steady clocks (measured:
 3 prefill warm-up steps leave the timed steps ~20 % slow), and the decode
 passes supply that load before the prefill's own warm-up. Prints ONE JSON line.
+
+The gated entry points (gate and L2-norm prologue on the device, raw q/k and
+gate pre-activations as inputs) are timed the same way on the same workloads
+and reported under "prefill_gated" and "decode_gated".
 
 ``--only copy`` runs a plain device-to-device copy of ``--copy-mib`` MiB
 (used to calibrate the HBM byte counters of rocprofv3 against a kernel of
@@ -105,19 +109,30 @@ def _events(torch, n):
             for _ in range(n)]
 
 
-def bench_prefill(torch, gdn, inputs, steps, warmup):
-    w = inputs.WORKLOADS["prefill_b4_s8192"]
-    d = inputs.draw_workload(w)
+L2_EPS = 1e-6                  # epsilon of the gated entry points' q/k normalisation
+
+
+def bench_prefill(torch, gdn, w, d, steps, warmup, gated=False):
+    """Times the prefill on the draw ``d`` (ungated: normalised q/k, g_log,
+    beta; gated: the raw q/k, a, b, A_log, dt_bias of the same draw)."""
     dev = torch.device("cuda", 0)
-    t = {k: torch.from_numpy(d[k]).to(dev) for k in d}
-    for k in ("q", "k", "v"):
+    keys = (("q_raw", "k_raw", "v", "a", "b", "A_log", "dt_bias") if gated
+            else ("q", "k", "v", "g_log", "beta"))
+    t = {k: torch.from_numpy(d[k]).to(dev) for k in keys}
+    for k in keys[:3]:
         t[k] = t[k].to(torch.bfloat16)
+    state = torch.from_numpy(d["state"]).to(dev)
     out = torch.empty((w.B, w.Hv, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], w.scale, t["state"],
-                            out=out, stream=stream)
+        if gated:
+            gdn.chunked_prefill_gated(t["q_raw"], t["k_raw"], t["v"], t["a"], t["b"], t["A_log"],
+                                      t["dt_bias"], w.scale, L2_EPS, state, out=out,
+                                      stream=stream)
+        else:
+            gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], w.scale, state,
+                                out=out, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -133,22 +148,29 @@ def bench_prefill(torch, gdn, inputs, steps, warmup):
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     ms_step = (t1 - t0) * 1e3 / steps
     nbytes, flops = prefill_algorithmic(w.B, w.Hk, w.Hv, w.S, w.Dk, w.Dv)
-    return w, d, ms_step, kern_ms, nbytes, flops
+    return ms_step, kern_ms, nbytes, flops
 
 
-def bench_decode(torch, gdn, inputs, reps, warmup):
-    w = inputs.WORKLOADS["decode_b256"]
-    state0, steps = inputs.draw_decode_steps(w)
+def bench_decode(torch, gdn, w, state0, steps, reps, warmup, gated=False):
+    """Times ``reps`` passes over the decode steps (each a dict of one token's
+    inputs, drawn with ``raw=True``), state carried on the device."""
     dev = torch.device("cuda", 0)
     st = torch.from_numpy(state0).to(dev)
+    tok = lambda s, k: torch.from_numpy(np.ascontiguousarray(s[k][:, :, 0])).to(dev)
     dev_steps = []
     for s in steps:
-        dev_steps.append({
-            "q": torch.from_numpy(s["q"][:, :, 0]).to(dev).to(torch.bfloat16),
-            "k": torch.from_numpy(s["k"][:, :, 0]).to(dev).to(torch.bfloat16),
-            "v": torch.from_numpy(s["v"][:, :, 0]).to(dev).to(torch.bfloat16),
-            "g": torch.from_numpy(np.ascontiguousarray(s["g_log"][:, :, 0])).to(dev),
-            "b": torch.from_numpy(np.ascontiguousarray(s["beta"][:, :, 0])).to(dev)})
+        if gated:
+            dev_steps.append({"q": tok(s, "q_raw").to(torch.bfloat16),
+                              "k": tok(s, "k_raw").to(torch.bfloat16),
+                              "v": tok(s, "v").to(torch.bfloat16),
+                              "g": tok(s, "a"), "b": tok(s, "b"),
+                              "A_log": torch.from_numpy(s["A_log"]).to(dev),
+                              "dt_bias": torch.from_numpy(s["dt_bias"]).to(dev)})
+        else:
+            dev_steps.append({"q": tok(s, "q").to(torch.bfloat16),
+                              "k": tok(s, "k").to(torch.bfloat16),
+                              "v": tok(s, "v").to(torch.bfloat16),
+                              "g": tok(s, "g_log"), "b": tok(s, "beta")})
     out = torch.empty((w.B, w.Hv, w.Dv), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -156,8 +178,12 @@ def bench_decode(torch, gdn, inputs, reps, warmup):
         for i, s in enumerate(dev_steps):
             if evs is not None:
                 evs[i][0].record(stream)
-            gdn.decode_step(s["q"], s["k"], s["v"], s["g"], s["b"], w.scale, st, out=out,
-                            stream=stream)
+            if gated:
+                gdn.decode_step_gated(s["q"], s["k"], s["v"], s["g"], s["b"], s["A_log"],
+                                      s["dt_bias"], w.scale, L2_EPS, st, out=out, stream=stream)
+            else:
+                gdn.decode_step(s["q"], s["k"], s["v"], s["g"], s["b"], w.scale, st, out=out,
+                                stream=stream)
             if evs is not None:
                 evs[i][1].record(stream)
 
@@ -173,7 +199,7 @@ def bench_decode(torch, gdn, inputs, reps, warmup):
     n = reps * len(dev_steps)
     kern_ms = float(np.mean([a.elapsed_time(b) for e in evs for a, b in e]))
     ms_step = (t1 - t0) * 1e3 / n
-    return w, steps, state0, ms_step, kern_ms, decode_algorithmic(w.B, w.Hk, w.Hv, w.Dk, w.Dv)
+    return ms_step, kern_ms, decode_algorithmic(w.B, w.Hk, w.Hv, w.Dk, w.Dv)
 
 
 def bench_copy(torch, mib, steps):
@@ -226,7 +252,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "prefill_gated", "decode_gated",
+                                       "copy"], default=None)
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -246,25 +273,37 @@ def main():
     if args.only == "copy":
         print(json.dumps({"copy": bench_copy(torch, args.copy_mib, args.steps)}), flush=True)
         return
-    if args.only == "decode":
-        dw, _, _, dms, dkern_ms, dbytes = bench_decode(torch, gdn, inputs, max(1, args.steps // 10),
-                                                       max(1, args.warmup // 10))
-        print(json.dumps({"decode_ms_per_step": dms, "kernel_ms": dkern_ms,
+    reps, dwarm = max(1, args.steps // 10), max(1, args.warmup // 10)
+    dw = inputs.WORKLOADS["decode_b256"]
+    w = inputs.WORKLOADS["prefill_b4_s8192"]
+    if args.only in ("decode", "decode_gated"):
+        dstate0, dsteps = inputs.draw_decode_steps(dw, raw=True)
+        dms, dkern_ms, dbytes = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm,
+                                             gated=args.only == "decode_gated")
+        print(json.dumps({args.only + "_ms_per_step": dms, "kernel_ms": dkern_ms,
                           "GB_s": dbytes / (dkern_ms / 1e3) / 1e9}), flush=True)
+        return
+    if args.only in ("prefill", "prefill_gated"):
+        d = inputs.draw_workload(w, raw=True)
+        ms_step, kern_ms, _, _ = bench_prefill(torch, gdn, w, d, args.steps, args.warmup,
+                                               gated=args.only == "prefill_gated")
+        print(json.dumps({args.only + "_ms_per_step": ms_step, "kernel_ms": kern_ms,
+                          "tokens_per_s": w.B * w.S / (ms_step / 1e3)}), flush=True)
         return
     # Decode first, then prefill: the GPU needs ~100 ms under load to reach its
     # steady clocks, and the decode passes (with their own warm-up) supply it
     # before the prefill's warm-up steps.
-    if args.only != "prefill":
-        dw, dsteps, dstate0, dms, dkern_ms, dbytes = bench_decode(
-            torch, gdn, inputs, max(1, args.steps // 10), max(1, args.warmup // 10))
-    w, d, ms_step, kern_ms, nbytes, flops = bench_prefill(torch, gdn, inputs, args.steps,
-                                                          args.warmup)
+    dstate0, dsteps = inputs.draw_decode_steps(dw, raw=True)
+    dms, dkern_ms, dbytes = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm)
+    gdms, gdkern_ms, _ = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm, gated=True)
+    d = inputs.draw_workload(w, raw=True)
+    ms_step, kern_ms, nbytes, flops = bench_prefill(torch, gdn, w, d, args.steps, args.warmup)
+    gms_step, gkern_ms, _, _ = bench_prefill(torch, gdn, w, d, args.steps, args.warmup,
+                                             gated=True)
     tokens = w.B * w.S
-    if args.only == "prefill":
-        print(json.dumps({"prefill_ms_per_step": ms_step, "kernel_ms": kern_ms,
-                          "tokens_per_s": tokens / (ms_step / 1e3)}), flush=True)
-        return
+    hbm = lambda b, ms: {"achieved": b / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "kernel_ms": ms,
+                         "algorithmic_bytes_per_launch": b}
     res = {
         "metric": METRIC,
         "value": tokens / (ms_step / 1e3),
@@ -281,11 +320,8 @@ def main():
         "config": {"workload": "prefill_b4_s8192", "B": w.B, "Hk": w.Hk, "Hv": w.Hv,
                    "S": w.S, "Dk": w.Dk, "Dv": w.Dv, "tokens_per_step": tokens,
                    "state": "fp32 in place, carried across steps"},
-        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_kernel",
-                     "achieved": nbytes / (kern_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": nbytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("gdn_prefill_kernel"), "kernel_ms": kern_ms,
-                     "algorithmic_bytes_per_launch": nbytes},
+        "roofline": dict(bound="hbm", kernel="gdn_prefill_kernel",
+                         traffic=measured_traffic("gdn_prefill_kernel"), **hbm(nbytes, kern_ms)),
         "mfma_util": {"achieved_tflops": flops / (kern_ms / 1e3) / 1e12,
                       "peak_tflops": BF16_PEAK_TFLOPS,
                       "frac": flops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
@@ -293,13 +329,19 @@ def main():
         "decode": {"workload": "decode_b256", "B": dw.B, "Hk": dw.Hk, "Hv": dw.Hv,
                    "value": 1e3 / dms, "unit": "steps/s", "ms_per_step": dms,
                    "tokens_per_s": dw.B * 1e3 / dms,
-                   "roofline": {"bound": "hbm", "kernel": "gdn_decode_kernel",
-                                "achieved": dbytes / (dkern_ms / 1e3) / 1e9,
-                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": dbytes / (dkern_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                "traffic": measured_traffic("gdn_decode_kernel"),
-                                "kernel_ms": dkern_ms,
-                                "algorithmic_bytes_per_launch": dbytes}},
+                   "roofline": dict(bound="hbm", kernel="gdn_decode_kernel",
+                                    traffic=measured_traffic("gdn_decode_kernel"),
+                                    **hbm(dbytes, dkern_ms))},
+        "prefill_gated": {"workload": "prefill_b4_s8192 (raw q/k, a, b, A_log, dt_bias)",
+                          "value": tokens / (gms_step / 1e3), "unit": "tokens/s",
+                          "ms_per_step": gms_step, "l2_eps": L2_EPS,
+                          "roofline": dict(bound="hbm", kernel="gdn_prefill_kernel (gated)",
+                                           **hbm(nbytes, gkern_ms))},
+        "decode_gated": {"workload": "decode_b256 (raw q/k, a, b, A_log, dt_bias)",
+                         "value": 1e3 / gdms, "unit": "steps/s", "ms_per_step": gdms,
+                         "l2_eps": L2_EPS,
+                         "roofline": dict(bound="hbm", kernel="gdn_decode_kernel (gated)",
+                                          **hbm(dbytes, gdkern_ms))},
         "host": {"cpu": platform.processor() or platform.machine(),
                  "gpu": torch.cuda.get_device_name(0)},
     }

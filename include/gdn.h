@@ -60,7 +60,8 @@ typedef enum {
     GDN_ERR_ALIGN = 5,        /* a tensor pointer is not 16-byte aligned              */
     GDN_ERR_ALIAS = 6,        /* out or state_inout overlaps another tensor argument  */
     GDN_ERR_WORKSPACE = 7,    /* workspace smaller than the queried size              */
-    GDN_ERR_HIP = 8           /* the HIP runtime refused a launch                     */
+    GDN_ERR_HIP = 8,          /* the HIP runtime refused a launch                     */
+    GDN_ERR_VALUE = 9         /* l2_eps is negative or not finite (gated entries)     */
 } gdn_status;
 
 /* Opaque stream handle: a hipStream_t. NULL selects the null stream. */
@@ -121,6 +122,51 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
                            float* state_inout, void* out,
                            int B, int Hk, int Hv, int Dk, int Dv, int dtype,
                            gdn_stream stream);
+
+/*
+ * Gated entry points: the same recurrence, preceded on the device by the
+ * prologue that the "GDN Block TKG Kernel API Reference" page lists ahead of
+ * its single-token recurrence (introduction: "l2norm/beta/g"; Parameters
+ * A_log, a per-value-head log decay, and dt_bias, a per-value-head softplus
+ * bias). Per batch b, value head h and token t:
+ *
+ *   g_log = -exp(A_log[h]) * softplus(a[b,h,t] + dt_bias[h]),
+ *           softplus(x) = ln(1 + e^x)
+ *   beta  = 1 / (1 + exp(-b[b,h,t]))
+ *   k_t   = k_raw_t / sqrt(sum_i k_raw_t[i]^2 + l2_eps), q_t likewise
+ *           (the normalisation the "GDN CTE Kernel API Reference" page
+ *           requires of its inputs, Notes; the pages give no epsilon)
+ *
+ * and then the recurrence above on (q_t, k_t, v_t, g_log, beta).
+ *
+ *   q, k        raw (un-normalised) query/key, shapes and dtype as in the
+ *               ungated entry
+ *   a, b        [B, Hv, S] fp32 ([B, Hv] for decode): gate pre-activations
+ *   A_log       [Hv] fp32, dt_bias [Hv] fp32 (4-byte aligned suffices)
+ *   l2_eps      >= 0 and finite, else GDN_ERR_VALUE; with l2_eps = 0 an
+ *               all-zero q or k row gives NaN
+ *
+ * The normalised q, k and the gates are never written to memory: the
+ * kernels fold 1/|k|, 1/|q| into per-token factors of the raw operands. All
+ * other arguments, constraints and errors are those of the ungated entry;
+ * out and state_inout must not overlap A_log or dt_bias either.
+ */
+gdn_status gdn_chunked_prefill_gated(const void* q, const void* k, const void* v,
+                                     const float* a, const float* b,
+                                     const float* A_log, const float* dt_bias,
+                                     float scale, float l2_eps,
+                                     float* state_inout, void* out,
+                                     int B, int Hk, int Hv, int S, int Dk, int Dv,
+                                     int dtype, void* workspace, size_t workspace_bytes,
+                                     gdn_stream stream);
+
+gdn_status gdn_decode_step_gated(const void* q, const void* k, const void* v,
+                                 const float* a, const float* b,
+                                 const float* A_log, const float* dt_bias,
+                                 float scale, float l2_eps,
+                                 float* state_inout, void* out,
+                                 int B, int Hk, int Hv, int Dk, int Dv, int dtype,
+                                 gdn_stream stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* gdn_status_string(int status);

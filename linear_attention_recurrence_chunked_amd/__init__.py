@@ -7,6 +7,8 @@ mirror the C ABI in ``include/gdn.h``:
 
 * :func:`chunked_prefill` -> ``gdn_chunked_prefill``
 * :func:`decode_step`     -> ``gdn_decode_step``
+* :func:`chunked_prefill_gated` -> ``gdn_chunked_prefill_gated``
+* :func:`decode_step_gated`     -> ``gdn_decode_step_gated``
 * :func:`prefill_workspace_bytes` -> ``gdn_chunked_prefill_workspace_bytes``
 * :func:`status_string`   -> ``gdn_status_string``
 
@@ -17,7 +19,8 @@ current stream, nothing else. If ``libgdn.so`` is missing these functions raise
 import ctypes
 import os
 
-__all__ = ["chunked_prefill", "decode_step", "prefill_workspace_bytes", "status_string",
+__all__ = ["chunked_prefill", "decode_step", "chunked_prefill_gated", "decode_step_gated",
+           "prefill_workspace_bytes", "status_string",
            "GdnError", "LibraryNotBuilt", "load_library", "LIB_PATH", "GDN_F32", "GDN_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_DTYPE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
-          8: "GDN_ERR_HIP"}
+          8: "GDN_ERR_HIP", 9: "GDN_ERR_VALUE"}
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -62,6 +65,13 @@ def load_library():
     lib.gdn_decode_step.restype = _I
     lib.gdn_decode_step.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                     _I, _I, _I, _I, _I, _I, _P]
+    lib.gdn_chunked_prefill_gated.restype = _I
+    lib.gdn_chunked_prefill_gated.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                              ctypes.c_float, _P, _P, _I, _I, _I, _I, _I, _I,
+                                              _I, _P, ctypes.c_size_t, _P]
+    lib.gdn_decode_step_gated.restype = _I
+    lib.gdn_decode_step_gated.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                          ctypes.c_float, _P, _P, _I, _I, _I, _I, _I, _I, _P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [_I]
     lib.gdn_version.restype = _I
@@ -175,5 +185,90 @@ def decode_step(q, k, v, g_log, beta, scale, state, out=None, stream=None):
     rc = lib.gdn_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g_log.data_ptr(),
                              beta.data_ptr(), float(scale), state.data_ptr(), out.data_ptr(),
                              B, Hk, Hv, Dk, Dv, code, _stream(stream, dev))
+    _raise(rc)
+    return out
+
+
+def _check_heads(A_log, dt_bias, Hv, dev):
+    import torch
+    for t, n in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        _check(t, n, torch.float32, dev)
+        if t.shape != (Hv,):
+            raise ValueError("%s must be [Hv]" % n)
+
+
+def chunked_prefill_gated(q, k, v, a, b, A_log, dt_bias, scale, l2_eps, state, out=None,
+                          workspace=None, stream=None):
+    """Prefill with the gate and normalisation prologue on the device
+    (``gdn_chunked_prefill_gated``).
+
+    q, k [B,Hk,S,Dk] raw (not normalised) and v [B,Hv,S,Dv], bf16 or fp32;
+    a, b [B,Hv,S] fp32 gate pre-activations; A_log, dt_bias [Hv] fp32; state
+    [B,Hv,Dk,Dv] fp32, updated in place. Returns out [B,Hv,S,Dv].
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    code = _dtype_code(q)
+    B, Hk, S, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[3]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    for t, n in ((a, "a"), (b, "b"), (state, "state")):
+        _check(t, n, torch.float32, dev)
+    _check_heads(A_log, dt_bias, Hv, dev)
+    if k.shape != q.shape or v.shape[0] != B or v.shape[2] != S:
+        raise ValueError("q/k/v shapes disagree")
+    if a.shape != (B, Hv, S) or b.shape != (B, Hv, S) or state.shape != (B, Hv, Dk, Dv):
+        raise ValueError("a/b/state shapes disagree with q/v")
+    if out is None:
+        out = torch.empty((B, Hv, S, Dv), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", q.dtype, dev)
+        if out.shape != (B, Hv, S, Dv):
+            raise ValueError("out shape must be [B,Hv,S,Dv]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = lib.gdn_chunked_prefill_gated(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(), A_log.data_ptr(),
+        dt_bias.data_ptr(), float(scale), float(l2_eps), state.data_ptr(), out.data_ptr(),
+        B, Hk, Hv, S, Dk, Dv, code, ws_ptr, ws_bytes, _stream(stream, dev))
+    _raise(rc)
+    return out
+
+
+def decode_step_gated(q, k, v, a, b, A_log, dt_bias, scale, l2_eps, state, out=None,
+                      stream=None):
+    """One-token step with the prologue on the device (``gdn_decode_step_gated``).
+
+    q, k [B,Hk,Dk] raw, v [B,Hv,Dv] (bf16 or fp32); a, b [B,Hv] fp32; A_log,
+    dt_bias [Hv] fp32; state [B,Hv,Dk,Dv] fp32, in place. Returns out [B,Hv,Dv].
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    code = _dtype_code(q)
+    B, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    for t, n in ((a, "a"), (b, "b"), (state, "state")):
+        _check(t, n, torch.float32, dev)
+    _check_heads(A_log, dt_bias, Hv, dev)
+    if k.shape != q.shape or v.shape[0] != B:
+        raise ValueError("q/k/v shapes disagree")
+    if a.shape != (B, Hv) or b.shape != (B, Hv) or state.shape != (B, Hv, Dk, Dv):
+        raise ValueError("a/b/state shapes disagree with q/v")
+    if out is None:
+        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", q.dtype, dev)
+        if out.shape != (B, Hv, Dv):
+            raise ValueError("out shape must be [B,Hv,Dv]")
+    rc = lib.gdn_decode_step_gated(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(), A_log.data_ptr(),
+        dt_bias.data_ptr(), float(scale), float(l2_eps), state.data_ptr(), out.data_ptr(),
+        B, Hk, Hv, Dk, Dv, code, _stream(stream, dev))
     _raise(rc)
     return out

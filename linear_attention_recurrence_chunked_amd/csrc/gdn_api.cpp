@@ -5,6 +5,7 @@
 #include "gdn.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "gdn_launch.h"
@@ -75,6 +76,52 @@ gdn_status validate(const Common& c, bool prefill) {
     return GDN_OK;
 }
 
+// Extra checks of the gated entry points: A_log and dt_bias [Hv] fp32, 4-byte
+// aligned, not overlapping what the call writes; l2_eps finite and >= 0.
+gdn_status validate_gates(const Common& c, const float* A_log, const float* dt_bias,
+                          float l2_eps) {
+    if (!A_log || !dt_bias) return GDN_ERR_NULL;
+    if (!(l2_eps >= 0.0f) || !isfinite(l2_eps)) return GDN_ERR_VALUE;
+    if (((uintptr_t)A_log & 3u) || ((uintptr_t)dt_bias & 3u)) return GDN_ERR_ALIGN;
+    const uint64_t es = c.dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t B = c.B, Hv = c.Hv, S = c.S, Dk = c.Dk, Dv = c.Dv;
+    Range ra, rd, rs, ro;
+    if (!extent(A_log, {Hv}, 4, ra) || !extent(dt_bias, {Hv}, 4, rd) ||
+        !extent(c.state, {B, Hv, Dk, Dv}, 4, rs) || !extent(c.out, {B, Hv, S, Dv}, es, ro))
+        return GDN_ERR_SHAPE;
+    if (overlaps(ra, rs) || overlaps(ra, ro) || overlaps(rd, rs) || overlaps(rd, ro))
+        return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
+gdn_status prefill_common(const Common& c, bool gated, const float* A_log, const float* dt_bias,
+                          float l2_eps, float scale, void* workspace, size_t workspace_bytes,
+                          gdn_stream stream) {
+    gdn_status st = validate(c, /*prefill=*/true);
+    if (st == GDN_OK && gated) st = validate_gates(c, A_log, dt_bias, l2_eps);
+    if (st != GDN_OK) return st;
+    const size_t need = gdn_chunked_prefill_workspace_bytes(c.B, c.Hk, c.Hv, c.S, c.Dk, c.Dv,
+                                                            c.dtype);
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return GDN_ERR_WORKSPACE;
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    const gdn::PrefillArgs a{c.q, c.k, c.v, c.g, c.beta, scale, c.state, c.out,
+                             c.B, c.Hk, c.Hv, c.S, c.Dk, c.Dv, gated, A_log, dt_bias, l2_eps};
+    return gdn::launch_prefill(a, c.dtype, (hipStream_t)stream) == hipSuccess ? GDN_OK
+                                                                               : GDN_ERR_HIP;
+}
+
+gdn_status decode_common(const Common& c, bool gated, const float* A_log, const float* dt_bias,
+                         float l2_eps, float scale, gdn_stream stream) {
+    gdn_status st = validate(c, /*prefill=*/false);
+    if (st == GDN_OK && gated) st = validate_gates(c, A_log, dt_bias, l2_eps);
+    if (st != GDN_OK) return st;
+    (void)hipGetLastError();
+    const gdn::DecodeArgs a{c.q, c.k, c.v, c.g, c.beta, scale, c.state, c.out,
+                            c.B, c.Hk, c.Hv, c.Dk, c.Dv, gated, A_log, dt_bias, l2_eps};
+    return gdn::launch_decode(a, c.dtype, (hipStream_t)stream) == hipSuccess ? GDN_OK
+                                                                             : GDN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,15 +139,21 @@ gdn_status gdn_chunked_prefill(const void* q, const void* k, const void* v,
                                int dtype, void* workspace, size_t workspace_bytes,
                                gdn_stream stream) {
     const Common c{q, k, v, g_log, beta, state_inout, out, B, Hk, Hv, S, Dk, Dv, dtype};
-    const gdn_status st = validate(c, /*prefill=*/true);
-    if (st != GDN_OK) return st;
-    const size_t need = gdn_chunked_prefill_workspace_bytes(B, Hk, Hv, S, Dk, Dv, dtype);
-    if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return GDN_ERR_WORKSPACE;
-    (void)hipGetLastError();  // clear a stale error so the check below is ours
-    const gdn::PrefillArgs a{q, k, v, g_log, beta, scale, state_inout, out,
-                             B, Hk, Hv, S, Dk, Dv};
-    return gdn::launch_prefill(a, dtype, (hipStream_t)stream) == hipSuccess ? GDN_OK
-                                                                             : GDN_ERR_HIP;
+    return prefill_common(c, false, nullptr, nullptr, 0.0f, scale, workspace, workspace_bytes,
+                          stream);
+}
+
+gdn_status gdn_chunked_prefill_gated(const void* q, const void* k, const void* v,
+                                     const float* a, const float* b,
+                                     const float* A_log, const float* dt_bias,
+                                     float scale, float l2_eps,
+                                     float* state_inout, void* out,
+                                     int B, int Hk, int Hv, int S, int Dk, int Dv,
+                                     int dtype, void* workspace, size_t workspace_bytes,
+                                     gdn_stream stream) {
+    const Common c{q, k, v, a, b, state_inout, out, B, Hk, Hv, S, Dk, Dv, dtype};
+    return prefill_common(c, true, A_log, dt_bias, l2_eps, scale, workspace, workspace_bytes,
+                          stream);
 }
 
 gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
@@ -109,12 +162,18 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
                            int B, int Hk, int Hv, int Dk, int Dv, int dtype,
                            gdn_stream stream) {
     const Common c{q, k, v, g_log, beta, state_inout, out, B, Hk, Hv, 1, Dk, Dv, dtype};
-    const gdn_status st = validate(c, /*prefill=*/false);
-    if (st != GDN_OK) return st;
-    (void)hipGetLastError();
-    const gdn::DecodeArgs a{q, k, v, g_log, beta, scale, state_inout, out, B, Hk, Hv, Dk, Dv};
-    return gdn::launch_decode(a, dtype, (hipStream_t)stream) == hipSuccess ? GDN_OK
-                                                                           : GDN_ERR_HIP;
+    return decode_common(c, false, nullptr, nullptr, 0.0f, scale, stream);
+}
+
+gdn_status gdn_decode_step_gated(const void* q, const void* k, const void* v,
+                                 const float* a, const float* b,
+                                 const float* A_log, const float* dt_bias,
+                                 float scale, float l2_eps,
+                                 float* state_inout, void* out,
+                                 int B, int Hk, int Hv, int Dk, int Dv, int dtype,
+                                 gdn_stream stream) {
+    const Common c{q, k, v, a, b, state_inout, out, B, Hk, Hv, 1, Dk, Dv, dtype};
+    return decode_common(c, true, A_log, dt_bias, l2_eps, scale, stream);
 }
 
 const char* gdn_status_string(int status) {
@@ -128,10 +187,11 @@ const char* gdn_status_string(int status) {
         case GDN_ERR_ALIAS: return "out or state_inout overlaps another tensor argument";
         case GDN_ERR_WORKSPACE: return "workspace too small";
         case GDN_ERR_HIP: return "HIP launch failed";
+        case GDN_ERR_VALUE: return "invalid scalar argument (l2_eps must be finite and >= 0)";
         default: return "unknown status";
     }
 }
 
-int gdn_version(void) { return 100; }
+int gdn_version(void) { return 200; }
 
 }  // extern "C"

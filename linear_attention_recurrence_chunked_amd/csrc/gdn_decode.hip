@@ -18,6 +18,14 @@
 // written with non-temporal stores (the written state is not re-read by this
 // step); measured on MI355X at B = 256 this layout streams 6.9 TB/s, against
 // 5.6 TB/s with non-temporal loads and 256 threads.
+//
+// GATED variant: the prologue the same page lists ahead of the recurrence
+// ("l2norm/beta/g"; Parameters A_log, dt_bias) runs here too. g_log and beta
+// then carry the raw a and b, g = -e^{A_log[h]} softplus(a + dt_bias[h]),
+// beta = sigmoid(b), and q, k are raw: every wave forms rk = 1/sqrt(|k|^2 +
+// eps) and rq from the staged vectors (same butterfly in every wave, so the
+// values agree) and the norms scale the reductions: x = rk S^T k,
+// y = rq S^T q, k.q = rk rq (k.q)_raw, and the write uses rk k.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -27,11 +35,12 @@ constexpr int kDecThreads = 512;
 constexpr int kDecRowPhases = kDecThreads / 32;   // 16
 constexpr int kDecRowsPerThread = 128 / kDecRowPhases;
 
-template <typename E>
+template <typename E, bool GATED>
 __global__ __launch_bounds__(kDecThreads) void gdn_decode_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const float* __restrict__ g_log, const float* __restrict__ beta, float scale,
-    float* __restrict__ state, E* __restrict__ out, int Hk, int Hv, int Dk, int Dv)
+    const float* __restrict__ g_log, const float* __restrict__ beta,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias, float l2_eps,
+    float scale, float* __restrict__ state, E* __restrict__ out, int Hk, int Hv, int Dk, int Dv)
 {
     const int bh = blockIdx.x;                 // b * Hv + h
     const int b = bh / Hv;
@@ -62,9 +71,30 @@ __global__ __launch_bounds__(kDecThreads) void gdn_decode_kernel(
         const f32x4 w = *(const f32x4*)(S + (size_t)min(r, Dk - 1) * Dv + cl);
         s[i] = (colok && r < Dk) ? w : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float a = __expf(g_log[bh]);
-    const float be = beta[bh];
+    float a, be;
+    if constexpr (GATED) {
+        const float xg = g_log[bh] + dt_bias[h];
+        const float sp = xg > 0.f ? xg + log1pf(expf(-xg)) : log1pf(expf(xg));
+        a = __expf(-expf(A_log[h]) * sp);
+        be = 1.f / (1.f + expf(-beta[bh]));
+    } else {
+        a = __expf(g_log[bh]);
+        be = beta[bh];
+    }
     __syncthreads();                           // sk, sq visible
+    float rk = 1.f, rq = 1.f;
+    if constexpr (GATED) {
+        const int ln = t & 63;
+        float pk = sk[ln] * sk[ln] + sk[ln + 64] * sk[ln + 64];
+        float pq = sq[ln] * sq[ln] + sq[ln + 64] * sq[ln + 64];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            pk += __shfl_xor(pk, off);
+            pq += __shfl_xor(pq, off);
+        }
+        rk = 1.f / sqrtf(pk + l2_eps);
+        rq = 1.f / sqrtf(pq + l2_eps);
+    }
 
     f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -88,14 +118,14 @@ __global__ __launch_bounds__(kDecThreads) void gdn_decode_kernel(
 #pragma unroll
         for (int p = 0; p < kDecRowPhases; ++p) { xs += red[0][p][t]; ys += red[1][p][t]; }
         const float vv = to_f32(v[(size_t)bh * Dv + t]);
-        const float u = be * (vv - a * xs);
+        const float u = be * (vv - a * (rk * xs));
         su[t] = u;
-        out[(size_t)bh * Dv + t] = from_f32<E>(scale * (a * ys + skq * u));
+        out[(size_t)bh * Dv + t] = from_f32<E>(scale * (a * (rq * ys) + (rk * rq * skq) * u));
     }
     __syncthreads();
 
     if (colok) {
-        const f32x4 uu = *(const f32x4*)&su[4 * cg];
+        const f32x4 uu = rk * *(const f32x4*)&su[4 * cg];   // the write uses rk k
 #pragma unroll
         for (int i = 0; i < kDecRowsPerThread; ++i) {
             const int r = r0 + kDecRowPhases * i;
@@ -107,19 +137,24 @@ __global__ __launch_bounds__(kDecThreads) void gdn_decode_kernel(
     }
 }
 
-template <typename E>
+template <typename E, bool GATED>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream)
 {
     const unsigned grid = (unsigned)a.B * (unsigned)a.Hv;
-    hipLaunchKernelGGL(gdn_decode_kernel<E>, dim3(grid), dim3(kDecThreads), 0, stream,
-                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.g_log, a.beta, a.scale,
+    hipLaunchKernelGGL((gdn_decode_kernel<E, GATED>), dim3(grid), dim3(kDecThreads), 0, stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.g_log, a.beta,
+                       a.A_log, a.dt_bias, a.l2_eps, a.scale,
                        a.state, (E*)a.out, a.Hk, a.Hv, a.Dk, a.Dv);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream)
 {
-    return dtype == 1 ? launch_decode_t<bf16>(a, stream) : launch_decode_t<float>(a, stream);
+    if (a.gated)
+        return dtype == 1 ? launch_decode_t<bf16, true>(a, stream)
+                          : launch_decode_t<float, true>(a, stream);
+    return dtype == 1 ? launch_decode_t<bf16, false>(a, stream)
+                      : launch_decode_t<float, false>(a, stream);
 }
 
 }  // namespace gdn

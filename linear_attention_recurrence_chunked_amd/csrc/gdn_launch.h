@@ -7,11 +7,17 @@
 
 namespace gdn {
 
+// With gated = false g_log and beta are the per-token decay and write
+// strength and q, k arrive L2-normalised; with gated = true g_log and beta
+// carry the raw gate inputs a and b, q and k are raw, and the kernels apply
+// the prologue with A_log, dt_bias [Hv] and l2_eps (unused otherwise).
 struct PrefillArgs {
     const void* q; const void* k; const void* v;
     const float* g_log; const float* beta; float scale;
     float* state; void* out;
     int B, Hk, Hv, S, Dk, Dv;
+    bool gated;
+    const float* A_log; const float* dt_bias; float l2_eps;
 };
 
 struct DecodeArgs {
@@ -19,6 +25,8 @@ struct DecodeArgs {
     const float* g_log; const float* beta; float scale;
     float* state; void* out;
     int B, Hk, Hv, Dk, Dv;
+    bool gated;
+    const float* A_log; const float* dt_bias; float l2_eps;
 };
 
 // dtype: 0 = fp32 operands, 1 = bf16 operands (gdn_dtype).

@@ -46,6 +46,17 @@
 // read once per slice, out written once, the state read and written once.
 // On the bf16 path every computed operand (S, T, R, P, U) is carried as a
 // hi/lo bf16 pair (see gdn_mfma.h), so products keep about 16 bits.
+//
+// GATED variant: the decode block's prologue ("GDN Block TKG Kernel API
+// Reference": introduction, "l2norm/beta/g"; Parameters A_log, dt_bias) runs
+// inside the stagers. The g_log/beta streams then carry the raw a and b, and
+// per token g = -e^{A_log[h]} softplus(a + dt_bias[h]), beta = sigmoid(b),
+// rk = 1/sqrt(|k|^2 + eps), rq likewise. The raw q and k tiles go to the
+// matrix cores unchanged and the norms ride on the per-token scalars:
+// A[r][s] = (beta_r rk_r) rk_s e^{..} (k_r.k_s), P[r][s] = rq_r rk_s e^{..}
+// (q_r.k_s), and R, the Q S0 term and the state update take rk_t, rq_t and
+// rk_t in their existing per-token factors. No normalised copy of q or k is
+// rounded to bf16.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 #include "gdn_mfma.h"
@@ -115,7 +126,7 @@ struct PipeCfg {
     // LDS layout (bytes)
     static constexpr int SZ_K = C * LDK * ES;
     static constexpr int SZ_V = C * LDV * ES;
-    static constexpr int SZ_SC = 8 * C * 4;
+    static constexpr int SZ_SC = (8 * C + 4) * 4;
     static constexpr int OFF_SK = 0, OFF_SQ = SZ_K, OFF_SV = 2 * SZ_K, OFF_SSC = 2 * SZ_K + SZ_V;
     static constexpr int SZ_SLOT = 2 * SZ_K + SZ_V + SZ_SC;
     static constexpr int SZ_TP = C * LDP * ES;
@@ -135,10 +146,11 @@ struct PipeCfg {
     static constexpr int OFF_P = OFF_T + NTBUF * SZ_TP;
     static constexpr int OFF_SLOTS = OFF_P + 2 * SZ_TP;
     static constexpr int LDS_BYTES = OFF_SLOTS + NSLOT * SZ_SLOT;
-    // scalar arrays inside a slot (floats): gamma, scale e^gamma, beta, beta e^gamma,
-    // e^{gamma_C - gamma}, [0] = e^{gamma_C}
+    // scalar arrays inside a slot (floats): gamma, scale e^gamma, beta, beta e^gamma rk,
+    // e^{gamma_C - gamma} rk, and on the GATED path rk, rq, beta rk; [0] = e^{gamma_C}
+    // (rk = rq = 1 without the prologue)
     static constexpr int SC_GAM = 0, SC_EG = C, SC_B = 2 * C, SC_BK = 3 * C, SC_DL = 4 * C,
-                         SC_EGC = 5 * C;
+                         SC_RK = 5 * C, SC_RQ = 6 * C, SC_BRK = 7 * C, SC_EGC = 8 * C;
 
     static_assert(C == 32, "the pipeline is laid out for 32-token chunks");
     static_assert(DK % 32 == 0 && BV % 16 == 0 && BV <= 64, "tile sizes");
@@ -147,11 +159,21 @@ struct PipeCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KiB LDS of a CU");
 };
 
-template <typename E, int C, int DK, int BV>
+// ln(1 + e^x) without overflow
+__device__ __forceinline__ float softplus_f(float x) {
+    return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+}
+
+// g_log, beta and the q/k streams: without GATED g_log and beta are the
+// per-token decay and write strength and q, k are L2-normalised by the
+// caller; with GATED g_log and beta carry the raw a and b of the prologue
+// and q, k are raw (A_log, dt_bias [Hv] and l2_eps are used only then).
+template <typename E, int C, int DK, int BV, bool GATED>
 __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const float* __restrict__ g_log, const float* __restrict__ beta, float scale,
-    float* __restrict__ state, E* __restrict__ out,
+    const float* __restrict__ g_log, const float* __restrict__ beta,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias, float l2_eps,
+    float scale, float* __restrict__ state, E* __restrict__ out,
     int Hk, int Hv, int S, int Dk, int Dv, int nvt)
 {
     using Cf = PipeCfg<E, C, DK, BV>;
@@ -237,7 +259,30 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             *(VecE*)(dst + t * LDK + d0) = r[n];
         }
     };
+    // GATED: dst[t] = 1/sqrt(|row t|^2 + eps) for the 32 rows of a chunk held
+    // as by load_rows (after store_rows zeroed any ragged columns). Lane l
+    // holds columns kd0 .. kd0+VE-1 of rows l / KPR + KRI n; the KPR lanes of
+    // a row add their partial sums in a fixed butterfly.
+    auto row_norms = [&](const VecE (&r)[Cf::NVK], float* dst) __attribute__((always_inline)) {
+        float ss[Cf::NVK];
+#pragma unroll
+        for (int n = 0; n < Cf::NVK; ++n) {
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) { const float x = to_f32(r[n][e]); acc += x * x; }
+            ss[n] = acc;
+        }
+#pragma unroll
+        for (int m = 1; m < KPR; m <<= 1)
+#pragma unroll
+            for (int n = 0; n < Cf::NVK; ++n) ss[n] += __shfl_xor(ss[n], m);
+        if (l % KPR == 0) {
+#pragma unroll
+            for (int n = 0; n < Cf::NVK; ++n) dst[l / KPR + KRI * n] = 1.f / sqrtf(ss[n] + l2_eps);
+        }
+    };
     struct KRegs { VecE k[Cf::NVK]; float g, b; };
+    float expA = 1.f, dtb = 0.f;                 // GATED: e^{A_log[h]}, dt_bias[h] (K stager)
     const uint32_t goff = (uint32_t)min(l, C - 1) * 4;
     const __amdgpu_buffer_rsrc_t rs_g = __builtin_amdgcn_make_buffer_rsrc((void*)gb, (short)0, S * 4, kBufDword3);
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)bb, (short)0, S * 4, kBufDword3);
@@ -251,7 +296,19 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         store_rows(R.k, (E*)(slot + Cf::OFF_SK));
         // gamma = inclusive cumulative sum of g over the chunk, and the scalars
         float* sc = (float*)(slot + Cf::OFF_SSC);
-        float x = l < C ? R.g : 0.f;
+        float gl = R.g, be = R.b, rk = 1.f;
+        if constexpr (GATED) {
+            row_norms(R.k, sc + Cf::SC_RK);
+            gl = -expA * softplus_f(R.g + dtb);
+            be = 1.f / (1.f + expf(-R.b));
+            // The norms written above are read back per token. LDS accesses of a
+            // wave complete in program order, so only the compiler must keep
+            // the read after the writes (no memory fence: that would also wait
+            // for the next chunk's loads in flight).
+            __builtin_amdgcn_wave_barrier();
+            rk = sc[Cf::SC_RK + min(l, C - 1)];
+        }
+        float x = l < C ? gl : 0.f;
 #pragma unroll
         for (int off = 1; off < C; off <<= 1) {
             const float y = __shfl_up(x, off);
@@ -262,9 +319,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             const float eg = __expf(x);
             sc[Cf::SC_GAM + l] = x;
             sc[Cf::SC_EG + l] = scale * eg;
-            sc[Cf::SC_B + l] = R.b;
-            sc[Cf::SC_BK + l] = R.b * eg;
-            sc[Cf::SC_DL + l] = __expf(gC - x);   // gC <= x: never overflows
+            sc[Cf::SC_B + l] = be;
+            sc[Cf::SC_BK + l] = be * eg * rk;
+            sc[Cf::SC_DL + l] = __expf(gC - x) * rk;   // gC <= x: never overflows
+            if constexpr (GATED) sc[Cf::SC_BRK + l] = be * rk;
         }
         if (l == 0) sc[Cf::SC_EGC] = __expf(gC);
     };
@@ -287,6 +345,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     auto stage_qv_store = [&](int c, QVRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
         store_rows(R.q, (E*)(slot + Cf::OFF_SQ));
+        if constexpr (GATED) row_norms(R.q, (float*)(slot + Cf::OFF_SSC) + Cf::SC_RQ);
         E* sV = (E*)(slot + Cf::OFF_SV);
         if (!vfull) {                            // uniform: only with a ragged value slice
 #pragma unroll
@@ -300,18 +359,21 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     };
 
     // ------------------------------------------------------------ producers
-    // Per-lane gamma/beta for the rows (16 ti + lr + e) and columns (16 tj + lc)
-    // of the three lower 16x16 tiles of a chunk, read once.
-    struct TileScalars { float gr[2][4], br[2][4], gs[2]; };
-    auto tile_scalars = [&](const float* __restrict__ sc) __attribute__((always_inline)) {
+    // Per-lane gamma and factors for the rows (16 ti + lr + e) and columns
+    // (16 tj + lc) of the three lower 16x16 tiles of a chunk, read once: the
+    // row factor from scalar array `rowf` (none when rowf < 0), the column
+    // factor rk_s (GATED only).
+    struct TileScalars { float gr[2][4], br[2][4], gs[2], cs[2]; };
+    auto tile_scalars = [&](const float* __restrict__ sc, int rowf) __attribute__((always_inline)) {
         TileScalars ts;
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
             ts.gs[ti] = sc[Cf::SC_GAM + 16 * ti + lc];
+            ts.cs[ti] = GATED ? sc[Cf::SC_RK + 16 * ti + lc] : 1.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 ts.gr[ti][e] = sc[Cf::SC_GAM + 16 * ti + lr + e];
-                ts.br[ti][e] = sc[Cf::SC_B + 16 * ti + lr + e];
+                ts.br[ti][e] = rowf >= 0 ? sc[rowf + 16 * ti + lr + e] : 1.f;
             }
         }
         return ts;
@@ -322,7 +384,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         const char* slot = slot_ptr(c);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
         float* __restrict__ sA = (float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
-        const TileScalars ts = tile_scalars((const float*)(slot + Cf::OFF_SSC));
+        const TileScalars ts =
+            tile_scalars((const float*)(slot + Cf::OFF_SSC), GATED ? Cf::SC_BRK : Cf::SC_B);
         // K K^T on the three lower tiles; per 32-deep step the K fragments of
         // both row tiles are loaded once and serve as both operands. Decay
         // factors e^{gamma_r - gamma_s} are only used where s < r.
@@ -339,17 +402,17 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         f32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {   // A11, stored transposed: [s][r], one vector per lane
-            const float dec = __expf(ts.gr[0][e] - ts.gs[0]);
+            const float dec = __expf(ts.gr[0][e] - ts.gs[0]) * ts.cs[0];
             w[e] = (lc < lr + e) ? ts.br[0][e] * dec * acc3[0][e] : 0.f;
         }
         *(f32x4*)(sA + Cf::AB_11T + lc * ALD + lr) = w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // A21 row-major: [r][s]
-            const float d21 = __expf(ts.gr[1][e] - ts.gs[0]);
+            const float d21 = __expf(ts.gr[1][e] - ts.gs[0]) * ts.cs[0];
             sA[Cf::AB_21 + (lr + e) * ALD + lc] = ts.br[1][e] * d21 * acc3[1][e];
             // A22 reversed: entry [15 - r][15 - s]
-            const float d22 = __expf(ts.gr[1][e] - ts.gs[1]);
+            const float d22 = __expf(ts.gr[1][e] - ts.gs[1]) * ts.cs[1];
             sA[Cf::AB_22R + (15 - lr - e) * ALD + 15 - lc] =
                 (lc < lr + e) ? ts.br[1][e] * d22 * acc3[2][e] : 0.f;
         }
@@ -502,13 +565,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
     };
 
-    // P wave: P = scale (Q K^T (.) Mincl).
+    // P wave: P = scale (Q K^T (.) Mincl) (GATED: times rq_r rk_s).
     auto build_P = [&](int c) __attribute__((always_inline)) {
         const char* slot = slot_ptr(c);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
         const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
         E* __restrict__ Pp = (E*)(smem + Cf::OFF_P + (c & 1) * Cf::SZ_TP);
-        const TileScalars ts = tile_scalars((const float*)(slot + Cf::OFF_SSC));
+        const TileScalars ts =
+            tile_scalars((const float*)(slot + Cf::OFF_SSC), GATED ? Cf::SC_RQ : -1);
         F kf[2][NKS], qf[2][NKS];
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
@@ -527,7 +591,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * ti + lr + e;
-                const float dec = __expf(ts.gr[ti][e] - ts.gs[tj]);
+                const float dec = __expf(ts.gr[ti][e] - ts.gs[tj]) * (ts.br[ti][e] * ts.cs[tj]);
                 store_pair<SP>(Pp + r * LDP + tpos(s), C, (s <= r) ? scale * dec * acc[e] : 0.f);
             }
         }
@@ -559,7 +623,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 bk[ti][e] = sc[Cf::SC_BK + t];
                 dl[ti][e] = sc[Cf::SC_DL + t];
             }
-            egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];   // scale e^gamma of token 16 ti + lc
+            egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];   // scale e^gamma (rq) of token 16 ti + lc
+            if constexpr (GATED) egt[ti] *= sc[Cf::SC_RQ + 16 * ti + lc];
         }
         const float egC = sc[Cf::SC_EGC];
         // LDS operands are read one stage ahead of the products that use them
@@ -777,6 +842,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             __syncthreads();
         }
     } else if (wave == Cf::W_S) {
+        if constexpr (GATED) { expA = expf(A_log[h]); dtb = dt_bias[h]; }
         // Loads are issued a full step before their data is stored: at step i
         // the loads of chunk i + LEAD + 1 go out first, then chunk i + LEAD
         // (loaded during step i - 1) is stored. Two register sets alternate
@@ -828,16 +894,17 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 
 // ---------------------------------------------------------------- launch
 
-template <typename E, int DK, int BV>
+template <typename E, int DK, int BV, bool GATED>
 static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream)
 {
     using Cf = PipeCfg<E, 32, DK, BV>;
     const int nvt = (a.Dv + BV - 1) / BV;
     const long long blocks = (long long)nvt * a.Hv * a.B;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gdn_prefill_kernel<E, 32, DK, BV>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((gdn_prefill_kernel<E, 32, DK, BV, GATED>), dim3((unsigned)blocks),
                        dim3(Cf::THREADS), 0, stream,
-                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.g_log, a.beta, a.scale,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.g_log, a.beta,
+                       a.A_log, a.dt_bias, a.l2_eps, a.scale,
                        a.state, (E*)a.out, a.Hk, a.Hv, a.S, a.Dk, a.Dv, nvt);
     return hipGetLastError();
 }
@@ -853,22 +920,30 @@ static int pick_bv(const PrefillArgs& a, int max_bv)
     return 16;
 }
 
-template <typename E, int DK>
+template <typename E, int DK, bool GATED>
 static hipError_t launch_dk(const PrefillArgs& a, int max_bv, hipStream_t stream)
 {
     switch (pick_bv(a, max_bv)) {
-        case 64: if constexpr (sizeof(E) == 2) return launch_cfg<E, DK, 64>(a, stream);
+        case 64: if constexpr (sizeof(E) == 2) return launch_cfg<E, DK, 64, GATED>(a, stream);
                  [[fallthrough]];
-        case 32: return launch_cfg<E, DK, 32>(a, stream);
-        default: return launch_cfg<E, DK, 16>(a, stream);
+        case 32: return launch_cfg<E, DK, 32, GATED>(a, stream);
+        default: return launch_cfg<E, DK, 16, GATED>(a, stream);
     }
+}
+
+template <bool GATED>
+static hipError_t launch_gated(const PrefillArgs& a, int dtype, hipStream_t stream)
+{
+    if (dtype == 1)
+        return a.Dk <= 64 ? launch_dk<bf16, 64, GATED>(a, 64, stream)
+                          : launch_dk<bf16, 128, GATED>(a, 64, stream);
+    return a.Dk <= 64 ? launch_dk<float, 64, GATED>(a, 32, stream)
+                      : launch_dk<float, 128, GATED>(a, 32, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, hipStream_t stream)
 {
-    if (dtype == 1)
-        return a.Dk <= 64 ? launch_dk<bf16, 64>(a, 64, stream) : launch_dk<bf16, 128>(a, 64, stream);
-    return a.Dk <= 64 ? launch_dk<float, 64>(a, 32, stream) : launch_dk<float, 128>(a, 32, stream);
+    return a.gated ? launch_gated<true>(a, dtype, stream) : launch_gated<false>(a, dtype, stream);
 }
 
 }  // namespace gdn

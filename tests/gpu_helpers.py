@@ -90,3 +90,19 @@ def check(name, dtype, out, ref_out, st, ref_st, tol=None):
     assert eo <= tol["out"], "%s: out error %.3e > %.0e" % (name, eo, tol["out"])
     assert es <= tol["state"], "%s: state error %.3e > %.0e" % (name, es, tol["state"])
     return eo, es
+
+
+def upload_raw(d, dtype, device="cuda"):
+    """Raw prologue inputs of a draw with ``raw=True`` -> device tensors:
+    q, k (un-normalised) and v in the compute dtype; a, b, A_log, dt_bias and
+    the state in fp32."""
+    import torch
+    td = torch_dtype(dtype)
+    out = {}
+    for key, src in (("q", "q_raw"), ("k", "k_raw"), ("v", "v")):
+        out[key] = torch.from_numpy(np.ascontiguousarray(d[src])).to(device=device, dtype=td)
+    for key in ("a", "b", "A_log", "dt_bias"):
+        out[key] = torch.from_numpy(np.ascontiguousarray(d[key])).to(device)
+    if d.get("state") is not None:
+        out["state"] = torch.from_numpy(np.ascontiguousarray(d["state"])).to(device)
+    return out

@@ -12,7 +12,7 @@ import linear_attention_recurrence_chunked_amd as gdn
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                       "include", "gdn.h")
 
-OK, NULL, SHAPE, UNSUP, DTYPE, ALIGN, ALIAS, WS, HIP = range(9)
+OK, NULL, SHAPE, UNSUP, DTYPE, ALIGN, ALIAS, WS, HIP, VALUE = range(10)
 
 
 def declared_functions():
@@ -32,6 +32,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"gdn_chunked_prefill", "gdn_decode_step",
+                          "gdn_chunked_prefill_gated", "gdn_decode_step_gated",
                           "gdn_chunked_prefill_workspace_bytes", "gdn_status_string",
                           "gdn_version"}
     for n in names:
@@ -39,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = lib.gdn_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.gdn_status_string(99).decode() == "unknown status"
@@ -74,7 +75,26 @@ def decode(lib, q=None, k=None, v=None, g=None, b=None, st=None, out=None,
                                P(st, 5), P(out, 6), B, Hk, Hv, Dk, Dv, dtype, None)
 
 
-CALLS = {"prefill": prefill, "decode": decode}
+def prefill_gated(lib, q=None, k=None, v=None, g=None, b=None, st=None, out=None, al=None,
+                  dtb=None, eps=1e-6, B=2, Hk=2, Hv=4, S=128, Dk=64, Dv=64, dtype=1, ws=None,
+                  wsb=0):
+    P = lambda x, i: fake(i) if x is None else x
+    return lib.gdn_chunked_prefill_gated(P(q, 0), P(k, 1), P(v, 2), P(g, 3), P(b, 4),
+                                         P(al, 7), P(dtb, 8), 0.125, eps, P(st, 5), P(out, 6),
+                                         B, Hk, Hv, S, Dk, Dv, dtype, ws, wsb, None)
+
+
+def decode_gated(lib, q=None, k=None, v=None, g=None, b=None, st=None, out=None, al=None,
+                 dtb=None, eps=1e-6, B=2, Hk=2, Hv=4, Dk=64, Dv=64, dtype=1):
+    P = lambda x, i: fake(i) if x is None else x
+    return lib.gdn_decode_step_gated(P(q, 0), P(k, 1), P(v, 2), P(g, 3), P(b, 4), P(al, 7),
+                                     P(dtb, 8), 0.125, eps, P(st, 5), P(out, 6), B, Hk, Hv,
+                                     Dk, Dv, dtype, None)
+
+
+CALLS = {"prefill": prefill, "decode": decode, "prefill_gated": prefill_gated,
+         "decode_gated": decode_gated}
+GATED = {"prefill_gated": prefill_gated, "decode_gated": decode_gated}
 
 
 @pytest.mark.parametrize("which", sorted(CALLS))
@@ -100,6 +120,36 @@ def test_bad_shape(lib, which, kw):
 @pytest.mark.parametrize("S", [0, 1, 63, 65, 100, 8191])
 def test_prefill_sequence_length_multiple_of_chunk(lib, S):
     assert prefill(lib, S=S) == SHAPE
+    assert prefill_gated(lib, S=S) == SHAPE
+
+
+@pytest.mark.parametrize("which", sorted(GATED))
+@pytest.mark.parametrize("arg", ["al", "dtb"])
+def test_gated_null_head_params(lib, which, arg):
+    assert GATED[which](lib, **{arg: 0}) == NULL
+
+
+@pytest.mark.parametrize("which", sorted(GATED))
+@pytest.mark.parametrize("eps", [-1e-6, float("nan"), float("inf"), -float("inf")])
+def test_gated_bad_epsilon(lib, which, eps):
+    assert GATED[which](lib, eps=eps) == VALUE
+
+
+@pytest.mark.parametrize("which", sorted(GATED))
+@pytest.mark.parametrize("arg", ["al", "dtb"])
+def test_gated_head_params_alignment(lib, which, arg):
+    idx = {"al": 7, "dtb": 8}[arg]
+    assert GATED[which](lib, **{arg: fake(idx, 2)}) == ALIGN
+    # 4-byte alignment suffices: the call then fails only on the bad dtype
+    assert GATED[which](lib, **{arg: fake(idx, 4)}, dtype=9) == DTYPE
+
+
+@pytest.mark.parametrize("which", sorted(GATED))
+@pytest.mark.parametrize("arg", ["al", "dtb"])
+def test_gated_writes_overlapping_head_params(lib, which, arg):
+    idx = {"al": 7, "dtb": 8}[arg]
+    assert GATED[which](lib, out=fake(idx, 0)) == ALIAS
+    assert GATED[which](lib, st=fake(idx, 0)) == ALIAS
 
 
 @pytest.mark.parametrize("which", sorted(CALLS))
