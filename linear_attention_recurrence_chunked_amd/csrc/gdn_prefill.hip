@@ -48,15 +48,17 @@
 // hi/lo bf16 pair (see gdn_mfma.h), so products keep about 16 bits.
 //
 // GATED variant: the decode block's prologue ("GDN Block TKG Kernel API
-// Reference": introduction, "l2norm/beta/g"; Parameters A_log, dt_bias) runs
-// inside the stagers. The g_log/beta streams then carry the raw a and b, and
-// per token g = -e^{A_log[h]} softplus(a + dt_bias[h]), beta = sigmoid(b),
-// rk = 1/sqrt(|k|^2 + eps), rq likewise. The raw q and k tiles go to the
-// matrix cores unchanged and the norms ride on the per-token scalars:
-// A[r][s] = (beta_r rk_r) rk_s e^{..} (k_r.k_s), P[r][s] = rq_r rk_s e^{..}
-// (q_r.k_s), and R, the Q S0 term and the state update take rk_t, rq_t and
-// rk_t in their existing per-token factors. No normalised copy of q or k is
-// rounded to bf16.
+// Reference": introduction, "l2norm/beta/g"; Parameters A_log, dt_bias) is
+// fused in. The g_log/beta streams then carry the raw a and b; the K stager
+// forms g = -e^{A_log[h]} softplus(a + dt_bias[h]) and beta = sigmoid(b) per
+// token. The raw q and k tiles go to the matrix cores unchanged and the
+// norms rk = 1/sqrt(|k|^2 + eps), rq likewise, ride on per-token factors:
+// |k_t|^2 is the diagonal of the K K^T tiles the A builder computes anyway,
+// so it forms rk and folds it into A[r][s] (rk_r rk_s), into beta e^gamma
+// (the K S0 term of R) and into e^{gamma_C - gamma} (the state update);
+// the P wave adds the two diagonal Q Q^T tiles for rq and folds rq rk_s into
+// P and rq into scale e^gamma (the Q S0 term). The consumers' code is the
+// same for both variants, and no normalised copy of q or k is rounded.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 #include "gdn_mfma.h"
@@ -146,11 +148,12 @@ struct PipeCfg {
     static constexpr int OFF_P = OFF_T + NTBUF * SZ_TP;
     static constexpr int OFF_SLOTS = OFF_P + 2 * SZ_TP;
     static constexpr int LDS_BYTES = OFF_SLOTS + NSLOT * SZ_SLOT;
-    // scalar arrays inside a slot (floats): gamma, scale e^gamma, beta, beta e^gamma rk,
-    // e^{gamma_C - gamma} rk, and on the GATED path rk, rq, beta rk; [0] = e^{gamma_C}
-    // (rk = rq = 1 without the prologue)
+    // scalar arrays inside a slot (floats): gamma, scale e^gamma, beta, beta e^gamma,
+    // e^{gamma_C - gamma}, [0] = e^{gamma_C}; on the GATED path rk (A builder), rq and
+    // the P wave's own rk (P wave), and the second, third and fifth arrays carry the
+    // factors rq, rk, rk once the A builder and the P wave have folded them in.
     static constexpr int SC_GAM = 0, SC_EG = C, SC_B = 2 * C, SC_BK = 3 * C, SC_DL = 4 * C,
-                         SC_RK = 5 * C, SC_RQ = 6 * C, SC_BRK = 7 * C, SC_EGC = 8 * C;
+                         SC_RK = 5 * C, SC_RQ = 6 * C, SC_RKP = 7 * C, SC_EGC = 8 * C;
 
     static_assert(C == 32, "the pipeline is laid out for 32-token chunks");
     static_assert(DK % 32 == 0 && BV % 16 == 0 && BV <= 64, "tile sizes");
@@ -159,9 +162,18 @@ struct PipeCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KiB LDS of a CU");
 };
 
-// ln(1 + e^x) without overflow
+// ln(1 + e^x) = max(x, 0) + log1p(e^{-|x|}), with log1p(t) = ln(u) t / (u - 1),
+// u = 1 + t, which cancels the rounding of u (accurate also for tiny t).
 __device__ __forceinline__ float softplus_f(float x) {
-    return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+    const float t = __expf(-fabsf(x));
+    const float u = 1.f + t;
+    const float lp = u == 1.f ? t : __logf(u) * (t * __builtin_amdgcn_rcpf(u - 1.f));
+    return fmaxf(x, 0.f) + lp;
+}
+
+// Element e (0..3, lane-dependent) of v, by selection (no indexed register access).
+__device__ __forceinline__ float pick4(f32x4 v, int e) {
+    return e == 0 ? v[0] : e == 1 ? v[1] : e == 2 ? v[2] : v[3];
 }
 
 // g_log, beta and the q/k streams: without GATED g_log and beta are the
@@ -259,28 +271,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             *(VecE*)(dst + t * LDK + d0) = r[n];
         }
     };
-    // GATED: dst[t] = 1/sqrt(|row t|^2 + eps) for the 32 rows of a chunk held
-    // as by load_rows (after store_rows zeroed any ragged columns). Lane l
-    // holds columns kd0 .. kd0+VE-1 of rows l / KPR + KRI n; the KPR lanes of
-    // a row add their partial sums in a fixed butterfly.
-    auto row_norms = [&](const VecE (&r)[Cf::NVK], float* dst) __attribute__((always_inline)) {
-        float ss[Cf::NVK];
-#pragma unroll
-        for (int n = 0; n < Cf::NVK; ++n) {
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) { const float x = to_f32(r[n][e]); acc += x * x; }
-            ss[n] = acc;
-        }
-#pragma unroll
-        for (int m = 1; m < KPR; m <<= 1)
-#pragma unroll
-            for (int n = 0; n < Cf::NVK; ++n) ss[n] += __shfl_xor(ss[n], m);
-        if (l % KPR == 0) {
-#pragma unroll
-            for (int n = 0; n < Cf::NVK; ++n) dst[l / KPR + KRI * n] = 1.f / sqrtf(ss[n] + l2_eps);
-        }
-    };
     struct KRegs { VecE k[Cf::NVK]; float g, b; };
     float expA = 1.f, dtb = 0.f;                 // GATED: e^{A_log[h]}, dt_bias[h] (K stager)
     const uint32_t goff = (uint32_t)min(l, C - 1) * 4;
@@ -296,17 +286,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         store_rows(R.k, (E*)(slot + Cf::OFF_SK));
         // gamma = inclusive cumulative sum of g over the chunk, and the scalars
         float* sc = (float*)(slot + Cf::OFF_SSC);
-        float gl = R.g, be = R.b, rk = 1.f;
+        float gl = R.g, be = R.b;
         if constexpr (GATED) {
-            row_norms(R.k, sc + Cf::SC_RK);
             gl = -expA * softplus_f(R.g + dtb);
-            be = 1.f / (1.f + expf(-R.b));
-            // The norms written above are read back per token. LDS accesses of a
-            // wave complete in program order, so only the compiler must keep
-            // the read after the writes (no memory fence: that would also wait
-            // for the next chunk's loads in flight).
-            __builtin_amdgcn_wave_barrier();
-            rk = sc[Cf::SC_RK + min(l, C - 1)];
+            be = __builtin_amdgcn_rcpf(1.f + __expf(-R.b));
         }
         float x = l < C ? gl : 0.f;
 #pragma unroll
@@ -320,9 +303,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             sc[Cf::SC_GAM + l] = x;
             sc[Cf::SC_EG + l] = scale * eg;
             sc[Cf::SC_B + l] = be;
-            sc[Cf::SC_BK + l] = be * eg * rk;
-            sc[Cf::SC_DL + l] = __expf(gC - x) * rk;   // gC <= x: never overflows
-            if constexpr (GATED) sc[Cf::SC_BRK + l] = be * rk;
+            sc[Cf::SC_BK + l] = be * eg;
+            sc[Cf::SC_DL + l] = __expf(gC - x);   // gC <= x: never overflows
         }
         if (l == 0) sc[Cf::SC_EGC] = __expf(gC);
     };
@@ -345,7 +327,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     auto stage_qv_store = [&](int c, QVRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
         store_rows(R.q, (E*)(slot + Cf::OFF_SQ));
-        if constexpr (GATED) row_norms(R.q, (float*)(slot + Cf::OFF_SSC) + Cf::SC_RQ);
         E* sV = (E*)(slot + Cf::OFF_SV);
         if (!vfull) {                            // uniform: only with a ragged value slice
 #pragma unroll
@@ -361,31 +342,50 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // ------------------------------------------------------------ producers
     // Per-lane gamma and factors for the rows (16 ti + lr + e) and columns
     // (16 tj + lc) of the three lower 16x16 tiles of a chunk, read once: the
-    // row factor from scalar array `rowf` (none when rowf < 0), the column
-    // factor rk_s (GATED only).
+    // row factor is the product of scalar arrays `rowf` and `rowf2`, the
+    // column factor scalar array `colf` (each omitted when < 0).
     struct TileScalars { float gr[2][4], br[2][4], gs[2], cs[2]; };
-    auto tile_scalars = [&](const float* __restrict__ sc, int rowf) __attribute__((always_inline)) {
+    auto tile_scalars = [&](const float* sc, int rowf, int rowf2, int colf)
+        __attribute__((always_inline)) {
         TileScalars ts;
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
             ts.gs[ti] = sc[Cf::SC_GAM + 16 * ti + lc];
-            ts.cs[ti] = GATED ? sc[Cf::SC_RK + 16 * ti + lc] : 1.f;
+            ts.cs[ti] = colf >= 0 ? sc[colf + 16 * ti + lc] : 1.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ts.gr[ti][e] = sc[Cf::SC_GAM + 16 * ti + lr + e];
-                ts.br[ti][e] = rowf >= 0 ? sc[rowf + 16 * ti + lr + e] : 1.f;
+                const int t = 16 * ti + lr + e;
+                ts.gr[ti][e] = sc[Cf::SC_GAM + t];
+                ts.br[ti][e] = (rowf >= 0 ? sc[rowf + t] : 1.f) * (rowf2 >= 0 ? sc[rowf2 + t] : 1.f);
             }
         }
         return ts;
     };
+    // GATED: from the two diagonal 16x16 tiles d[0], d[1] of X X^T (X = K or Q
+    // of a chunk), dst[t] = 1/sqrt(|x_t|^2 + eps) for the 32 tokens. Lane
+    // (lr/4, lc) holds rows lr + e, column lc, so the lanes with lc / 4 == lr / 4
+    // hold the diagonal, in element lc % 4.
+    auto diag_norms = [&](const f32x4 (&d)[2], float* dst) __attribute__((always_inline)) {
+        if ((lc >> 2) == (lr >> 2)) {
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+                dst[16 * ti + lc] = __builtin_amdgcn_rsqf(pick4(d[ti], lc & 3) + l2_eps);
+        }
+        // Later reads of dst by other lanes of this wave: LDS accesses of a
+        // wave complete in program order, so only the compiler must keep them
+        // after these writes.
+        __builtin_amdgcn_wave_barrier();
+    };
 
     // A = diag(beta) (K K^T) (.) Mstrict of chunk c, into A buffer c % NABUF.
+    // GATED: rk from the diagonal of K K^T first, then A = diag(beta rk)
+    // (K K^T) diag(rk) (.) Mstrict, and rk folded into the chunk's beta
+    // e^gamma and e^{gamma_C - gamma}.
     auto build_A = [&](int c) __attribute__((always_inline)) {
-        const char* slot = slot_ptr(c);
+        char* slot = slot_ptr(c);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
+        float* sc = (float*)(slot + Cf::OFF_SSC);
         float* __restrict__ sA = (float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
-        const TileScalars ts =
-            tile_scalars((const float*)(slot + Cf::OFF_SSC), GATED ? Cf::SC_BRK : Cf::SC_B);
         // K K^T on the three lower tiles; per 32-deep step the K fragments of
         // both row tiles are loaded once and serve as both operands. Decay
         // factors e^{gamma_r - gamma_s} are only used where s < r.
@@ -398,6 +398,17 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             acc3[1] = O::mma(k1, k0, acc3[1]);
             acc3[2] = O::mma(k1, k1, acc3[2]);
         }
+        if constexpr (GATED) {
+            const f32x4 dg[2] = {acc3[0], acc3[2]};
+            diag_norms(dg, sc + Cf::SC_RK);
+            if (l < C) {
+                const float rk = sc[Cf::SC_RK + l];
+                sc[Cf::SC_BK + l] *= rk;
+                sc[Cf::SC_DL + l] *= rk;
+            }
+        }
+        const TileScalars ts = tile_scalars(sc, Cf::SC_B, GATED ? Cf::SC_RK : -1,
+                                            GATED ? Cf::SC_RK : -1);
         // lane (lr/4, lc) holds rows r = lr + e, column s = lc of each tile
         f32x4 w;
 #pragma unroll
@@ -565,14 +576,17 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
     };
 
-    // P wave: P = scale (Q K^T (.) Mincl) (GATED: times rq_r rk_s).
+    // P wave: P = scale (Q K^T (.) Mincl). GATED: rq from the diagonal of
+    // Q Q^T, P = scale diag(rq) (Q K^T) diag(rk) (.) Mincl, and rq folded into
+    // the chunk's scale e^gamma. rk comes from the A builder, which finished
+    // this chunk at least one step earlier on the bf16 path; on the fp32 path
+    // it runs in the same step, so the P wave forms its own copy.
     auto build_P = [&](int c) __attribute__((always_inline)) {
-        const char* slot = slot_ptr(c);
+        char* slot = slot_ptr(c);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
         const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
+        float* sc = (float*)(slot + Cf::OFF_SSC);
         E* __restrict__ Pp = (E*)(smem + Cf::OFF_P + (c & 1) * Cf::SZ_TP);
-        const TileScalars ts =
-            tile_scalars((const float*)(slot + Cf::OFF_SSC), GATED ? Cf::SC_RQ : -1);
         F kf[2][NKS], qf[2][NKS];
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
@@ -581,6 +595,25 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 kf[t2][m] = O::ldc(sK, LDK, 16 * t2, 32 * m);
                 qf[t2][m] = O::ldc(sQ, LDK, 16 * t2, 32 * m);
             }
+        constexpr int RKP = Cf::SPREAD ? Cf::SC_RK : Cf::SC_RKP;
+        if constexpr (GATED) {
+            f32x4 dq[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int m = 0; m < NKS; ++m) dq[ti] = O::mma(qf[ti][m], qf[ti][m], dq[ti]);
+            diag_norms(dq, sc + Cf::SC_RQ);
+            if constexpr (!Cf::SPREAD) {
+                f32x4 dk[2] = {zero4(), zero4()};
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                    for (int m = 0; m < NKS; ++m) dk[ti] = O::mma(kf[ti][m], kf[ti][m], dk[ti]);
+                diag_norms(dk, sc + Cf::SC_RKP);
+            }
+            if (l < C) sc[Cf::SC_EG + l] *= sc[Cf::SC_RQ + l];
+        }
+        const TileScalars ts = tile_scalars(sc, GATED ? Cf::SC_RQ : -1, -1, GATED ? RKP : -1);
 #pragma unroll
         for (int tt = 0; tt < 3; ++tt) {
             const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
@@ -623,8 +656,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 bk[ti][e] = sc[Cf::SC_BK + t];
                 dl[ti][e] = sc[Cf::SC_DL + t];
             }
-            egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];   // scale e^gamma (rq) of token 16 ti + lc
-            if constexpr (GATED) egt[ti] *= sc[Cf::SC_RQ + 16 * ti + lc];
+            egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];   // scale e^gamma of token 16 ti + lc
         }
         const float egC = sc[Cf::SC_EGC];
         // LDS operands are read one stage ahead of the products that use them
@@ -824,9 +856,11 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             __syncthreads();
         }
     } else if (wave == Cf::W_P) {
+        // P of chunk 0 after the second barrier: on the GATED bf16 path it
+        // reads the norms the A wave forms between the first two.
+        __syncthreads();
         __syncthreads();
         if (NC > 0) build_P(0);
-        __syncthreads();
         __syncthreads();
         for (int i = 0; i < NC; ++i) {
             if (i + 1 < NC) build_P(i + 1);
