@@ -32,13 +32,21 @@ prologue on the device: ``q_raw``, ``k_raw`` (the N(0, 1) draws of step 2,
 rounded to bf16 for bf16 workloads), ``a``, ``b`` (step 4, float32) and
 ``A_log``, ``dt_bias`` (step 1, float32). They come from the same random
 stream, so raw and derived inputs describe the same tokens.
+
+Depthwise conv1d inputs (:func:`draw_conv`), from ``rng([100, B, C, T, K,
+step])``: the raw mixed tensor ``[B, C, T]`` ~ N(0, 1) (rounded to bf16 for
+bf16), weights ``[C, K]`` ~ U(-1/sqrt(K), 1/sqrt(K)) in float32 (the default
+initialisation of a depthwise convolution with K taps), and for decode a
+window state ``[B, C, K]`` ~ N(0, 1) and one token ``[B, C]`` per step. The
+mixed tensor of the prefill workloads has C = 2 Hk Dk + Hv Dv channels (q|k|v,
+"GDN Block TKG Kernel API Reference", Dimensions) and T = S tokens.
 """
 from dataclasses import dataclass, field
 
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "bf16_round", "draw_prefill", "draw_workload",
-           "draw_decode_steps"]
+           "draw_decode_steps", "ConvWorkload", "CONV_WORKLOADS", "draw_conv"]
 
 _DECAY = {"std": (1.0, 16.0), "strong": (8.0, 64.0), "weak": (0.01, 0.1)}
 _VARIANT_ID = {"std": 0, "strong": 1, "weak": 2}
@@ -160,3 +168,42 @@ def draw_decode_steps(w, nsteps=None, variant="std", **overrides):
         del d["state"]
         steps.append(d)
     return state, steps
+
+
+@dataclass(frozen=True)
+class ConvWorkload:
+    """A depthwise conv1d workload: batch, channels, tokens (1 = decode), taps."""
+    name: str
+    B: int
+    C: int
+    T: int
+    K: int
+    dtype: str
+
+
+CONV_WORKLOADS = {
+    w.name: w for w in (
+        # the mixed q|k|v tensor of the B=4, S=8192 prefill (C = 2*16*128 + 32*128)
+        ConvWorkload("conv_prefill_b4_t8192", 4, 8192, 8192, 4, "bf16"),
+        # one decode token for the B=256 decode batch
+        ConvWorkload("conv_decode_b256", 256, 8192, 1, 4, "bf16"),
+    )
+}
+
+
+def draw_conv(B, C, T, K, dtype="bf16", step=0, decode=False):
+    """Draw conv1d inputs. Returns float32 arrays: ``x`` [B, C, T] (decode:
+    [B, C]), ``w`` [C, K], and for decode ``state`` [B, C, K]; bf16-exact
+    for dtype bf16."""
+    rng = np.random.default_rng([100, B, C, T, K, step])
+    w = rng.uniform(-1.0, 1.0, (C, K)).astype(np.float32) / np.float32(np.sqrt(K))
+    if decode:
+        x = rng.standard_normal((B, C), dtype=np.float32)
+        st = rng.standard_normal((B, C, K), dtype=np.float32)
+        if dtype == "bf16":
+            x, st = bf16_round(x), bf16_round(st)
+        return {"x": x, "w": w, "state": st}
+    x = rng.standard_normal((B, C, T), dtype=np.float32)
+    if dtype == "bf16":
+        x = bf16_round(x)
+    return {"x": x, "w": w}

@@ -433,3 +433,117 @@ GATED_PINS = [
     gpin_gated_pure_decay, gpin_gated_equals_normalised_serial, gpin_gated_norm_invariance,
     gpin_gated_heads_independent,
 ]
+
+
+# --------------------------------------------------- depthwise causal conv1d
+#
+# "GDN Conv1D Kernel API Reference": prefill returns silu(causal depthwise
+# conv1d(mixed)) and the last K raw tokens; decode shifts the window by the
+# new token and returns silu of the K-tap dot product. Every ``cpin_*`` takes
+# a namespace ``o`` with o.prefill(x, w) -> (out, state) and
+# o.decode(x, state, w) -> (out, new_state), checked against library filters
+# (scipy.signal.lfilter, numpy.convolve), the logistic function, an impulse
+# response and the prefill/decode chain.
+
+def conv_case(seed, B=2, C=5, T=11, K=4):
+    r = _rng(seed)
+    x = r.standard_normal((B, C, T)).astype(np.float32)
+    w = (r.standard_normal((C, K)) * 0.5).astype(np.float32)
+    return x, w
+
+
+def cpin_matches_lfilter(o):
+    """Per channel, the pre-activation is the FIR y[n] = sum_k b[k] x[n-k] with
+    b = the weights reversed (scipy.signal.lfilter), and out = y * expit(y)."""
+    from scipy.signal import lfilter
+    x, w = conv_case(40, B=2, C=3, T=13, K=4)
+    out, _ = o.prefill(x, w)
+    for b in range(2):
+        for c in range(3):
+            y = lfilter(w[c, ::-1].astype(np.float64), [1.0], x[b, c].astype(np.float64))
+            _close(out[b, c], y * _expit(y), 1e-13, "conv vs lfilter")
+
+
+def cpin_matches_convolve(o):
+    """The same through numpy.convolve (full convolution, first T outputs),
+    for every K from 1 to 8 and T shorter and longer than K."""
+    for K in range(1, 9):
+        for T in (1, K - 1, K, 3 * K + 2):
+            if T < 1:
+                continue
+            x, w = conv_case(41 + K, B=1, C=2, T=T, K=K)
+            out, _ = o.prefill(x, w)
+            for c in range(2):
+                y = np.convolve(x[0, c].astype(np.float64), w[c].astype(np.float64)[::-1])[:T]
+                _close(out[0, c], y * _expit(y), 1e-13, "conv vs convolve K=%d T=%d" % (K, T))
+
+
+def cpin_impulse_response(o):
+    """A unit impulse at t0 gives pre-activations w[K-1], w[K-2], ..., w[0] at
+    t0, t0+1, ..., t0+K-1 (the current token takes the last weight) and zero
+    elsewhere; silu maps them through y / (1 + e^{-y})."""
+    K, T, t0 = 4, 12, 3
+    x = np.zeros((1, 1, T), np.float32)
+    x[0, 0, t0] = 1.0
+    w = np.array([[0.5, -1.0, 2.0, 3.0]], np.float32)
+    out, _ = o.prefill(x, w)
+    y = np.zeros(T)
+    y[t0:t0 + K] = [3.0, 2.0, -1.0, 0.5]
+    _close(out[0, 0], y / (1.0 + np.exp(-y)), 1e-15, "impulse")
+    # silu closed forms: silu(0) = 0, silu(3) = 3 / (1 + e^-3)
+    assert out[0, 0, 0] == 0.0 and out[0, 0, T - 1] == 0.0
+
+
+def cpin_state_is_last_raw_tokens(o):
+    """The prefill state is the last K raw (pre-convolution) tokens, with
+    zeros in front when T < K."""
+    x, w = conv_case(50, B=2, C=3, T=9, K=4)
+    _, st = o.prefill(x, w)
+    _close(st, x[:, :, 5:9], 0.0, "state = last K raw")
+    x2, w2 = conv_case(51, B=1, C=2, T=2, K=4)
+    _, st2 = o.prefill(x2, w2)
+    exp = np.zeros((1, 2, 4))
+    exp[:, :, 2:] = x2
+    _close(st2, exp, 0.0, "state with T < K")
+
+
+def cpin_decode_continues_prefill(o):
+    """prefill(T) followed by n decode steps equals prefill(T + n): outputs
+    and window state, for K = 3 and K = 4."""
+    for K in (3, 4):
+        x, w = conv_case(52 + K, B=2, C=4, T=10, K=K)
+        full_out, full_st = o.prefill(x, w)
+        out, st = o.prefill(x[:, :, :6], w)
+        _close(out, full_out[:, :, :6], 1e-15, "prefix")
+        for t in range(6, 10):
+            ot, st = o.decode(x[:, :, t], st, w)
+            _close(ot, full_out[:, :, t], 1e-13, "decode step t=%d K=%d" % (t, K))
+        _close(st, full_st, 0.0, "decode window state")
+
+
+def cpin_decode_window_shift(o):
+    """A decode step drops the oldest token and appends the new one, and its
+    output is silu(sum_j w_j window_j), worked by hand for K = 3."""
+    st = np.array([[[1.0, 2.0, 3.0]]], np.float32)
+    w = np.array([[0.5, -1.0, 0.25]], np.float32)
+    out, nst = o.decode(np.array([[4.0]], np.float32), st, w)
+    _close(nst, [[[2.0, 3.0, 4.0]]], 0.0, "window shift")
+    y = 0.5 * 2.0 - 1.0 * 3.0 + 0.25 * 4.0          # = -1
+    _close(out, [[y / (1.0 + np.exp(-y))]], 1e-15, "decode dot product")
+
+
+def cpin_channels_independent(o):
+    """Each channel uses only its own weights and its own input row."""
+    x, w = conv_case(56, B=1, C=4, T=9, K=3)
+    out, st = o.prefill(x, w)
+    for c in range(4):
+        oc, sc = o.prefill(x[:, c:c + 1], w[c:c + 1])
+        _close(out[:, c:c + 1], oc, 0.0, "channel out")
+        _close(st[:, c:c + 1], sc, 0.0, "channel state")
+
+
+CONV_PINS = [
+    cpin_matches_lfilter, cpin_matches_convolve, cpin_impulse_response,
+    cpin_state_is_last_raw_tokens, cpin_decode_continues_prefill, cpin_decode_window_shift,
+    cpin_channels_independent,
+]

@@ -73,3 +73,10 @@ def test_gated_pin(pin):
     from types import SimpleNamespace
     pin(SimpleNamespace(gated=oracle.gdn_serial_gated, gates=oracle.gdn_gates,
                         l2norm=oracle.l2_normalize))
+
+
+@pytest.mark.parametrize("pin", P.CONV_PINS, ids=lambda f: f.__name__)
+def test_conv_pin(pin):
+    from types import SimpleNamespace
+    from oracle import conv1d
+    pin(SimpleNamespace(prefill=conv1d.conv1d_prefill, decode=conv1d.conv1d_decode))

@@ -129,3 +129,40 @@ def test_mutant_is_caught(name):
             except AssertionError:
                 caught.append(pin.__name__)
         assert caught, "planted mistake %r passed every pin" % name
+
+
+# The conv1d oracle is numpy: its mutants are edited copies of the module
+# source, executed as fresh modules.
+CONV_SRC = os.path.join(os.path.dirname(oracle.__file__), "conv1d.py")
+CONV_MUTANTS = {
+    "tap_order": ("lag = K - 1 - j", "lag = j"),
+    "lag_off_by_one": ("lag = K - 1 - j", "lag = K - j"),
+    "no_silu": ("return silu(y), state", "return y, state"),
+    "sigmoid_not_silu": ("return y / (1.0 + np.exp(-y))", "return 1.0 / (1.0 + np.exp(-y))"),
+    "state_from_output": ("state[:, :, j] = x[:, :, t]", "state[:, :, j] = y[:, :, t]"),
+    "state_off_by_one": ("t = T - K + j\n", "t = T - K + j - 1\n"),
+    "decode_shift_wrong": ("window = np.concatenate([state[:, :, 1:], x[:, :, None]], axis=2)",
+                           "window = np.concatenate([x[:, :, None], state[:, :, :-1]], axis=2)"),
+    "decode_no_silu": ("return silu(y), window", "return y, window"),
+    "wrong_channel_weights": ("w[None, :, j, None]", "w[None, ::-1, j, None]"),
+    "decode_reversed_taps": ("y += w[None, :, j] * window[:, :, j]",
+                             "y += w[None, :, K - 1 - j] * window[:, :, j]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conv_mutant_is_caught(name):
+    import types
+    old, new = CONV_MUTANTS[name]
+    src = open(CONV_SRC).read()
+    assert src.count(old) == 1, "mutation site for %s not unique" % name
+    mod = types.ModuleType("conv1d_mutant_" + name)
+    exec(compile(src.replace(old, new), "<mutant %s>" % name, "exec"), mod.__dict__)
+    ns = SimpleNamespace(prefill=mod.conv1d_prefill, decode=mod.conv1d_decode)
+    caught = []
+    for pin in P.CONV_PINS:
+        try:
+            pin(ns)
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, "planted mistake %r passed every pin" % name
