@@ -55,7 +55,8 @@ typedef enum {
     GDN_OK = 0,
     GDN_ERR_NULL = 1,         /* a required pointer is NULL                          */
     GDN_ERR_SHAPE = 2,        /* B, Hk, Hv, S < 1, Hv % Hk != 0, S % 64 != 0 (prefill) */
-    GDN_ERR_UNSUPPORTED = 3,  /* Dk or Dv outside [16, 128] or not a multiple of 16   */
+    GDN_ERR_UNSUPPORTED = 3,  /* Dk or Dv outside [16, 128] or not a multiple of 16;  *
+                               * conv1d window K > 8                                 */
     GDN_ERR_DTYPE = 4,        /* dtype is not a gdn_dtype value                       */
     GDN_ERR_ALIGN = 5,        /* a tensor pointer is not 16-byte aligned              */
     GDN_ERR_ALIAS = 6,        /* out or state_inout overlaps another tensor argument  */
@@ -167,6 +168,45 @@ gdn_status gdn_decode_step_gated(const void* q, const void* k, const void* v,
                                  float* state_inout, void* out,
                                  int B, int Hk, int Hv, int Dk, int Dv, int dtype,
                                  gdn_stream stream);
+
+/*
+ * gdn_conv1d_prefill -- depthwise causal conv1d + SiLU over T tokens and the
+ * window state, the step ahead of the recurrence ("GDN Conv1D Kernel API
+ * Reference": gdn_conv1d_prefill, Parameters, Returns, Notes).
+ *
+ *   mixed          [B, C, T]  compute dtype: raw q|k|v channels (T contiguous)
+ *   conv_weight    [C, K]     fp32 depthwise weights, 1 <= K <= 8
+ *   out            [B, C, T]  compute dtype, written:
+ *                  out[b,c,t] = silu(sum_j w[c,j] mixed[b,c,t-(K-1)+j]),
+ *                  silu(y) = y / (1 + e^{-y}), mixed = 0 before t = 0
+ *   conv_state_out [B, C, K]  compute dtype, written: the last K raw tokens,
+ *                  conv_state_out[b,c,j] = mixed[b,c,T-K+j] (0 where T-K+j < 0)
+ *
+ * The page gives no tap order, bias or window width: the weights act as a
+ * squeezed depthwise convolution weight (w[c,K-1] multiplies the current
+ * token), there is no bias, and K is an argument. Any T >= 1; pointers
+ * 16-byte aligned; out and conv_state_out overlap nothing else.
+ */
+gdn_status gdn_conv1d_prefill(const void* mixed, const float* conv_weight, void* out,
+                              void* conv_state_out, int B, int C, int T, int K, int dtype,
+                              gdn_stream stream);
+
+/*
+ * gdn_conv1d_decode -- one token ("GDN Conv1D Kernel API Reference":
+ * gdn_conv1d_decode): the window drops its oldest token and appends x, and
+ * the output is silu of its K-tap dot product with the weights.
+ *
+ *   x                [B, C]     compute dtype, the new raw token
+ *   conv_weight      [C, K]     fp32
+ *   conv_state_inout [B, C, K]  compute dtype, the previous window in, the
+ *                    shifted window out (in place; the page returns it as a
+ *                    new tensor)
+ *   out              [B, C]     compute dtype: silu(sum_j w[c,j] window[b,c,j])
+ *
+ * Same constraints as gdn_conv1d_prefill with T = 1.
+ */
+gdn_status gdn_conv1d_decode(const void* x, const float* conv_weight, void* conv_state_inout,
+                             void* out, int B, int C, int K, int dtype, gdn_stream stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* gdn_status_string(int status);

@@ -9,6 +9,8 @@ mirror the C ABI in ``include/gdn.h``:
 * :func:`decode_step`     -> ``gdn_decode_step``
 * :func:`chunked_prefill_gated` -> ``gdn_chunked_prefill_gated``
 * :func:`decode_step_gated`     -> ``gdn_decode_step_gated``
+* :func:`conv1d_prefill`  -> ``gdn_conv1d_prefill``
+* :func:`conv1d_decode`   -> ``gdn_conv1d_decode``
 * :func:`prefill_workspace_bytes` -> ``gdn_chunked_prefill_workspace_bytes``
 * :func:`status_string`   -> ``gdn_status_string``
 
@@ -20,6 +22,7 @@ import ctypes
 import os
 
 __all__ = ["chunked_prefill", "decode_step", "chunked_prefill_gated", "decode_step_gated",
+           "conv1d_prefill", "conv1d_decode",
            "prefill_workspace_bytes", "status_string",
            "GdnError", "LibraryNotBuilt", "load_library", "LIB_PATH", "GDN_F32", "GDN_BF16"]
 
@@ -72,6 +75,10 @@ def load_library():
     lib.gdn_decode_step_gated.restype = _I
     lib.gdn_decode_step_gated.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                           ctypes.c_float, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+    lib.gdn_conv1d_prefill.restype = _I
+    lib.gdn_conv1d_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
+    lib.gdn_conv1d_decode.restype = _I
+    lib.gdn_conv1d_decode.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [_I]
     lib.gdn_version.restype = _I
@@ -271,4 +278,66 @@ def decode_step_gated(q, k, v, a, b, A_log, dt_bias, scale, l2_eps, state, out=N
         dt_bias.data_ptr(), float(scale), float(l2_eps), state.data_ptr(), out.data_ptr(),
         B, Hk, Hv, Dk, Dv, code, _stream(stream, dev))
     _raise(rc)
+    return out
+
+
+def conv1d_prefill(mixed, weight, out=None, state=None, stream=None):
+    """Depthwise causal conv1d + SiLU (``gdn_conv1d_prefill``).
+
+    mixed [B,C,T] bf16 or fp32 (raw q|k|v channels); weight [C,K] fp32,
+    K <= 8. Returns (out [B,C,T], state [B,C,K]) in mixed's dtype, allocated
+    if not given: out = silu(causal conv), state = the last K raw tokens.
+    """
+    import torch
+    lib = load_library()
+    dev = mixed.device
+    code = _dtype_code(mixed)
+    _check(mixed, "mixed", mixed.dtype, dev)
+    _check(weight, "weight", torch.float32, dev)
+    if mixed.dim() != 3 or weight.dim() != 2 or weight.shape[0] != mixed.shape[1]:
+        raise ValueError("mixed must be [B,C,T] and weight [C,K]")
+    B, C, T = mixed.shape
+    K = weight.shape[1]
+    if out is None:
+        out = torch.empty_like(mixed)
+    else:
+        _check(out, "out", mixed.dtype, dev)
+        if out.shape != mixed.shape:
+            raise ValueError("out must be [B,C,T]")
+    if state is None:
+        state = torch.empty((B, C, K), dtype=mixed.dtype, device=dev)
+    else:
+        _check(state, "state", mixed.dtype, dev)
+        if state.shape != (B, C, K):
+            raise ValueError("state must be [B,C,K]")
+    _raise(lib.gdn_conv1d_prefill(mixed.data_ptr(), weight.data_ptr(), out.data_ptr(),
+                                  state.data_ptr(), B, C, T, K, code, _stream(stream, dev)))
+    return out, state
+
+
+def conv1d_decode(x, state, weight, out=None, stream=None):
+    """One conv1d decode token (``gdn_conv1d_decode``): x [B,C] and the window
+    state [B,C,K] (updated in place) in bf16 or fp32, weight [C,K] fp32.
+    Returns out [B,C]."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    code = _dtype_code(x)
+    _check(x, "x", x.dtype, dev)
+    _check(state, "state", x.dtype, dev)
+    _check(weight, "weight", torch.float32, dev)
+    if x.dim() != 2 or weight.dim() != 2 or weight.shape[0] != x.shape[1]:
+        raise ValueError("x must be [B,C] and weight [C,K]")
+    B, C = x.shape
+    K = weight.shape[1]
+    if state.shape != (B, C, K):
+        raise ValueError("state must be [B,C,K]")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check(out, "out", x.dtype, dev)
+        if out.shape != x.shape:
+            raise ValueError("out must be [B,C]")
+    _raise(lib.gdn_conv1d_decode(x.data_ptr(), weight.data_ptr(), state.data_ptr(),
+                                 out.data_ptr(), B, C, K, code, _stream(stream, dev)))
     return out

@@ -13,6 +13,7 @@
 namespace {
 
 constexpr int kChunk = 64;        // prefill chunk length (tokens)
+constexpr int kMaxConvTaps = 8;   // conv1d window width the kernels support
 constexpr int kMaxHeadDim = 128;  // Dk, Dv upper bound ("GDN CTE", Notes)
 
 struct Range {
@@ -122,6 +123,31 @@ gdn_status decode_common(const Common& c, bool gated, const float* A_log, const 
                                                                              : GDN_ERR_HIP;
 }
 
+// conv1d checks: prefill (T tokens) or decode (T = 1, x [B, C]).
+gdn_status validate_conv(const void* x, const float* w, const void* state, const void* out,
+                         int B, int C, int T, int K, int dtype) {
+    if (!x || !w || !state || !out) return GDN_ERR_NULL;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (B < 1 || C < 1 || T < 1 || K < 1) return GDN_ERR_SHAPE;
+    if (K > kMaxConvTaps) return GDN_ERR_UNSUPPORTED;
+    const int64_t tiles = ((int64_t)T + 2047) / 2048;
+    if ((int64_t)B * C * tiles > INT32_MAX) return GDN_ERR_SHAPE;
+    const void* ptrs[] = {x, w, state, out};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_ALIGN;
+    const uint64_t es = dtype == GDN_BF16 ? 2 : 4;
+    Range rx, rw, rs, ro;
+    if (!extent(x, {(uint64_t)B, (uint64_t)C, (uint64_t)T}, es, rx) ||
+        !extent(w, {(uint64_t)C, (uint64_t)K}, 4, rw) ||
+        !extent(state, {(uint64_t)B, (uint64_t)C, (uint64_t)K}, es, rs) ||
+        !extent(out, {(uint64_t)B, (uint64_t)C, (uint64_t)T}, es, ro))
+        return GDN_ERR_SHAPE;
+    if (overlaps(ro, rx) || overlaps(ro, rw) || overlaps(rs, rx) || overlaps(rs, rw) ||
+        overlaps(ro, rs))
+        return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,12 +202,33 @@ gdn_status gdn_decode_step_gated(const void* q, const void* k, const void* v,
     return decode_common(c, true, A_log, dt_bias, l2_eps, scale, stream);
 }
 
+gdn_status gdn_conv1d_prefill(const void* mixed, const float* conv_weight, void* out,
+                              void* conv_state_out, int B, int C, int T, int K, int dtype,
+                              gdn_stream stream) {
+    const gdn_status st = validate_conv(mixed, conv_weight, conv_state_out, out, B, C, T, K, dtype);
+    if (st != GDN_OK) return st;
+    (void)hipGetLastError();
+    const gdn::ConvArgs a{mixed, conv_weight, out, conv_state_out, B, C, T, K};
+    return gdn::launch_conv1d(a, dtype, false, (hipStream_t)stream) == hipSuccess ? GDN_OK
+                                                                                  : GDN_ERR_HIP;
+}
+
+gdn_status gdn_conv1d_decode(const void* x, const float* conv_weight, void* conv_state_inout,
+                             void* out, int B, int C, int K, int dtype, gdn_stream stream) {
+    const gdn_status st = validate_conv(x, conv_weight, conv_state_inout, out, B, C, 1, K, dtype);
+    if (st != GDN_OK) return st;
+    (void)hipGetLastError();
+    const gdn::ConvArgs a{x, conv_weight, out, conv_state_inout, B, C, 1, K};
+    return gdn::launch_conv1d(a, dtype, true, (hipStream_t)stream) == hipSuccess ? GDN_OK
+                                                                                 : GDN_ERR_HIP;
+}
+
 const char* gdn_status_string(int status) {
     switch (status) {
         case GDN_OK: return "ok";
         case GDN_ERR_NULL: return "a required pointer is NULL";
         case GDN_ERR_SHAPE: return "invalid shape (sizes < 1, Hv % Hk != 0, S % 64 != 0, or overflow)";
-        case GDN_ERR_UNSUPPORTED: return "unsupported head dimension (Dk, Dv must be multiples of 16 in [16, 128])";
+        case GDN_ERR_UNSUPPORTED: return "unsupported size (Dk, Dv must be multiples of 16 in [16, 128]; conv taps K <= 8)";
         case GDN_ERR_DTYPE: return "invalid dtype";
         case GDN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case GDN_ERR_ALIAS: return "out or state_inout overlaps another tensor argument";

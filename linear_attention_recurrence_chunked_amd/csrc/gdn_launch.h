@@ -29,8 +29,16 @@ struct DecodeArgs {
     const float* A_log; const float* dt_bias; float l2_eps;
 };
 
+// Depthwise conv1d: x [B, C, T] (decode: [B, C]), w [C, K] fp32, out like x,
+// state [B, C, K] (prefill: written; decode: in and out); 1 <= K <= 8.
+struct ConvArgs {
+    const void* x; const float* w; void* out; void* state;
+    int B, C, T, K;
+};
+
 // dtype: 0 = fp32 operands, 1 = bf16 operands (gdn_dtype).
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_conv1d(const ConvArgs& a, int dtype, bool decode, hipStream_t stream);
 
 }  // namespace gdn

@@ -18,7 +18,7 @@ OK, NULL, SHAPE, UNSUP, DTYPE, ALIGN, ALIAS, WS, HIP, VALUE = range(10)
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -33,6 +33,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"gdn_chunked_prefill", "gdn_decode_step",
                           "gdn_chunked_prefill_gated", "gdn_decode_step_gated",
+                          "gdn_conv1d_prefill", "gdn_conv1d_decode",
                           "gdn_chunked_prefill_workspace_bytes", "gdn_status_string",
                           "gdn_version"}
     for n in names:
@@ -191,3 +192,54 @@ def test_adjacent_buffers_are_not_aliases(lib):
 def test_size_overflow_is_a_shape_error(lib):
     huge = 1 << 30
     assert prefill(lib, B=huge, Hk=1, Hv=2, S=huge // 64 * 64) == SHAPE
+
+
+# ------------------------------------------------------------------ conv1d
+
+def conv_prefill(lib, x=None, w=None, out=None, st=None, B=2, C=16, T=100, K=4, dtype=1):
+    P = lambda v, i: fake(i) if v is None else v
+    return lib.gdn_conv1d_prefill(P(x, 0), P(w, 1), P(out, 2), P(st, 3), B, C, T, K, dtype, None)
+
+
+def conv_decode(lib, x=None, w=None, out=None, st=None, B=2, C=16, T=1, K=4, dtype=1):
+    P = lambda v, i: fake(i) if v is None else v
+    return lib.gdn_conv1d_decode(P(x, 0), P(w, 1), P(st, 3), P(out, 2), B, C, K, dtype, None)
+
+
+CONV = {"conv_prefill": conv_prefill, "conv_decode": conv_decode}
+
+
+@pytest.mark.parametrize("which", sorted(CONV))
+@pytest.mark.parametrize("arg", ["x", "w", "out", "st"])
+def test_conv_null(lib, which, arg):
+    assert CONV[which](lib, **{arg: 0}) == NULL
+
+
+@pytest.mark.parametrize("which", sorted(CONV))
+def test_conv_dtype_shape_taps(lib, which):
+    f = CONV[which]
+    assert f(lib, dtype=3) == DTYPE
+    for kw in (dict(B=0), dict(C=0), dict(K=0), dict(B=-2)):
+        assert f(lib, **kw) == SHAPE, kw
+    assert f(lib, K=9) == UNSUP
+    assert f(lib, K=8, dtype=5) == DTYPE        # K = 8 is accepted: the dtype fails
+
+
+def test_conv_prefill_tokens(lib):
+    assert conv_prefill(lib, T=0) == SHAPE
+    assert conv_prefill(lib, B=1 << 20, C=1 << 12, T=4096) == SHAPE   # grid overflow
+
+
+@pytest.mark.parametrize("which", sorted(CONV))
+@pytest.mark.parametrize("arg", ["x", "w", "out", "st"])
+def test_conv_misaligned(lib, which, arg):
+    idx = ["x", "w", "out", "st"].index(arg)
+    assert CONV[which](lib, **{arg: fake(idx, 8)}) == ALIGN
+
+
+@pytest.mark.parametrize("which", sorted(CONV))
+def test_conv_aliasing(lib, which):
+    f = CONV[which]
+    assert f(lib, out=fake(0, 16)) == ALIAS          # out over x
+    assert f(lib, st=fake(1, 0)) == ALIAS            # state over the weights
+    assert f(lib, out=fake(3, 0)) == ALIAS           # out over the state
