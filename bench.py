@@ -1,7 +1,8 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|prefill_gated|decode_gated|copy]
+                    [--only prefill|decode|prefill_gated|decode_gated|conv_prefill|
+                            conv_decode|copy]
 
 One step = one ``gdn_chunked_prefill`` call on the batched long prefill
 workload (B=4, Hk=16, Hv=32, Dk=Dv=128, S=8192, bf16 q/k/v, fp32 g/beta and
@@ -20,7 +21,10 @@ passes supply that load before the prefill's own warm-up. Prints ONE JSON line.
 
 The gated entry points (gate and L2-norm prologue on the device, raw q/k and
 gate pre-activations as inputs) are timed the same way on the same workloads
-and reported under "prefill_gated" and "decode_gated".
+and reported under "prefill_gated" and "decode_gated"; the depthwise conv1d
+that precedes them (prefill over the B=4, T=8192 mixed q|k|v tensor with
+C = 8192 channels and K = 4 taps; one decode token at B=256) under
+"conv1d_prefill" and "conv1d_decode".
 
 ``--only copy`` runs a plain device-to-device copy of ``--copy-mib`` MiB
 (used to calibrate the HBM byte counters of rocprofv3 against a kernel of
@@ -81,6 +85,10 @@ KERNEL_SOURCES = {
     "gdn_prefill_kernel": "linear_attention_recurrence_chunked_amd/csrc/gdn_prefill.hip",
     "gdn_decode_kernel": "linear_attention_recurrence_chunked_amd/csrc/gdn_decode.hip",
 }
+KERNEL_SOURCES["gdn_prefill_kernel_gated"] = KERNEL_SOURCES["gdn_prefill_kernel"]
+KERNEL_SOURCES["gdn_decode_kernel_gated"] = KERNEL_SOURCES["gdn_decode_kernel"]
+KERNEL_SOURCES["gdn_conv1d_prefill_kernel"] = "linear_attention_recurrence_chunked_amd/csrc/gdn_conv1d.hip"
+KERNEL_SOURCES["gdn_conv1d_decode_kernel"] = KERNEL_SOURCES["gdn_conv1d_prefill_kernel"]
 
 
 def source_digest(kernel):
@@ -202,6 +210,51 @@ def bench_decode(torch, gdn, w, state0, steps, reps, warmup, gated=False):
     return ms_step, kern_ms, decode_algorithmic(w.B, w.Hk, w.Hv, w.Dk, w.Dv)
 
 
+def conv_algorithmic(B, C, T, K, esize=2):
+    """HBM bytes of one conv1d call: x read, out written ([B,C,T] each), the
+    window state written (prefill) or read and written (decode, T = 1), and
+    the fp32 weights [C,K]."""
+    state = B * C * K * esize * (2 if T == 1 else 1)
+    return float(2 * B * C * T * esize + state + C * K * 4)
+
+
+def bench_conv(torch, gdn, inputs, name, steps, warmup):
+    """Times the conv1d workload ``name`` (prefill: one call per step;
+    decode: one token per step, window state carried)."""
+    w = inputs.CONV_WORKLOADS[name]
+    decode = w.T == 1
+    d = inputs.draw_conv(w.B, w.C, w.T, w.K, dtype=w.dtype, decode=decode)
+    dev = torch.device("cuda", 0)
+    x = torch.from_numpy(d["x"]).to(dev).to(torch.bfloat16)
+    wt = torch.from_numpy(d["w"]).to(dev)
+    out = torch.empty_like(x)
+    if decode:
+        st = torch.from_numpy(d["state"]).to(dev).to(torch.bfloat16)
+    else:
+        st = torch.empty((w.B, w.C, w.K), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        if decode:
+            gdn.conv1d_decode(x, st, wt, out=out, stream=stream)
+        else:
+            gdn.conv1d_prefill(x, wt, out=out, state=st, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    ev = _events(torch, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return w, (t1 - t0) * 1e3 / steps, kern_ms, conv_algorithmic(w.B, w.C, w.T, w.K)
+
+
 def bench_copy(torch, mib, steps):
     """Streaming elementwise kernel over ``mib`` MiB of fp32: b = -a reads and
     writes that many bytes once (a same-dtype copy_ would be a DMA transfer,
@@ -246,6 +299,27 @@ def cpu_baseline_decode(w, steps, state0):
             "sample": "all %d decode steps at B=%d, state carried, fp64, %.2f s" % (len(steps), w.B, dt)}
 
 
+def cpu_baseline_conv(inputs, cw, decode):
+    """The conv1d oracle (numpy fp64): prefill on one batch row of the
+    workload (all C channels, all T tokens), decode on one whole step."""
+    from oracle import conv1d
+    d = inputs.draw_conv(1 if not decode else cw.B, cw.C, cw.T, cw.K, dtype=cw.dtype,
+                         decode=decode)
+    t0 = time.perf_counter()
+    if decode:
+        conv1d.conv1d_decode(d["x"], d["state"], d["w"])
+    else:
+        conv1d.conv1d_prefill(d["x"], d["w"])
+    dt = time.perf_counter() - t0
+    if decode:
+        return {"value": 1.0 / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
+                "sample": "one decode step at B=%d, C=%d, K=%d, numpy fp64, %.3f s"
+                          % (cw.B, cw.C, cw.K, dt)}
+    return {"value": cw.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "one of the %d batch rows (C=%d channels x T=%d tokens, K=%d), numpy fp64, "
+                      "%.2f s" % (cw.B, cw.C, cw.T, cw.K, dt)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,7 +327,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "prefill_gated", "decode_gated",
-                                       "copy"], default=None)
+                                       "conv_prefill", "conv_decode", "copy"], default=None)
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -283,6 +357,13 @@ def main():
         print(json.dumps({args.only + "_ms_per_step": dms, "kernel_ms": dkern_ms,
                           "GB_s": dbytes / (dkern_ms / 1e3) / 1e9}), flush=True)
         return
+    if args.only in ("conv_prefill", "conv_decode"):
+        name = {"conv_prefill": "conv_prefill_b4_t8192", "conv_decode": "conv_decode_b256"}
+        cw, cms, ckern_ms, cbytes = bench_conv(torch, gdn, inputs, name[args.only], args.steps,
+                                               args.warmup)
+        print(json.dumps({args.only + "_ms_per_step": cms, "kernel_ms": ckern_ms,
+                          "GB_s": cbytes / (ckern_ms / 1e3) / 1e9}), flush=True)
+        return
     if args.only in ("prefill", "prefill_gated"):
         d = inputs.draw_workload(w, raw=True)
         ms_step, kern_ms, _, _ = bench_prefill(torch, gdn, w, d, args.steps, args.warmup,
@@ -300,6 +381,10 @@ def main():
     ms_step, kern_ms, nbytes, flops = bench_prefill(torch, gdn, w, d, args.steps, args.warmup)
     gms_step, gkern_ms, _, _ = bench_prefill(torch, gdn, w, d, args.steps, args.warmup,
                                              gated=True)
+    cpw, cpms, cpkern, cpbytes = bench_conv(torch, gdn, inputs, "conv_prefill_b4_t8192",
+                                            args.steps, args.warmup)
+    cdw, cdms, cdkern, cdbytes = bench_conv(torch, gdn, inputs, "conv_decode_b256",
+                                            10 * args.steps, args.warmup)
     tokens = w.B * w.S
     hbm = lambda b, ms: {"achieved": b / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "kernel_ms": ms,
@@ -336,18 +421,33 @@ def main():
                           "value": tokens / (gms_step / 1e3), "unit": "tokens/s",
                           "ms_per_step": gms_step, "l2_eps": L2_EPS,
                           "roofline": dict(bound="hbm", kernel="gdn_prefill_kernel (gated)",
+                                           traffic=measured_traffic("gdn_prefill_kernel_gated"),
                                            **hbm(nbytes, gkern_ms))},
         "decode_gated": {"workload": "decode_b256 (raw q/k, a, b, A_log, dt_bias)",
                          "value": 1e3 / gdms, "unit": "steps/s", "ms_per_step": gdms,
                          "l2_eps": L2_EPS,
                          "roofline": dict(bound="hbm", kernel="gdn_decode_kernel (gated)",
+                                          traffic=measured_traffic("gdn_decode_kernel_gated"),
                                           **hbm(dbytes, gdkern_ms))},
+        "conv1d_prefill": {"workload": cpw.name, "B": cpw.B, "C": cpw.C, "T": cpw.T,
+                           "K": cpw.K, "value": cpw.B * cpw.T / (cpms / 1e3),
+                           "unit": "tokens/s", "ms_per_step": cpms,
+                           "roofline": dict(bound="hbm", kernel="gdn_conv1d_prefill_kernel",
+                                            traffic=measured_traffic("gdn_conv1d_prefill_kernel"),
+                                            **hbm(cpbytes, cpkern))},
+        "conv1d_decode": {"workload": cdw.name, "B": cdw.B, "C": cdw.C, "K": cdw.K,
+                          "value": 1e3 / cdms, "unit": "steps/s", "ms_per_step": cdms,
+                          "roofline": dict(bound="hbm", kernel="gdn_conv1d_decode_kernel",
+                                           traffic=measured_traffic("gdn_conv1d_decode_kernel"),
+                                           **hbm(cdbytes, cdkern))},
         "host": {"cpu": platform.processor() or platform.machine(),
                  "gpu": torch.cuda.get_device_name(0)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(w, d)
         res["decode"]["cpu_baseline"] = cpu_baseline_decode(dw, dsteps, dstate0)
+        res["conv1d_prefill"]["cpu_baseline"] = cpu_baseline_conv(inputs, cpw, False)
+        res["conv1d_decode"]["cpu_baseline"] = cpu_baseline_conv(inputs, cdw, True)
     print(json.dumps(res), flush=True)
 
 

@@ -130,7 +130,7 @@ gdn_status validate_conv(const void* x, const float* w, const void* state, const
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
     if (B < 1 || C < 1 || T < 1 || K < 1) return GDN_ERR_SHAPE;
     if (K > kMaxConvTaps) return GDN_ERR_UNSUPPORTED;
-    const int64_t tiles = ((int64_t)T + 2047) / 2048;
+    const int64_t tiles = ((int64_t)T + 2047) / 2048;  // at least the kernel's tile count
     if ((int64_t)B * C * tiles > INT32_MAX) return GDN_ERR_SHAPE;
     const void* ptrs[] = {x, w, state, out};
     for (const void* p : ptrs)

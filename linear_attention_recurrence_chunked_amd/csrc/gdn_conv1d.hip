@@ -11,22 +11,29 @@
 //            state <- window (in place)
 //
 // Both are streams over HBM with a handful of flops per byte. Prefill: one
-// workgroup of 256 threads covers 2048 consecutive tokens of one channel row
-// ([B, C, T] rows are contiguous in T); each thread owns 8 consecutive
-// tokens, read and written as 16-byte vectors (two on the fp32 path). The
+// workgroup of 256 threads covers 8192 consecutive tokens of one channel row
+// ([B, C, T] rows are contiguous in T) as four groups of 2048; in each group
+// a thread owns 8 consecutive tokens, read and written as one 16-byte vector
+// (two on the fp32 path), so a wave's load covers 1 KiB contiguously; all
+// four loads are issued before any use (64 bytes per thread in flight). The
 // K-1 tokens of history a thread needs are the last ones of the previous
 // lane's 8, passed by a lane shuffle; lane 0 of each wave reads them from
-// memory (they belong to the previous wave's range and are cache hits, except
-// at the first wave of a workgroup). The taps are a template parameter so the
-// filter window stays in registers.
+// memory (the previous wave's range: cache hits, except at the first wave of
+// a group). The taps are a template parameter so the filter window stays in
+// registers. Measured on MI355X at B=4, C=8192, T=8192, bf16: 5.4 TB/s,
+// against 5.0 TB/s with each thread's 16 or 32 tokens contiguous, and
+// non-temporal stores were slower still.
+// Decode: one thread per (batch, channel); the window row is read and written
+// as one vector where its size allows.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
 constexpr int kConvThreads = 256;
-constexpr int kConvNE = 8;                         // tokens per thread
-constexpr int kConvTile = kConvThreads * kConvNE;  // tokens per workgroup
+constexpr int kConvNE = 8;                         // tokens per vector
+constexpr int kConvNV = 4;                         // vectors per thread
+constexpr int kConvTile = kConvThreads * kConvNE * kConvNV;  // tokens per workgroup
 
 __device__ __forceinline__ float silu_f(float y) {
     return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
@@ -71,8 +78,8 @@ __device__ __forceinline__ void store8(E* p, int n, const float (&v)[kConvNE]) {
     }
 }
 
-// ALIGNED: T % 8 == 0 (every thread's 8 tokens are in range or all out of it,
-// and rows start 16-byte aligned).
+// ALIGNED: T % 8 == 0 (every 8-token vector is wholly in range or wholly out
+// of it, and rows start 16-byte aligned).
 template <typename E, int K, bool ALIGNED>
 __global__ __launch_bounds__(kConvThreads) void gdn_conv1d_prefill_kernel(
     const E* __restrict__ x, const float* __restrict__ w, E* __restrict__ out,
@@ -86,57 +93,94 @@ __global__ __launch_bounds__(kConvThreads) void gdn_conv1d_prefill_kernel(
     float wk[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) wk[j] = w[(size_t)c * K + j];
-
     const E* xr = x + (size_t)row * T;
-    const int t0 = tile * kConvTile + kConvNE * (int)threadIdx.x;
-    const int n = min(kConvNE, T - t0);                 // tokens of this thread in range
-    float cur[kConvNE];
-    if (n > 0) load8<E, ALIGNED>(xr + t0, n, cur);
-    else {
+    // vector group v holds tokens tile * kConvTile + 8 (256 v + tid) .. +7: the
+    // 64 lanes of a wave cover 1 KiB (bf16) contiguously per load instruction.
+    // All groups are loaded before any is used.
+    float cur[kConvNV][kConvNE];
 #pragma unroll
-        for (int e = 0; e < kConvNE; ++e) cur[e] = 0.f;
-    }
-    // history: the previous 8 tokens (only the last K-1 are used)
-    float prev[kConvNE];
-#pragma unroll
-    for (int e = 0; e < kConvNE; ++e) prev[e] = __shfl_up(cur[e], 1);
-    if (lane == 0) {
-        if (t0 >= kConvNE) load8<E, ALIGNED>(xr + t0 - kConvNE, kConvNE, prev);
+    for (int v = 0; v < kConvNV; ++v) {
+        const int tv = tile * kConvTile + kConvNE * (kConvThreads * v + (int)threadIdx.x);
+        const int n = min(kConvNE, T - tv);
+        if (n > 0) load8<E, ALIGNED>(xr + tv, n, cur[v]);
         else {
 #pragma unroll
-            for (int e = 0; e < kConvNE; ++e) prev[e] = 0.f;
+            for (int e = 0; e < kConvNE; ++e) cur[v][e] = 0.f;
         }
     }
-    if (n <= 0) return;
-
-    float o[kConvNE];
 #pragma unroll
-    for (int e = 0; e < kConvNE; ++e) {
-        float y = 0.f;
+    for (int v = 0; v < kConvNV; ++v) {
+        const int tv = tile * kConvTile + kConvNE * (kConvThreads * v + (int)threadIdx.x);
+        float prev[kConvNE];
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            const int i = e - (K - 1) + j;              // token t0 + i
-            y += wk[j] * (i < 0 ? prev[kConvNE + i] : cur[i]);
-        }
-        o[e] = silu_f(y);
-    }
-    store8<E, ALIGNED>(out + (size_t)row * T + t0, n, o);
-
-    // state: the thread holding token T-1 writes the last K raw tokens
-    if (t0 <= T - 1 && T - 1 < t0 + kConvNE) {
-        E* st = state + (size_t)row * K;
+        for (int e = 0; e < kConvNE; ++e) prev[e] = __shfl_up(cur[v][e], 1);
+        if (lane == 0) {
+            if (tv >= kConvNE) load8<E, ALIGNED>(xr + tv - kConvNE, kConvNE, prev);
+            else {
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            const int i = T - K + j - t0;               // in [-8, 8)
-            const int t = T - K + j;
-            float vj = 0.f;
-#pragma unroll
-            for (int e = 0; e < kConvNE; ++e) {
-                if (i == e) vj = cur[e];
-                if (i == e - kConvNE) vj = prev[e];
+                for (int e = 0; e < kConvNE; ++e) prev[e] = 0.f;
             }
-            st[j] = from_f32<E>(t >= 0 ? vj : 0.f);
         }
+        const int n = min(kConvNE, T - tv);
+        if (n <= 0) continue;                           // (after the shuffle: all lanes take part)
+        float o[kConvNE];
+#pragma unroll
+        for (int e = 0; e < kConvNE; ++e) {
+            float y = 0.f;
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const int i = e - (K - 1) + j;
+                y += wk[j] * (i < 0 ? prev[kConvNE + i] : cur[v][i]);
+            }
+            o[e] = silu_f(y);
+        }
+        store8<E, ALIGNED>(out + (size_t)row * T + tv, n, o);
+        if (tv <= T - 1 && T - 1 < tv + kConvNE) {
+            E* st = state + (size_t)row * K;
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const int i = T - K + j - tv;
+                float vj = 0.f;
+#pragma unroll
+                for (int e = 0; e < kConvNE; ++e) {
+                    if (i == e) vj = cur[v][e];
+                    if (i == e - kConvNE) vj = prev[e];
+                }
+                st[j] = from_f32<E>(T - K + j >= 0 ? vj : 0.f);
+            }
+        }
+    }
+}
+
+// The window row of K elements of E as one vector load/store when it is 4, 8
+// or 16 bytes (rows are then naturally aligned), else element by element.
+template <typename E, int K>
+__device__ __forceinline__ void load_row(const E* p, float (&v)[K]) {
+    constexpr int NB = K * (int)sizeof(E);
+    if constexpr (NB == 4 || NB == 8 || NB == 16) {
+        typedef uint32_t W __attribute__((ext_vector_type(NB / 4)));
+        union { W w; E e[K]; } u;
+        u.w = *(const W*)p;
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = to_f32(u.e[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = to_f32(p[j]);
+    }
+}
+
+template <typename E, int K>
+__device__ __forceinline__ void store_row(E* p, const float (&v)[K]) {
+    constexpr int NB = K * (int)sizeof(E);
+    if constexpr (NB == 4 || NB == 8 || NB == 16) {
+        typedef uint32_t W __attribute__((ext_vector_type(NB / 4)));
+        union { W w; E e[K]; } u;
+#pragma unroll
+        for (int j = 0; j < K; ++j) u.e[j] = from_f32<E>(v[j]);
+        *(W*)p = u.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) p[j] = from_f32<E>(v[j]);
     }
 }
 
@@ -149,16 +193,16 @@ __global__ __launch_bounds__(kConvThreads) void gdn_conv1d_decode_kernel(
     if (i >= total) return;
     const int c = (int)(i % C);
     E* st = state + i * K;
-    float win[K];
+    float old[K], win[K];
+    load_row<E, K>(st, old);
 #pragma unroll
-    for (int j = 0; j + 1 < K; ++j) win[j] = to_f32(st[j + 1]);
+    for (int j = 0; j + 1 < K; ++j) win[j] = old[j + 1];
     win[K - 1] = to_f32(x[i]);
     float y = 0.f;
 #pragma unroll
     for (int j = 0; j < K; ++j) y += w[(size_t)c * K + j] * win[j];
     out[i] = from_f32<E>(silu_f(y));
-#pragma unroll
-    for (int j = 0; j < K; ++j) st[j] = from_f32<E>(win[j]);   // exact: values are E
+    store_row<E, K>(st, win);                          // exact: the values are E
 }
 
 // ---------------------------------------------------------------- launch
