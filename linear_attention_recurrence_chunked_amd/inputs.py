@@ -40,13 +40,21 @@ initialisation of a depthwise convolution with K taps), and for decode a
 window state ``[B, C, K]`` ~ N(0, 1) and one token ``[B, C]`` per step. The
 mixed tensor of the prefill workloads has C = 2 Hk Dk + Hv Dv channels (q|k|v,
 "GDN Block TKG Kernel API Reference", Dimensions) and T = S tokens.
+
+Decode-block inputs (:func:`draw_block`), from ``rng([200, B, Hk, Hv, Dk, Dv,
+K, step])``: the raw mixed token ``[B, C]`` and the gate ``z [B, Hv Dv]`` ~
+N(0, 1), ``a, b [B, Hv]`` ~ N(0, 1) (float32), the conv window ``[B, C, K]``
+~ N(0, 1), conv weights as above, ``norm_weight [Dv]`` ~ 1 + N(0, 0.1^2), the
+recurrent state ~ N(0, 0.02^2); ``A_log``, ``dt_bias`` as in step 1 (standard
+decay) from ``rng([200, Hv])``. Operand tensors (mixed, z, window) are
+bf16-exact for bf16.
 """
 from dataclasses import dataclass, field
 
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "bf16_round", "draw_prefill", "draw_workload",
-           "draw_decode_steps", "ConvWorkload", "CONV_WORKLOADS", "draw_conv"]
+           "draw_decode_steps", "ConvWorkload", "CONV_WORKLOADS", "draw_conv", "draw_block"]
 
 _DECAY = {"std": (1.0, 16.0), "strong": (8.0, 64.0), "weak": (0.01, 0.1)}
 _VARIANT_ID = {"std": 0, "strong": 1, "weak": 2}
@@ -207,3 +215,28 @@ def draw_conv(B, C, T, K, dtype="bf16", step=0, decode=False):
     if dtype == "bf16":
         x = bf16_round(x)
     return {"x": x, "w": w}
+
+
+def draw_block(B, Hk, Hv, Dk, Dv, K=4, dtype="bf16", step=0, with_state=True):
+    """Inputs of one decode-block token (see the module docstring). Returns a
+    dict of float32 arrays: mixed, z, a, b, conv_state, conv_weight, A_log,
+    dt_bias, norm_weight, state (step > 0 with ``with_state=False`` omits the
+    window, the weights and the states, which carry over between steps)."""
+    C = 2 * Hk * Dk + Hv * Dv
+    rng = np.random.default_rng([200, B, Hk, Hv, Dk, Dv, K, step])
+    d = {"mixed": rng.standard_normal((B, C), dtype=np.float32),
+         "z": rng.standard_normal((B, Hv * Dv), dtype=np.float32),
+         "a": rng.standard_normal((B, Hv), dtype=np.float32),
+         "b": rng.standard_normal((B, Hv), dtype=np.float32)}
+    if with_state:
+        d["conv_state"] = rng.standard_normal((B, C, K), dtype=np.float32)
+        d["conv_weight"] = (rng.uniform(-1.0, 1.0, (C, K)) / np.sqrt(K)).astype(np.float32)
+        d["norm_weight"] = (1.0 + 0.1 * rng.standard_normal(Dv)).astype(np.float32)
+        d["state"] = (0.02 * rng.standard_normal((B, Hv, Dk, Dv))).astype(np.float32)
+        A_log, dt_bias = _head_params("std", Hv, (200, Hv))
+        d["A_log"], d["dt_bias"] = A_log.astype(np.float32), dt_bias.astype(np.float32)
+    if dtype == "bf16":
+        for key in ("mixed", "z", "conv_state"):
+            if key in d:
+                d[key] = bf16_round(d[key])
+    return d

@@ -23,7 +23,8 @@ import numpy as np
 
 from . import build as _build
 
-__all__ = ["gdn_serial", "gdn_serial_gated", "gdn_gates", "l2_normalize", "default_threads"]
+__all__ = ["gdn_serial", "gdn_serial_gated", "gdn_serial_gated_f64", "gdn_gates", "l2_normalize",
+           "default_threads"]
 
 _LIB = None
 
@@ -48,6 +49,8 @@ def _lib():
             ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
             ctypes.c_long, ctypes.c_int]
+        lib.oracle_gdn_serial_gated_f64.restype = ctypes.c_int
+        lib.oracle_gdn_serial_gated_f64.argtypes = lib.oracle_gdn_serial_gated.argtypes
         lib.oracle_gdn_gates.restype = ctypes.c_int
         lib.oracle_gdn_gates.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_long] * 3
         lib.oracle_l2norm.restype = ctypes.c_int
@@ -113,7 +116,7 @@ def gdn_serial(q, k, v, g_log, beta, scale, state=None, nthreads=None, inplace=F
 
 
 def gdn_serial_gated(q, k, v, a, b, A_log, dt_bias, scale, eps, state=None, nthreads=None,
-                     inplace=False):
+                     inplace=False, _f64=False):
     """Token-serial fp64 gated delta rule from the raw prologue inputs.
 
     Shapes: q, k [B,Hk,S,Dk] (not normalised); v [B,Hv,S,Dv]; a, b [B,Hv,S];
@@ -122,7 +125,8 @@ def gdn_serial_gated(q, k, v, a, b, A_log, dt_bias, scale, eps, state=None, nthr
     q and k divided by sqrt(sum of squares + eps), all in fp64; then the
     recurrence of :func:`gdn_serial`. Returns (out, final state), float64.
     """
-    q, k, v, a, b, A_log, dt_bias = (_f32(x) for x in (q, k, v, a, b, A_log, dt_bias))
+    conv = (lambda x: np.ascontiguousarray(np.asarray(x, dtype=np.float64))) if _f64 else _f32
+    q, k, v, a, b, A_log, dt_bias = (conv(x) for x in (q, k, v, a, b, A_log, dt_bias))
     B, Hk, S, Dk = q.shape
     Bv, Hv, Sv, Dv = v.shape
     if k.shape != q.shape or (Bv, Sv) != (B, S) or a.shape != (B, Hv, S) \
@@ -133,13 +137,22 @@ def gdn_serial_gated(q, k, v, a, b, A_log, dt_bias, scale, eps, state=None, nthr
     st = _state_arg(state, (B, Hv, Dk, Dv), inplace)
     out = np.empty((B, Hv, S, Dv), dtype=np.float64)
     n = default_threads() if nthreads is None else int(nthreads)
-    rc = _lib().oracle_gdn_serial_gated(
+    fn = _lib().oracle_gdn_serial_gated_f64 if _f64 else _lib().oracle_gdn_serial_gated
+    rc = fn(
         q.ctypes.data, k.ctypes.data, v.ctypes.data, a.ctypes.data, b.ctypes.data,
         A_log.ctypes.data, dt_bias.ctypes.data, float(eps), float(scale),
         st.ctypes.data, out.ctypes.data, B, Hk, Hv, S, Dk, Dv, n)
     if rc != 0:
         raise RuntimeError("oracle_gdn_serial_gated failed with code %d" % rc)
     return out, st
+
+
+def gdn_serial_gated_f64(q, k, v, a, b, A_log, dt_bias, scale, eps, state=None,
+                         nthreads=None, inplace=False):
+    """:func:`gdn_serial_gated` with every input taken in float64 (for inputs
+    that are themselves fp64 results, such as the conv1d output)."""
+    return gdn_serial_gated(q, k, v, a, b, A_log, dt_bias, scale, eps, state, nthreads,
+                            inplace, _f64=True)
 
 
 def gdn_gates(a, b, A_log, dt_bias):

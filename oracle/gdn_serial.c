@@ -72,13 +72,19 @@ static double sigmoid(double x)
     return 1.0 / (1.0 + exp(-x));
 }
 
-/* y = x / sqrt(sum x^2 + eps) over one vector of length D */
-static void l2norm_row(const float* x, double eps, double* y, long D)
+/* element i of an input array of float (f64 == 0) or double (f64 == 1) */
+static double in_at(const void* p, long i, int f64)
+{
+    return f64 ? ((const double*)p)[i] : (double)((const float*)p)[i];
+}
+
+/* y = x / sqrt(sum x^2 + eps) over the vector x[off .. off+D-1] */
+static void l2norm_row(const void* x, long off, int f64, double eps, double* y, long D)
 {
     double ss = 0.0;
-    for (long i = 0; i < D; ++i) ss += (double)x[i] * (double)x[i];
+    for (long i = 0; i < D; ++i) ss += in_at(x, off + i, f64) * in_at(x, off + i, f64);
     const double r = 1.0 / sqrt(ss + eps);
-    for (long i = 0; i < D; ++i) y[i] = (double)x[i] * r;
+    for (long i = 0; i < D; ++i) y[i] = in_at(x, off + i, f64) * r;
 }
 
 /* g_log and beta of token t of value head h */
@@ -123,13 +129,14 @@ static void gdn_token(double* St, const double* kt, const double* qt, const doub
 }
 
 /*
- * Both entries share this driver. Without gates (A_log == NULL) g_log and
+ * Every entry shares this driver. Without gates (A_log == NULL) g_log and
  * beta are the per-token decay and write strength and q, k are used as given;
  * with gates, gl/bt hold the raw a and b and q, k are normalised with eps.
+ * All array inputs are float (f64 == 0) or all double (f64 == 1).
  */
-static int serial(const float* q, const float* k, const float* v,
-                  const float* gl, const float* bt, const float* A_log, const float* dt_bias,
-                  double eps, double scale, double* state, double* out,
+static int serial(const void* q, const void* k, const void* v,
+                  const void* gl, const void* bt, const void* A_log, const void* dt_bias,
+                  int f64, double eps, double scale, double* state, double* out,
                   long B, long Hk, long Hv, long S, long Dk, long Dv, int nthreads)
 {
     if (B < 0 || Hk <= 0 || Hv <= 0 || S < 0 || Dk <= 0 || Dv <= 0) return 1;
@@ -155,24 +162,24 @@ static int serial(const float* q, const float* k, const float* v,
         double* vd = buf + 2 * Dk;
         double* u = buf + 2 * Dk + Dv;
         for (long t = 0; t < S; ++t) {
-            const float* kt = k + ((b * Hk + j) * S + t) * Dk;
-            const float* qt = q + ((b * Hk + j) * S + t) * Dk;
-            const float* vt = v + ((b * Hv + h) * S + t) * Dv;
+            const long kt = ((b * Hk + j) * S + t) * Dk;   /* offsets of k_t, q_t, v_t */
+            const long qt = kt;
+            const long vt = ((b * Hv + h) * S + t) * Dv;
             double g, be;
             if (A_log) {
-                gates((double)gl[bh * S + t], (double)bt[bh * S + t], (double)A_log[h],
-                      (double)dt_bias[h], &g, &be);
-                l2norm_row(kt, eps, kd, Dk);
-                l2norm_row(qt, eps, qd, Dk);
+                gates(in_at(gl, bh * S + t, f64), in_at(bt, bh * S + t, f64),
+                      in_at(A_log, h, f64), in_at(dt_bias, h, f64), &g, &be);
+                l2norm_row(k, kt, f64, eps, kd, Dk);
+                l2norm_row(q, qt, f64, eps, qd, Dk);
             } else {
-                g = (double)gl[bh * S + t];
-                be = (double)bt[bh * S + t];
+                g = in_at(gl, bh * S + t, f64);
+                be = in_at(bt, bh * S + t, f64);
                 for (long i = 0; i < Dk; ++i) {
-                    kd[i] = (double)kt[i];
-                    qd[i] = (double)qt[i];
+                    kd[i] = in_at(k, kt + i, f64);
+                    qd[i] = in_at(q, qt + i, f64);
                 }
             }
-            for (long c = 0; c < Dv; ++c) vd[c] = (double)vt[c];
+            for (long c = 0; c < Dv; ++c) vd[c] = in_at(v, vt + c, f64);
             gdn_token(St, kd, qd, vd, exp(g), be, scale, u, out + (bh * S + t) * Dv, Dk, Dv);
         }
         free(buf);
@@ -186,7 +193,7 @@ int oracle_gdn_serial(const float* q, const float* k, const float* v,
                       long B, long Hk, long Hv, long S, long Dk, long Dv,
                       int nthreads)
 {
-    return serial(q, k, v, g_log, beta, NULL, NULL, 0.0, scale, state, out,
+    return serial(q, k, v, g_log, beta, NULL, NULL, 0, 0.0, scale, state, out,
                   B, Hk, Hv, S, Dk, Dv, nthreads);
 }
 
@@ -198,7 +205,21 @@ int oracle_gdn_serial_gated(const float* q, const float* k, const float* v,
                             int nthreads)
 {
     if (!A_log || !dt_bias) return 1;
-    return serial(q, k, v, a, b, A_log, dt_bias, eps, scale, state, out,
+    return serial(q, k, v, a, b, A_log, dt_bias, 0, eps, scale, state, out,
+                  B, Hk, Hv, S, Dk, Dv, nthreads);
+}
+
+/* The same with every array input in double (for inputs that are themselves
+ * results of other fp64 steps). */
+int oracle_gdn_serial_gated_f64(const double* q, const double* k, const double* v,
+                                const double* a, const double* b,
+                                const double* A_log, const double* dt_bias,
+                                double eps, double scale, double* state, double* out,
+                                long B, long Hk, long Hv, long S, long Dk, long Dv,
+                                int nthreads)
+{
+    if (!A_log || !dt_bias) return 1;
+    return serial(q, k, v, a, b, A_log, dt_bias, 1, eps, scale, state, out,
                   B, Hk, Hv, S, Dk, Dv, nthreads);
 }
 
@@ -220,6 +241,6 @@ int oracle_gdn_gates(const float* a, const float* b, const float* A_log, const f
 int oracle_l2norm(const float* x, double eps, double* y, long rows, long D)
 {
     if (rows < 0 || D <= 0) return 1;
-    for (long r = 0; r < rows; ++r) l2norm_row(x + r * D, eps, y + r * D, D);
+    for (long r = 0; r < rows; ++r) l2norm_row(x, r * D, 0, eps, y + r * D, D);
     return 0;
 }

@@ -428,10 +428,24 @@ def gpin_gated_heads_independent(o):
         _close(st[:, sl], sh, 1e-14, "heads state")
 
 
+def gpin_gated_f64_inputs(o):
+    """The fp64-input entry gives exactly the float entry's result on inputs
+    that float32 represents exactly, and differs on inputs it does not."""
+    q, k, v, a, b, A_log, dt_bias, s0 = raw_case(37, B=1, Hk=1, Hv=2, S=6, Dk=4, Dv=3)
+    o1, s1 = o.gated(q, k, v, a, b, A_log, dt_bias, 0.7, 1e-6, s0)
+    f = lambda x: x.astype(np.float64)
+    o2, s2 = o.gated_f64(f(q), f(k), f(v), f(a), f(b), f(A_log), f(dt_bias), 0.7, 1e-6, s0)
+    _close(o2, o1, 0.0, "f64 entry out")
+    _close(s2, s1, 0.0, "f64 entry state")
+    v3 = f(v) + 1e-9                                  # not representable in float32
+    o3, _ = o.gated_f64(f(q), f(k), v3, f(a), f(b), f(A_log), f(dt_bias), 0.7, 1e-6, s0)
+    assert np.max(np.abs(o3 - o1)) > 0.0, "f64 entry must read double inputs"
+
+
 GATED_PINS = [
     gpin_gates_match_library, gpin_l2norm_closed_forms, gpin_gated_golden,
     gpin_gated_pure_decay, gpin_gated_equals_normalised_serial, gpin_gated_norm_invariance,
-    gpin_gated_heads_independent,
+    gpin_gated_heads_independent, gpin_gated_f64_inputs,
 ]
 
 
@@ -547,3 +561,126 @@ CONV_PINS = [
     cpin_state_is_last_raw_tokens, cpin_decode_continues_prefill, cpin_decode_window_shift,
     cpin_channels_independent,
 ]
+
+
+# ------------------------------------------- RMSNormGated and the decode block
+#
+# RMSNormGated ("GDN Block TKG Kernel API Reference": introduction, norm_weight
+# gamma over head_v_dim, gated by the z projection), read as
+#     y = o / sqrt(mean(o^2) + eps) * gamma * silu(z)   over each head's Dv.
+# ``rpin_*`` take a namespace with o.rmsnorm(o, z, w, eps) and
+# o.block(...) (oracle.block.decode_block's signature).
+
+def rpin_rmsnorm_matches_torch(o):
+    """Against torch.nn.functional.rms_norm and silu in float64."""
+    import torch
+    import torch.nn.functional as F
+    r = _rng(60)
+    x = r.standard_normal((3, 4, 16)) * 2.0
+    z = r.standard_normal((3, 4, 16)) * 3.0
+    w = r.uniform(0.5, 1.5, 16)
+    for eps in (0.0, 1e-6, 0.3):
+        y = o.rmsnorm(x, z, w, eps)
+        t = F.rms_norm(torch.from_numpy(x), (16,), weight=torch.from_numpy(w), eps=eps) \
+            * F.silu(torch.from_numpy(z))
+        _close(y, t.numpy(), 1e-13, "rmsnorm vs torch eps=%g" % eps)
+
+
+def rpin_rmsnorm_closed_forms(o):
+    """A constant row c gives c / sqrt(c^2 + eps); z = 0 gives 0; with eps = 0
+    scaling o changes nothing."""
+    D = 8
+    y = o.rmsnorm(np.full((1, D), 3.0), np.full((1, D), 50.0), np.ones(D), 16.0)
+    _close(y, np.full((1, D), 3.0 / 5.0 * 50.0), 1e-13, "constant row")   # silu(50) = 50
+    y0 = o.rmsnorm(_rng(61).standard_normal((2, D)), np.zeros((2, D)), np.ones(D), 1e-6)
+    assert np.all(y0 == 0.0), "silu(0) = 0 gates everything off"
+    x = _rng(62).standard_normal((2, 3, D))
+    z = _rng(63).standard_normal((2, 3, D))
+    w = _rng(64).uniform(0.5, 2.0, D)
+    _close(o.rmsnorm(7.5 * x, z, w, 0.0), o.rmsnorm(x, z, w, 0.0), 1e-14, "scale invariance")
+
+
+def block_case(seed, B=2, Hk=2, Hv=4, Dk=4, Dv=3, K=4):
+    r = _rng(seed)
+    C = 2 * Hk * Dk + Hv * Dv
+    return dict(
+        mixed=r.standard_normal((B, C)).astype(np.float32),
+        z=r.standard_normal((B, Hv * Dv)).astype(np.float32),
+        a=r.standard_normal((B, Hv)).astype(np.float32),
+        b=r.standard_normal((B, Hv)).astype(np.float32),
+        conv_state=r.standard_normal((B, C, K)).astype(np.float32),
+        conv_weight=(r.uniform(-1, 1, (C, K)) / np.sqrt(K)).astype(np.float32),
+        A_log=r.uniform(0.0, np.log(16.0), Hv).astype(np.float32),
+        dt_bias=r.uniform(-1, 1, Hv).astype(np.float32),
+        norm_weight=r.uniform(0.5, 1.5, Dv).astype(np.float32),
+        state=(0.5 * r.standard_normal((B, Hv, Dk, Dv))).astype(np.float32),
+        scale=0.5, l2_eps=1e-6, norm_eps=1e-5, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv)
+
+
+def bpin_block_from_library_steps(o):
+    """The block equals its steps done with library routines: the conv window
+    as an explicit dot product and scipy's logistic function, the q|k|v split
+    in that channel order, numpy norms, gates from the logistic function, the
+    (separately pinned) token-serial recurrence on those inputs, and torch's
+    rms_norm times silu(z)."""
+    import oracle
+    import torch
+    import torch.nn.functional as F
+    d = block_case(65)
+    B, Hk, Hv, Dk, Dv = 2, d["Hk"], d["Hv"], d["Dk"], d["Dv"]
+    out, conv_st, st = o.block(**d)
+    f = lambda x: np.asarray(x, np.float64)
+    win = np.concatenate([f(d["conv_state"])[:, :, 1:], f(d["mixed"])[:, :, None]], axis=2)
+    pre = np.einsum("bck,ck->bc", win, f(d["conv_weight"]))
+    xc = pre * _expit(pre)
+    _close(conv_st, win, 0.0, "block conv state")
+    q = xc[:, :Hk * Dk].reshape(B, Hk, 1, Dk)
+    k = xc[:, Hk * Dk:2 * Hk * Dk].reshape(B, Hk, 1, Dk)
+    v = xc[:, 2 * Hk * Dk:].reshape(B, Hv, 1, Dv)
+    nrm = lambda x: x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + d["l2_eps"])
+    g = np.log(_decay_by_library(d["a"][:, :, None], d["A_log"], d["dt_bias"]))
+    ro, rs = oracle.gdn_serial(nrm(q), nrm(k), v, g, _expit(d["b"])[:, :, None], d["scale"],
+                               d["state"])
+    _close(st, rs, 2e-6, "block state")         # the serial oracle takes float32 inputs
+    zz = torch.from_numpy(f(d["z"]).reshape(B, Hv, Dv))
+    y = F.rms_norm(torch.from_numpy(ro[:, :, 0]), (Dv,), weight=torch.from_numpy(f(d["norm_weight"])),
+                   eps=d["norm_eps"]) * F.silu(zz)
+    _close(out, y.numpy().reshape(B, Hv * Dv), 2e-5, "block out")
+
+
+def bpin_block_chain_matches_prefill(o):
+    """Three block steps from a zero conv window equal one conv prefill of the
+    three tokens followed by the gated recurrence over them (the state and
+    the normalised outputs of each step)."""
+    import oracle
+    from oracle import conv1d
+    d = block_case(66, B=1, Hk=1, Hv=2, Dk=4, Dv=3, K=3)
+    Hk, Hv, Dk, Dv = d["Hk"], d["Hv"], d["Dk"], d["Dv"]
+    C = d["mixed"].shape[1]
+    r = _rng(67)
+    toks = r.standard_normal((3, 1, C)).astype(np.float32)
+    zs = r.standard_normal((3, 1, Hv * Dv)).astype(np.float32)
+    a3 = r.standard_normal((3, 1, Hv)).astype(np.float32)
+    b3 = r.standard_normal((3, 1, Hv)).astype(np.float32)
+    cs = np.zeros((1, C, 3), np.float32)
+    st = d["state"]
+    outs = []
+    for t in range(3):
+        dd = dict(d, mixed=toks[t], z=zs[t], a=a3[t], b=b3[t], conv_state=cs, state=st)
+        y, cs, st = o.block(**dd)
+        outs.append(y)
+    xc, _ = conv1d.conv1d_prefill(np.transpose(toks, (1, 2, 0)), d["conv_weight"])   # [1, C, 3]
+    q = np.transpose(xc[:, :Hk * Dk].reshape(1, Hk, Dk, 3), (0, 1, 3, 2))
+    k = np.transpose(xc[:, Hk * Dk:2 * Hk * Dk].reshape(1, Hk, Dk, 3), (0, 1, 3, 2))
+    v = np.transpose(xc[:, 2 * Hk * Dk:].reshape(1, Hv, Dv, 3), (0, 1, 3, 2))
+    ro, rs = oracle.gdn_serial_gated_f64(q, k, v, np.transpose(a3, (1, 2, 0)),
+                                         np.transpose(b3, (1, 2, 0)), d["A_log"], d["dt_bias"],
+                                         d["scale"], d["l2_eps"], d["state"])
+    _close(st, rs, 1e-12, "chained block state")
+    for t in range(3):
+        y = o.rmsnorm(ro[:, :, t], zs[t].reshape(1, Hv, Dv), d["norm_weight"], d["norm_eps"])
+        _close(outs[t], y.reshape(1, Hv * Dv), 1e-12, "chained block out %d" % t)
+
+
+RMS_PINS = [rpin_rmsnorm_matches_torch, rpin_rmsnorm_closed_forms,
+            bpin_block_from_library_steps, bpin_block_chain_matches_prefill]

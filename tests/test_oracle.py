@@ -71,8 +71,8 @@ def test_workload_inputs_are_seeded_and_normalised():
 @pytest.mark.parametrize("pin", P.GATED_PINS, ids=lambda f: f.__name__)
 def test_gated_pin(pin):
     from types import SimpleNamespace
-    pin(SimpleNamespace(gated=oracle.gdn_serial_gated, gates=oracle.gdn_gates,
-                        l2norm=oracle.l2_normalize))
+    pin(SimpleNamespace(gated=oracle.gdn_serial_gated, gated_f64=oracle.gdn_serial_gated_f64,
+                        gates=oracle.gdn_gates, l2norm=oracle.l2_normalize))
 
 
 @pytest.mark.parametrize("pin", P.CONV_PINS, ids=lambda f: f.__name__)
@@ -80,3 +80,10 @@ def test_conv_pin(pin):
     from types import SimpleNamespace
     from oracle import conv1d
     pin(SimpleNamespace(prefill=conv1d.conv1d_prefill, decode=conv1d.conv1d_decode))
+
+
+@pytest.mark.parametrize("pin", P.RMS_PINS, ids=lambda f: f.__name__)
+def test_rms_block_pin(pin):
+    from types import SimpleNamespace
+    from oracle import block
+    pin(SimpleNamespace(rmsnorm=block.rmsnorm_gated, block=block.decode_block))

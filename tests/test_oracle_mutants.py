@@ -18,6 +18,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn_serial.c")
 
 MUTANTS = {
     "no_decay": ("St[i * Dv + c] *= a;", "St[i * Dv + c] *= 1.0;"),
+    "f64_inputs_as_float": ("return f64 ? ((const double*)p)[i]", "return 0 ? ((const double*)p)[i]"),
     "decay_twice": ("St[i * Dv + c] *= a;", "St[i * Dv + c] *= a * a;"),
     "delta_sign": ("u[c] = be * (vt[c] - x);", "u[c] = be * (vt[c] + x);"),
     "no_beta": ("u[c] = be * (vt[c] - x);", "u[c] = (vt[c] - x);"),
@@ -37,13 +38,13 @@ MUTANTS = {
     "sigmoid_sign": ("1.0 / (1.0 + exp(-x));", "1.0 / (1.0 + exp(x));"),
     "norm_no_sqrt": ("1.0 / sqrt(ss + eps);", "1.0 / (ss + eps);"),
     "norm_eps_outside": ("1.0 / sqrt(ss + eps);", "1.0 / (sqrt(ss) + eps);"),
-    "q_not_normalised": ("l2norm_row(qt, eps, qd, Dk);",
-                         "for (long i = 0; i < Dk; ++i) qd[i] = (double)qt[i];"),
-    "k_not_normalised": ("l2norm_row(kt, eps, kd, Dk);",
-                         "for (long i = 0; i < Dk; ++i) kd[i] = (double)kt[i];"),
-    "gate_key_head": ("(double)A_log[h],", "(double)A_log[j],"),
-    "gates_swapped": ("gates((double)gl[bh * S + t], (double)bt[bh * S + t],",
-                      "gates((double)bt[bh * S + t], (double)gl[bh * S + t],"),
+    "q_not_normalised": ("l2norm_row(q, qt, f64, eps, qd, Dk);",
+                         "for (long i = 0; i < Dk; ++i) qd[i] = in_at(q, qt + i, f64);"),
+    "k_not_normalised": ("l2norm_row(k, kt, f64, eps, kd, Dk);",
+                         "for (long i = 0; i < Dk; ++i) kd[i] = in_at(k, kt + i, f64);"),
+    "gate_key_head": ("in_at(A_log, h, f64)", "in_at(A_log, j, f64)"),
+    "gates_swapped": ("gates(in_at(gl, bh * S + t, f64), in_at(bt, bh * S + t, f64),",
+                      "gates(in_at(bt, bh * S + t, f64), in_at(gl, bh * S + t, f64),"),
 }
 
 
@@ -64,8 +65,8 @@ def _wrap(libpath):
     """The mutant's three entries, marshalled like the real oracle's."""
     lib = ctypes.CDLL(libpath)
     real = oracle._lib()
-    for name in ("oracle_gdn_serial", "oracle_gdn_serial_gated", "oracle_gdn_gates",
-                 "oracle_l2norm"):
+    for name in ("oracle_gdn_serial", "oracle_gdn_serial_gated", "oracle_gdn_serial_gated_f64",
+                 "oracle_gdn_gates", "oracle_l2norm"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = getattr(real, name).argtypes
     f32 = lambda *xs: [np.ascontiguousarray(np.asarray(x, np.float32)) for x in xs]
@@ -99,6 +100,20 @@ def _wrap(libpath):
         assert rc == 0
         return out, st
 
+    def gated_f64(q, k, v, a, b, A_log, dt_bias, scale, eps, state=None):
+        q, k, v, a, b, A_log, dt_bias = [np.ascontiguousarray(np.asarray(x, np.float64))
+                                         for x in (q, k, v, a, b, A_log, dt_bias)]
+        B, Hk, S, Dk = q.shape
+        Hv, Dv = v.shape[1], v.shape[3]
+        st = state_of(state, B, Hv, Dk, Dv)
+        out = np.empty((B, Hv, S, Dv))
+        rc = lib.oracle_gdn_serial_gated_f64(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, a.ctypes.data, b.ctypes.data,
+            A_log.ctypes.data, dt_bias.ctypes.data, float(eps), float(scale), st.ctypes.data,
+            out.ctypes.data, B, Hk, Hv, S, Dk, Dv, 1)
+        assert rc == 0
+        return out, st
+
     def gates(a, b, A_log, dt_bias):
         a, b, A_log, dt_bias = f32(a, b, A_log, dt_bias)
         g = np.empty(a.shape)
@@ -115,7 +130,7 @@ def _wrap(libpath):
                                  x.size // x.shape[-1], x.shape[-1]) == 0
         return y
 
-    return fn, SimpleNamespace(gated=gated, gates=gates, l2norm=l2norm)
+    return fn, SimpleNamespace(gated=gated, gated_f64=gated_f64, gates=gates, l2norm=l2norm)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -161,6 +176,40 @@ def test_conv_mutant_is_caught(name):
     ns = SimpleNamespace(prefill=mod.conv1d_prefill, decode=mod.conv1d_decode)
     caught = []
     for pin in P.CONV_PINS:
+        try:
+            pin(ns)
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, "planted mistake %r passed every pin" % name
+
+
+BLOCK_SRC = os.path.join(os.path.dirname(oracle.__file__), "block.py")
+BLOCK_MUTANTS = {
+    "rms_no_sqrt": ("return o / np.sqrt(ms + eps)", "return o / (ms + eps)"),
+    "rms_sum_not_mean": ("ms = np.mean(o * o, axis=-1, keepdims=True)",
+                         "ms = np.sum(o * o, axis=-1, keepdims=True)"),
+    "gate_sigmoid_not_silu": ("* (z / (1.0 + np.exp(-z)))", "* (1.0 / (1.0 + np.exp(-z)))"),
+    "no_weight": ("/ np.sqrt(ms + eps) * weight *", "/ np.sqrt(ms + eps) *"),
+    "q_k_swapped": ("q = xc[:, :Hk * Dk].reshape(B, Hk, 1, Dk)",
+                    "q = xc[:, Hk * Dk:2 * Hk * Dk].reshape(B, Hk, 1, Dk)"),
+    "v_from_k": ("v = xc[:, 2 * Hk * Dk:].reshape(B, Hv, 1, Dv)",
+                 "v = xc[:, Hk * Dk:Hk * Dk + Hv * Dv].reshape(B, Hv, 1, Dv)"),
+    "z_not_applied": ("np.asarray(z, np.float64).reshape(B, Hv, Dv)",
+                      "np.ones((B, Hv, Dv)) * 30.0"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BLOCK_MUTANTS))
+def test_block_mutant_is_caught(name):
+    import types
+    old, new = BLOCK_MUTANTS[name]
+    src = open(BLOCK_SRC).read()
+    assert src.count(old) == 1, "mutation site for %s not unique" % name
+    mod = types.ModuleType("block_mutant_" + name)
+    exec(compile(src.replace(old, new), "<mutant %s>" % name, "exec"), mod.__dict__)
+    ns = SimpleNamespace(rmsnorm=mod.rmsnorm_gated, block=mod.decode_block)
+    caught = []
+    for pin in P.RMS_PINS:
         try:
             pin(ns)
         except (AssertionError, IndexError, ValueError):
