@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--only prefill|decode|prefill_gated|decode_gated|conv_prefill|
-                            conv_decode|copy]
+                            conv_decode|rmsnorm|decode_block|copy]
 
 One step = one ``gdn_chunked_prefill`` call on the batched long prefill
 workload (B=4, Hk=16, Hv=32, Dk=Dv=128, S=8192, bf16 q/k/v, fp32 g/beta and
@@ -24,7 +24,9 @@ gate pre-activations as inputs) are timed the same way on the same workloads
 and reported under "prefill_gated" and "decode_gated"; the depthwise conv1d
 that precedes them (prefill over the B=4, T=8192 mixed q|k|v tensor with
 C = 8192 channels and K = 4 taps; one decode token at B=256) under
-"conv1d_prefill" and "conv1d_decode".
+"conv1d_prefill" and "conv1d_decode"; the RMSNormGated epilogue over the
+prefill output under "rmsnorm_gated"; the fused decode block (conv1d step,
+prologue, recurrence, RMSNormGated; B=256, K=4) under "decode_block".
 
 ``--only copy`` runs a plain device-to-device copy of ``--copy-mib`` MiB
 (used to calibrate the HBM byte counters of rocprofv3 against a kernel of
@@ -89,6 +91,8 @@ KERNEL_SOURCES["gdn_prefill_kernel_gated"] = KERNEL_SOURCES["gdn_prefill_kernel"
 KERNEL_SOURCES["gdn_decode_kernel_gated"] = KERNEL_SOURCES["gdn_decode_kernel"]
 KERNEL_SOURCES["gdn_conv1d_prefill_kernel"] = "linear_attention_recurrence_chunked_amd/csrc/gdn_conv1d.hip"
 KERNEL_SOURCES["gdn_conv1d_decode_kernel"] = KERNEL_SOURCES["gdn_conv1d_prefill_kernel"]
+KERNEL_SOURCES["gdn_rmsnorm_gated_kernel"] = "linear_attention_recurrence_chunked_amd/csrc/gdn_norm.hip"
+KERNEL_SOURCES["gdn_decode_kernel_block"] = KERNEL_SOURCES["gdn_decode_kernel"]
 
 
 def source_digest(kernel):
@@ -255,6 +259,69 @@ def bench_conv(torch, gdn, inputs, name, steps, warmup):
     return w, (t1 - t0) * 1e3 / steps, kern_ms, conv_algorithmic(w.B, w.C, w.T, w.K)
 
 
+def _timed(torch, stream, step, steps, warmup):
+    """W untimed calls, then K calls each bracketed by events on ``stream``;
+    returns (wall ms per call, mean event ms per call)."""
+    for _ in range(warmup):
+        step(0)
+    ev = _events(torch, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def bench_rmsnorm(torch, gdn, steps, warmup):
+    """RMSNormGated over the prefill output of the B=4, S=8192 workload."""
+    B, Hv, S, Dv = 4, 32, 8192, 128
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev).manual_seed(11)
+    o = torch.randn((B, Hv, S, Dv), device=dev, generator=g).to(torch.bfloat16)
+    z = torch.randn((B, S, Hv, Dv), device=dev, generator=g).to(torch.bfloat16)
+    w = 1.0 + 0.1 * torch.randn((Dv,), device=dev, generator=g)
+    out = torch.empty_like(z)
+    stream = torch.cuda.current_stream(dev)
+    ms, kern = _timed(torch, stream, lambda i: gdn.rmsnorm_gated(o, z, w, 1e-6, out=out,
+                                                                 stream=stream), steps, warmup)
+    nbytes = float(3 * B * Hv * S * Dv * 2 + Dv * 4)
+    return dict(B=B, Hv=Hv, S=S, Dv=Dv), ms, kern, nbytes
+
+
+def bench_decode_block(torch, gdn, inputs, steps, warmup):
+    """The fused decode block at B=256, Hk=16, Hv=32, Dk=Dv=128, K=4, bf16:
+    eight seeded token draws cycled, conv windows ping-ponged, state carried."""
+    B, Hk, Hv, Dk, Dv, K = 256, 16, 32, 128, 128, 4
+    dev = torch.device("cuda", 0)
+    d0 = inputs.draw_block(B, Hk, Hv, Dk, Dv, K)
+    toks = [d0] + [inputs.draw_block(B, Hk, Hv, Dk, Dv, K, step=i, with_state=False)
+                   for i in range(1, 8)]
+    up = lambda a, bf: torch.from_numpy(a).to(dev).to(torch.bfloat16 if bf else torch.float32)
+    dtoks = [{k: up(t[k], k in ("mixed", "z")) for k in ("mixed", "z", "a", "b")} for t in toks]
+    fx = {k: up(d0[k], False) for k in ("conv_weight", "A_log", "dt_bias", "norm_weight")}
+    st = up(d0["state"], False)
+    win = [up(d0["conv_state"], True), up(d0["conv_state"], True)]
+    out = torch.empty((B, Hv * Dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        t = dtoks[i % 8]
+        gdn.decode_block(t["mixed"], t["z"], t["a"], t["b"], win[i & 1], fx["conv_weight"],
+                         fx["A_log"], fx["dt_bias"], fx["norm_weight"], 1.0 / np.sqrt(Dk), 1e-6,
+                         1e-6, st, Hk, Hv, Dk, Dv, conv_state_out=win[(i + 1) & 1], out=out,
+                         stream=stream)
+
+    ms, kern = _timed(torch, stream, step, steps, warmup)
+    C = 2 * Hk * Dk + Hv * Dv
+    nbytes = float(2 * B * Hv * Dk * Dv * 4 + B * C * 2 + B * Hv * Dv * 2 * 2 + B * Hv * 8
+                   + 2 * B * C * K * 2 + C * K * 4 + Hv * 8 + Dv * 4)
+    return dict(B=B, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, K=K), ms, kern, nbytes
+
+
 def bench_copy(torch, mib, steps):
     """Streaming elementwise kernel over ``mib`` MiB of fp32: b = -a reads and
     writes that many bytes once (a same-dtype copy_ would be a DMA transfer,
@@ -327,7 +394,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "prefill_gated", "decode_gated",
-                                       "conv_prefill", "conv_decode", "copy"], default=None)
+                                       "conv_prefill", "conv_decode", "rmsnorm", "decode_block",
+                                       "copy"], default=None)
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -357,6 +425,16 @@ def main():
         print(json.dumps({args.only + "_ms_per_step": dms, "kernel_ms": dkern_ms,
                           "GB_s": dbytes / (dkern_ms / 1e3) / 1e9}), flush=True)
         return
+    if args.only == "rmsnorm":
+        _, ms, kern, nb = bench_rmsnorm(torch, gdn, args.steps, args.warmup)
+        print(json.dumps({"rmsnorm_ms": ms, "kernel_ms": kern, "GB_s": nb / (kern / 1e3) / 1e9}),
+              flush=True)
+        return
+    if args.only == "decode_block":
+        _, ms, kern, nb = bench_decode_block(torch, gdn, inputs, args.steps, args.warmup)
+        print(json.dumps({"decode_block_ms": ms, "kernel_ms": kern,
+                          "GB_s": nb / (kern / 1e3) / 1e9}), flush=True)
+        return
     if args.only in ("conv_prefill", "conv_decode"):
         name = {"conv_prefill": "conv_prefill_b4_t8192", "conv_decode": "conv_decode_b256"}
         cw, cms, ckern_ms, cbytes = bench_conv(torch, gdn, inputs, name[args.only], args.steps,
@@ -385,6 +463,9 @@ def main():
                                             args.steps, args.warmup)
     cdw, cdms, cdkern, cdbytes = bench_conv(torch, gdn, inputs, "conv_decode_b256",
                                             10 * args.steps, args.warmup)
+    rcfg, rms_ms, rms_kern, rms_bytes = bench_rmsnorm(torch, gdn, args.steps, args.warmup)
+    bcfg, blk_ms, blk_kern, blk_bytes = bench_decode_block(torch, gdn, inputs, args.steps,
+                                                           args.warmup)
     tokens = w.B * w.S
     hbm = lambda b, ms: {"achieved": b / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "kernel_ms": ms,
@@ -440,6 +521,16 @@ def main():
                           "roofline": dict(bound="hbm", kernel="gdn_conv1d_decode_kernel",
                                            traffic=measured_traffic("gdn_conv1d_decode_kernel"),
                                            **hbm(cdbytes, cdkern))},
+        "rmsnorm_gated": dict(workload="prefill_b4_s8192 output", value=rcfg["B"] * rcfg["S"]
+                              / (rms_ms / 1e3), unit="tokens/s", ms_per_step=rms_ms,
+                              roofline=dict(bound="hbm", kernel="gdn_rmsnorm_gated_kernel",
+                                            traffic=measured_traffic("gdn_rmsnorm_gated_kernel"),
+                                            **hbm(rms_bytes, rms_kern)), **rcfg),
+        "decode_block": dict(workload="decode_block_b256", value=1e3 / blk_ms, unit="steps/s",
+                             ms_per_step=blk_ms,
+                             roofline=dict(bound="hbm", kernel="gdn_decode_kernel (block)",
+                                           traffic=measured_traffic("gdn_decode_kernel_block"),
+                                           **hbm(blk_bytes, blk_kern)), **bcfg),
         "host": {"cpu": platform.processor() or platform.machine(),
                  "gpu": torch.cuda.get_device_name(0)},
     }

@@ -62,7 +62,7 @@ typedef enum {
     GDN_ERR_ALIAS = 6,        /* out or state_inout overlaps another tensor argument  */
     GDN_ERR_WORKSPACE = 7,    /* workspace smaller than the queried size              */
     GDN_ERR_HIP = 8,          /* the HIP runtime refused a launch                     */
-    GDN_ERR_VALUE = 9         /* l2_eps is negative or not finite (gated entries)     */
+    GDN_ERR_VALUE = 9         /* an epsilon argument is negative or not finite        */
 } gdn_status;
 
 /* Opaque stream handle: a hipStream_t. NULL selects the null stream. */
@@ -207,6 +207,67 @@ gdn_status gdn_conv1d_prefill(const void* mixed, const float* conv_weight, void*
  */
 gdn_status gdn_conv1d_decode(const void* x, const float* conv_weight, void* conv_state_inout,
                              void* out, int B, int C, int K, int dtype, gdn_stream stream);
+
+/*
+ * gdn_rmsnorm_gated -- the RMSNormGated output epilogue ("GDN Block TKG Kernel
+ * API Reference": introduction, "RMSNormGated"; Parameters norm_weight, the
+ * gamma over head_v_dim, and W_in_z, whose projection z gates it), applied
+ * to a prefill output. The page gives no formula: read as the gated RMS
+ * norm over each (token, head) row of Dv values, normalised first,
+ *
+ *   out[b,s,h,:] = o[b,h,s,:] / sqrt(mean(o[b,h,s,:]^2) + eps)
+ *                  * norm_weight * silu(z[b,s,h,:]),   silu(x) = x / (1 + e^-x)
+ *
+ *   o            [B, Hv, S, Dv] compute dtype: head-major, as gdn_chunked_prefill
+ *                writes it
+ *   z, out       [B, S, Hv, Dv] compute dtype: token-major (heads of a token
+ *                adjacent), the layout of the block's output
+ *   norm_weight  [Dv] fp32;  eps >= 0 and finite, else GDN_ERR_VALUE
+ *
+ * 16 <= Dv <= 128, a multiple of 16; pointers 16-byte aligned; out overlaps
+ * no input.
+ */
+gdn_status gdn_rmsnorm_gated(const void* o, const void* z, const float* norm_weight, float eps,
+                             void* out, int B, int Hv, int S, int Dv, int dtype,
+                             gdn_stream stream);
+
+/*
+ * gdn_decode_block -- one token through the "GDN Block TKG Kernel API
+ * Reference" decode layer between its input and output projections
+ * (introduction), in one kernel:
+ *
+ *   1. conv1d decode step over the raw mixed token ("GDN Conv1D Kernel API
+ *      Reference", gdn_conv1d_decode): windows shift, x = silu(w . window);
+ *   2. split x into q (Hk heads of Dk), k (Hk x Dk), v (Hv x Dv), in that
+ *      channel order (conv_dim = 2 key_dim + value_dim, Dimensions);
+ *   3. the gated prologue and single-token recurrence of
+ *      gdn_decode_step_gated (value head h reads key head h / (Hv/Hk));
+ *   4. RMSNormGated of each head's Dv outputs with z and norm_weight, as in
+ *      gdn_rmsnorm_gated.
+ *
+ *   mixed          [B, C] compute dtype, C = 2 Hk Dk + Hv Dv (raw q|k|v)
+ *   z              [B, Hv Dv] compute dtype (the z projection)
+ *   a, b           [B, Hv] fp32 gate pre-activations
+ *   conv_state_in  [B, C, K] compute dtype, the previous windows (read)
+ *   conv_state_out [B, C, K] compute dtype, the shifted windows (written; a
+ *                  separate buffer, as the page returns a new conv state:
+ *                  the heads of a GQA group read the same q/k windows)
+ *   conv_weight    [C, K] fp32, 1 <= K <= 8
+ *   A_log, dt_bias [Hv] fp32;  norm_weight [Dv] fp32
+ *   scale, l2_eps, norm_eps  as in gdn_decode_step_gated / gdn_rmsnorm_gated
+ *   state_inout    [B, Hv, Dk, Dv] fp32, updated in place
+ *   out            [B, Hv Dv] compute dtype (token-major normalised output)
+ *
+ * Dk, Dv as for gdn_decode_step; pointers 16-byte aligned; the written
+ * buffers (conv_state_out, state_inout, out) overlap nothing else.
+ */
+gdn_status gdn_decode_block(const void* mixed, const void* z, const float* a, const float* b,
+                            const void* conv_state_in, void* conv_state_out,
+                            const float* conv_weight, const float* A_log, const float* dt_bias,
+                            const float* norm_weight, float scale, float l2_eps, float norm_eps,
+                            float* state_inout, void* out,
+                            int B, int Hk, int Hv, int Dk, int Dv, int K, int dtype,
+                            gdn_stream stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* gdn_status_string(int status);

@@ -11,6 +11,8 @@ mirror the C ABI in ``include/gdn.h``:
 * :func:`decode_step_gated`     -> ``gdn_decode_step_gated``
 * :func:`conv1d_prefill`  -> ``gdn_conv1d_prefill``
 * :func:`conv1d_decode`   -> ``gdn_conv1d_decode``
+* :func:`rmsnorm_gated`   -> ``gdn_rmsnorm_gated``
+* :func:`decode_block`    -> ``gdn_decode_block``
 * :func:`prefill_workspace_bytes` -> ``gdn_chunked_prefill_workspace_bytes``
 * :func:`status_string`   -> ``gdn_status_string``
 
@@ -22,7 +24,7 @@ import ctypes
 import os
 
 __all__ = ["chunked_prefill", "decode_step", "chunked_prefill_gated", "decode_step_gated",
-           "conv1d_prefill", "conv1d_decode",
+           "conv1d_prefill", "conv1d_decode", "rmsnorm_gated", "decode_block",
            "prefill_workspace_bytes", "status_string",
            "GdnError", "LibraryNotBuilt", "load_library", "LIB_PATH", "GDN_F32", "GDN_BF16"]
 
@@ -33,6 +35,7 @@ GDN_F32, GDN_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_DTYPE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
           8: "GDN_ERR_HIP", 9: "GDN_ERR_VALUE"}
+_F = ctypes.c_float
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -79,6 +82,10 @@ def load_library():
     lib.gdn_conv1d_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
     lib.gdn_conv1d_decode.restype = _I
     lib.gdn_conv1d_decode.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P]
+    lib.gdn_rmsnorm_gated.restype = _I
+    lib.gdn_rmsnorm_gated.argtypes = [_P, _P, _P, ctypes.c_float, _P, _I, _I, _I, _I, _I, _P]
+    lib.gdn_decode_block.restype = _I
+    lib.gdn_decode_block.argtypes = [_P] * 10 + [ctypes.c_float] * 3 + [_P, _P] + [_I] * 7 + [_P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [_I]
     lib.gdn_version.restype = _I
@@ -341,3 +348,76 @@ def conv1d_decode(x, state, weight, out=None, stream=None):
     _raise(lib.gdn_conv1d_decode(x.data_ptr(), weight.data_ptr(), state.data_ptr(),
                                  out.data_ptr(), B, C, K, code, _stream(stream, dev)))
     return out
+
+
+def rmsnorm_gated(o, z, weight, eps, out=None, stream=None):
+    """RMSNormGated epilogue (``gdn_rmsnorm_gated``): o [B,Hv,S,Dv] head-major
+    (a prefill output), z [B,S,Hv,Dv] token-major, weight [Dv] fp32. Returns
+    out [B,S,Hv,Dv] = o / sqrt(mean(o^2) + eps) * weight * silu(z)."""
+    import torch
+    lib = load_library()
+    dev = o.device
+    code = _dtype_code(o)
+    _check(o, "o", o.dtype, dev)
+    _check(z, "z", o.dtype, dev)
+    _check(weight, "weight", torch.float32, dev)
+    if o.dim() != 4:
+        raise ValueError("o must be [B,Hv,S,Dv]")
+    B, Hv, S, Dv = o.shape
+    if z.shape != (B, S, Hv, Dv) or weight.shape != (Dv,):
+        raise ValueError("z must be [B,S,Hv,Dv] and weight [Dv]")
+    if out is None:
+        out = torch.empty_like(z)
+    else:
+        _check(out, "out", o.dtype, dev)
+        if out.shape != z.shape:
+            raise ValueError("out must be [B,S,Hv,Dv]")
+    _raise(lib.gdn_rmsnorm_gated(o.data_ptr(), z.data_ptr(), weight.data_ptr(), float(eps),
+                                 out.data_ptr(), B, Hv, S, Dv, code, _stream(stream, dev)))
+    return out
+
+
+def decode_block(mixed, z, a, b, conv_state_in, conv_weight, A_log, dt_bias, norm_weight,
+                 scale, l2_eps, norm_eps, state, Hk, Hv, Dk, Dv, conv_state_out=None,
+                 out=None, stream=None):
+    """One token through the decode block without projections
+    (``gdn_decode_block``). mixed [B,C] (C = 2 Hk Dk + Hv Dv) and z [B,Hv Dv]
+    in bf16 or fp32; a, b [B,Hv] fp32; conv_state_in [B,C,K] (compute dtype);
+    conv_weight [C,K], A_log, dt_bias [Hv], norm_weight [Dv] fp32; state
+    [B,Hv,Dk,Dv] fp32 (in place). Returns (out [B,Hv Dv], conv_state_out)."""
+    import torch
+    lib = load_library()
+    dev = mixed.device
+    code = _dtype_code(mixed)
+    B, C = mixed.shape
+    K = conv_weight.shape[1]
+    if C != 2 * Hk * Dk + Hv * Dv:
+        raise ValueError("mixed must have 2 Hk Dk + Hv Dv channels")
+    for t, n in ((mixed, "mixed"), (z, "z"), (conv_state_in, "conv_state_in")):
+        _check(t, n, mixed.dtype, dev)
+    for t, n in ((a, "a"), (b, "b"), (conv_weight, "conv_weight"), (A_log, "A_log"),
+                 (dt_bias, "dt_bias"), (norm_weight, "norm_weight"), (state, "state")):
+        _check(t, n, torch.float32, dev)
+    if (z.shape != (B, Hv * Dv) or a.shape != (B, Hv) or b.shape != (B, Hv)
+            or conv_state_in.shape != (B, C, K) or conv_weight.shape != (C, K)
+            or A_log.shape != (Hv,) or dt_bias.shape != (Hv,) or norm_weight.shape != (Dv,)
+            or state.shape != (B, Hv, Dk, Dv)):
+        raise ValueError("decode_block: inconsistent shapes")
+    if conv_state_out is None:
+        conv_state_out = torch.empty_like(conv_state_in)
+    else:
+        _check(conv_state_out, "conv_state_out", mixed.dtype, dev)
+        if conv_state_out.shape != (B, C, K):
+            raise ValueError("conv_state_out must be [B,C,K]")
+    if out is None:
+        out = torch.empty((B, Hv * Dv), dtype=mixed.dtype, device=dev)
+    else:
+        _check(out, "out", mixed.dtype, dev)
+        if out.shape != (B, Hv * Dv):
+            raise ValueError("out must be [B,Hv*Dv]")
+    _raise(lib.gdn_decode_block(
+        mixed.data_ptr(), z.data_ptr(), a.data_ptr(), b.data_ptr(), conv_state_in.data_ptr(),
+        conv_state_out.data_ptr(), conv_weight.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
+        norm_weight.data_ptr(), float(scale), float(l2_eps), float(norm_eps), state.data_ptr(),
+        out.data_ptr(), B, Hk, Hv, Dk, Dv, K, code, _stream(stream, dev)))
+    return out, conv_state_out

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libgdn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip", "gdn_conv1d.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip", "gdn_conv1d.hip", "gdn_norm.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

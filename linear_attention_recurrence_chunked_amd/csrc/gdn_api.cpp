@@ -223,6 +223,82 @@ gdn_status gdn_conv1d_decode(const void* x, const float* conv_weight, void* conv
                                                                                  : GDN_ERR_HIP;
 }
 
+gdn_status gdn_decode_block(const void* mixed, const void* z, const float* a, const float* b,
+                            const void* conv_state_in, void* conv_state_out,
+                            const float* conv_weight, const float* A_log, const float* dt_bias,
+                            const float* norm_weight, float scale, float l2_eps, float norm_eps,
+                            float* state_inout, void* out,
+                            int B, int Hk, int Hv, int Dk, int Dv, int K, int dtype,
+                            gdn_stream stream) {
+    if (!mixed || !z || !a || !b || !conv_state_in || !conv_state_out || !conv_weight ||
+        !A_log || !dt_bias || !norm_weight || !state_inout || !out)
+        return GDN_ERR_NULL;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (B < 1 || Hk < 1 || Hv < 1 || K < 1 || Hv % Hk != 0) return GDN_ERR_SHAPE;
+    if ((int64_t)B * Hv > INT32_MAX) return GDN_ERR_SHAPE;
+    if (Dk < 16 || Dk > kMaxHeadDim || Dk % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    if (Dv < 16 || Dv > kMaxHeadDim || Dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    if (K > kMaxConvTaps) return GDN_ERR_UNSUPPORTED;
+    if (!(l2_eps >= 0.0f) || !isfinite(l2_eps) || !(norm_eps >= 0.0f) || !isfinite(norm_eps))
+        return GDN_ERR_VALUE;
+    const void* ptrs[] = {mixed, z, a, b, conv_state_in, conv_state_out, conv_weight, A_log,
+                          dt_bias, norm_weight, state_inout, out};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_ALIGN;
+    const uint64_t es = dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t C = 2 * (uint64_t)Hk * Dk + (uint64_t)Hv * Dv;
+    if (C > INT32_MAX) return GDN_ERR_SHAPE;
+    const uint64_t uB = B, uHv = Hv, uK = K;
+    Range rmx, rz, ra, rb, rci, rco, rw, ral, rdt, rnw, rs, ro;
+    if (!extent(mixed, {uB, C}, es, rmx) || !extent(z, {uB, uHv * Dv}, es, rz) ||
+        !extent(a, {uB, uHv}, 4, ra) || !extent(b, {uB, uHv}, 4, rb) ||
+        !extent(conv_state_in, {uB, C, uK}, es, rci) ||
+        !extent(conv_state_out, {uB, C, uK}, es, rco) || !extent(conv_weight, {C, uK}, 4, rw) ||
+        !extent(A_log, {uHv}, 4, ral) || !extent(dt_bias, {uHv}, 4, rdt) ||
+        !extent(norm_weight, {(uint64_t)Dv}, 4, rnw) ||
+        !extent(state_inout, {uB, uHv, (uint64_t)Dk, (uint64_t)Dv}, 4, rs) ||
+        !extent(out, {uB, uHv * Dv}, es, ro))
+        return GDN_ERR_SHAPE;
+    const Range reads[] = {rmx, rz, ra, rb, rci, rw, ral, rdt, rnw};
+    const Range writes[] = {rco, rs, ro};
+    for (const Range& w : writes)
+        for (const Range& r : reads)
+            if (overlaps(w, r)) return GDN_ERR_ALIAS;
+    if (overlaps(rco, rs) || overlaps(rco, ro) || overlaps(rs, ro)) return GDN_ERR_ALIAS;
+    (void)hipGetLastError();
+    const gdn::DecodeArgs da{nullptr, nullptr, nullptr, a, b, scale, state_inout, out,
+                             B, Hk, Hv, Dk, Dv, true, A_log, dt_bias, l2_eps};
+    const gdn::BlockArgs blk{mixed, z, conv_state_in, conv_state_out, conv_weight, norm_weight,
+                             norm_eps, K};
+    return gdn::launch_decode_block(da, blk, dtype, (hipStream_t)stream) == hipSuccess
+               ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_rmsnorm_gated(const void* o, const void* z, const float* norm_weight, float eps,
+                             void* out, int B, int Hv, int S, int Dv, int dtype,
+                             gdn_stream stream) {
+    if (!o || !z || !norm_weight || !out) return GDN_ERR_NULL;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (B < 1 || Hv < 1 || S < 1) return GDN_ERR_SHAPE;
+    if (Dv < 16 || Dv > kMaxHeadDim || Dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return GDN_ERR_VALUE;
+    const void* ptrs[] = {o, z, norm_weight, out};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_ALIGN;
+    const uint64_t es = dtype == GDN_BF16 ? 2 : 4;
+    Range ro, rz, rw, rout;
+    if (!extent(o, {(uint64_t)B, (uint64_t)Hv, (uint64_t)S, (uint64_t)Dv}, es, ro) ||
+        !extent(z, {(uint64_t)B, (uint64_t)S, (uint64_t)Hv, (uint64_t)Dv}, es, rz) ||
+        !extent(norm_weight, {(uint64_t)Dv}, 4, rw) ||
+        !extent(out, {(uint64_t)B, (uint64_t)S, (uint64_t)Hv, (uint64_t)Dv}, es, rout))
+        return GDN_ERR_SHAPE;
+    if (overlaps(rout, ro) || overlaps(rout, rz) || overlaps(rout, rw)) return GDN_ERR_ALIAS;
+    (void)hipGetLastError();
+    const gdn::NormArgs na{o, z, norm_weight, eps, out, B, Hv, S, Dv};
+    return gdn::launch_rmsnorm_gated(na, dtype, (hipStream_t)stream) == hipSuccess ? GDN_OK
+                                                                                   : GDN_ERR_HIP;
+}
+
 const char* gdn_status_string(int status) {
     switch (status) {
         case GDN_OK: return "ok";
@@ -234,7 +310,7 @@ const char* gdn_status_string(int status) {
         case GDN_ERR_ALIAS: return "out or state_inout overlaps another tensor argument";
         case GDN_ERR_WORKSPACE: return "workspace too small";
         case GDN_ERR_HIP: return "HIP launch failed";
-        case GDN_ERR_VALUE: return "invalid scalar argument (l2_eps must be finite and >= 0)";
+        case GDN_ERR_VALUE: return "invalid scalar argument (an epsilon is negative or not finite)";
         default: return "unknown status";
     }
 }

@@ -36,9 +36,26 @@ struct ConvArgs {
     int B, C, T, K;
 };
 
+// Decode block extras: mixed [B, C] raw token (C = 2 Hk Dk + Hv Dv), z
+// [B, Hv Dv], conv windows [B, C, K] in and out, conv_w [C, K], norm_w [Dv].
+struct BlockArgs {
+    const void* mixed; const void* z; const void* conv_in; void* conv_out;
+    const float* conv_w; const float* norm_w; float norm_eps; int K;
+};
+
+// RMSNormGated over rows of Dv: o [B, Hv, S, Dv] (head-major), z and out
+// [B, S, Hv, Dv] (token-major), w [Dv].
+struct NormArgs {
+    const void* o; const void* z; const float* w; float eps; void* out;
+    int B, Hv, S, Dv;
+};
+
 // dtype: 0 = fp32 operands, 1 = bf16 operands (gdn_dtype).
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_conv1d(const ConvArgs& a, int dtype, bool decode, hipStream_t stream);
+hipError_t launch_decode_block(const DecodeArgs& a, const BlockArgs& blk, int dtype,
+                               hipStream_t stream);
+hipError_t launch_rmsnorm_gated(const NormArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace gdn

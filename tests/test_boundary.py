@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"gdn_chunked_prefill", "gdn_decode_step",
                           "gdn_chunked_prefill_gated", "gdn_decode_step_gated",
-                          "gdn_conv1d_prefill", "gdn_conv1d_decode",
+                          "gdn_conv1d_prefill", "gdn_conv1d_decode", "gdn_rmsnorm_gated",
+                          "gdn_decode_block",
                           "gdn_chunked_prefill_workspace_bytes", "gdn_status_string",
                           "gdn_version"}
     for n in names:
@@ -243,3 +244,67 @@ def test_conv_aliasing(lib, which):
     assert f(lib, out=fake(0, 16)) == ALIAS          # out over x
     assert f(lib, st=fake(1, 0)) == ALIAS            # state over the weights
     assert f(lib, out=fake(3, 0)) == ALIAS           # out over the state
+
+
+# ------------------------------------------------- RMSNormGated, decode block
+
+def rms(lib, o=None, z=None, w=None, out=None, eps=1e-6, B=2, Hv=4, S=8, Dv=64, dtype=1):
+    P = lambda v, i: fake(i) if v is None else v
+    return lib.gdn_rmsnorm_gated(P(o, 0), P(z, 1), P(w, 2), eps, P(out, 3), B, Hv, S, Dv, dtype,
+                                 None)
+
+
+BLOCK_ARGS = ["mixed", "z", "a", "b", "cin", "cout", "cw", "al", "dtb", "nw", "st", "out"]
+
+
+def block(lib, l2=1e-6, ne=1e-5, B=2, Hk=2, Hv=4, Dk=64, Dv=64, K=4, dtype=1, **ptr):
+    p = [ptr.get(n, fake(i)) for i, n in enumerate(BLOCK_ARGS)]
+    return lib.gdn_decode_block(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], p[9],
+                                0.125, l2, ne, p[10], p[11], B, Hk, Hv, Dk, Dv, K, dtype, None)
+
+
+@pytest.mark.parametrize("arg", ["o", "z", "w", "out"])
+def test_rmsnorm_null_and_alignment(lib, arg):
+    assert rms(lib, **{arg: 0}) == NULL
+    idx = ["o", "z", "w", "out"].index(arg)
+    assert rms(lib, **{arg: fake(idx, 4)}) == ALIGN
+
+
+def test_rmsnorm_checks(lib):
+    assert rms(lib, dtype=2) == DTYPE
+    for kw in (dict(B=0), dict(Hv=0), dict(S=0)):
+        assert rms(lib, **kw) == SHAPE
+    for dv in (0, 8, 24, 136):
+        assert rms(lib, Dv=dv) == UNSUP
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert rms(lib, eps=eps) == VALUE
+    assert rms(lib, out=fake(0, 32)) == ALIAS
+    assert rms(lib, out=fake(1, 0)) == ALIAS
+    assert rms(lib, out=fake(2, 0)) == ALIAS
+
+
+@pytest.mark.parametrize("arg", BLOCK_ARGS)
+def test_block_null_and_alignment(lib, arg):
+    assert block(lib, **{arg: 0}) == NULL
+    assert block(lib, **{arg: fake(BLOCK_ARGS.index(arg), 8)}) == ALIGN
+
+
+def test_block_checks(lib):
+    assert block(lib, dtype=4) == DTYPE
+    for kw in (dict(B=0), dict(Hk=0), dict(Hv=0), dict(K=0), dict(Hk=3, Hv=4)):
+        assert block(lib, **kw) == SHAPE, kw
+    for kw in (dict(Dk=8), dict(Dv=200), dict(K=9)):
+        assert block(lib, **kw) == UNSUP, kw
+    for kw in (dict(l2=-1.0), dict(ne=float("nan"))):
+        assert block(lib, **kw) == VALUE, kw
+
+
+@pytest.mark.parametrize("w", ["cout", "st", "out"])
+@pytest.mark.parametrize("r", ["mixed", "z", "a", "cin", "cw", "nw"])
+def test_block_written_buffers_overlapping_reads(lib, w, r):
+    assert block(lib, **{w: fake(BLOCK_ARGS.index(r), 0)}) == ALIAS
+
+
+def test_block_written_buffers_overlapping_each_other(lib):
+    assert block(lib, out=fake(BLOCK_ARGS.index("st"), 0)) == ALIAS
+    assert block(lib, cout=fake(BLOCK_ARGS.index("out"), 0)) == ALIAS
