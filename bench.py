@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--only prefill|decode|prefill_gated|decode_gated|conv_prefill|
-                            conv_decode|rmsnorm|decode_block|copy]
+                            conv_decode|rmsnorm|decode_block|inverse_ab|copy]
 
 One step = one ``gdn_chunked_prefill`` call on the batched long prefill
 workload (B=4, Hk=16, Hv=32, Dk=Dv=128, S=8192, bf16 q/k/v, fp32 g/beta and
@@ -27,6 +27,10 @@ C = 8192 channels and K = 4 taps; one decode token at B=256) under
 "conv1d_prefill" and "conv1d_decode"; the RMSNormGated epilogue over the
 prefill output under "rmsnorm_gated"; the fused decode block (conv1d step,
 prologue, recurrence, RMSNormGated; B=256, K=4) under "decode_block".
+"inverse_ab" times the prefill with each intra-chunk inverse (blocked
+substitution, the default, and the Neumann product) at S = 128 .. 8192 with
+the rest of the bench workload fixed: the shape of the pages' only measured
+comparison between inverse methods.
 
 ``--only copy`` runs a plain device-to-device copy of ``--copy-mib`` MiB
 (used to calibrate the HBM byte counters of rocprofv3 against a kernel of
@@ -322,6 +326,32 @@ def bench_decode_block(torch, gdn, inputs, steps, warmup):
     return dict(B=B, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, K=K), ms, kern, nbytes
 
 
+def bench_inverse_ab(torch, gdn, w, d, steps, warmup, lengths=(128, 512, 2048, 8192)):
+    """Kernel time of the prefill with each inverse method over the first S
+    tokens of the draw ``d`` (state carried, as in the main prefill line)."""
+    dev = torch.device("cuda", 0)
+    rows = []
+    for S in lengths:
+        t = {k: torch.from_numpy(np.ascontiguousarray(d[k][:, :, :S])).to(dev)
+             for k in ("q", "k", "v", "g_log", "beta")}
+        for k in ("q", "k", "v"):
+            t[k] = t[k].to(torch.bfloat16)
+        state = torch.from_numpy(d["state"]).to(dev)
+        out = torch.empty((w.B, w.Hv, S, w.Dv), dtype=torch.bfloat16, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        row = {"S": S}
+        for name, inv in (("substitution", gdn.GDN_INV_SUBSTITUTION),
+                          ("neumann", gdn.GDN_INV_NEUMANN)):
+            step = lambda i, inv=inv: gdn.chunked_prefill(
+                t["q"], t["k"], t["v"], t["g_log"], t["beta"], w.scale, state, out=out,
+                stream=stream, inverse=inv)
+            _, kern = _timed(torch, stream, step, steps, warmup)
+            row[name + "_ms"] = kern
+        row["neumann_over_substitution"] = row["neumann_ms"] / row["substitution_ms"]
+        rows.append(row)
+    return rows
+
+
 def bench_copy(torch, mib, steps):
     """Streaming elementwise kernel over ``mib`` MiB of fp32: b = -a reads and
     writes that many bytes once (a same-dtype copy_ would be a DMA transfer,
@@ -395,7 +425,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "prefill_gated", "decode_gated",
                                        "conv_prefill", "conv_decode", "rmsnorm", "decode_block",
-                                       "copy"], default=None)
+                                       "inverse_ab", "copy"], default=None)
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -424,6 +454,11 @@ def main():
                                              gated=args.only == "decode_gated")
         print(json.dumps({args.only + "_ms_per_step": dms, "kernel_ms": dkern_ms,
                           "GB_s": dbytes / (dkern_ms / 1e3) / 1e9}), flush=True)
+        return
+    if args.only == "inverse_ab":
+        d = inputs.draw_workload(w)
+        print(json.dumps({"inverse_ab": bench_inverse_ab(torch, gdn, w, d, args.steps,
+                                                         args.warmup)}), flush=True)
         return
     if args.only == "rmsnorm":
         _, ms, kern, nb = bench_rmsnorm(torch, gdn, args.steps, args.warmup)
@@ -466,6 +501,7 @@ def main():
     rcfg, rms_ms, rms_kern, rms_bytes = bench_rmsnorm(torch, gdn, args.steps, args.warmup)
     bcfg, blk_ms, blk_kern, blk_bytes = bench_decode_block(torch, gdn, inputs, args.steps,
                                                            args.warmup)
+    inv_ab = bench_inverse_ab(torch, gdn, w, d, max(10, args.steps // 2), max(5, args.warmup // 2))
     tokens = w.B * w.S
     hbm = lambda b, ms: {"achieved": b / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "kernel_ms": ms,
@@ -531,6 +567,8 @@ def main():
                              roofline=dict(bound="hbm", kernel="gdn_decode_kernel (block)",
                                            traffic=measured_traffic("gdn_decode_kernel_block"),
                                            **hbm(blk_bytes, blk_kern)), **bcfg),
+        "inverse_ab": {"workload": "prefill_b4_s8192, first S tokens", "unit": "ms per launch",
+                       "rows": inv_ab},
         "host": {"cpu": platform.processor() or platform.machine(),
                  "gpu": torch.cuda.get_device_name(0)},
     }

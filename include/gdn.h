@@ -62,7 +62,8 @@ typedef enum {
     GDN_ERR_ALIAS = 6,        /* out or state_inout overlaps another tensor argument  */
     GDN_ERR_WORKSPACE = 7,    /* workspace smaller than the queried size              */
     GDN_ERR_HIP = 8,          /* the HIP runtime refused a launch                     */
-    GDN_ERR_VALUE = 9         /* an epsilon argument is negative or not finite        */
+    GDN_ERR_VALUE = 9         /* an epsilon argument is negative or not finite, or an *
+                               * unknown inverse method                              */
 } gdn_status;
 
 /* Opaque stream handle: a hipStream_t. NULL selects the null stream. */
@@ -97,6 +98,29 @@ gdn_status gdn_chunked_prefill(const void* q, const void* k, const void* v,
                                int B, int Hk, int Hv, int S, int Dk, int Dv,
                                int dtype, void* workspace, size_t workspace_bytes,
                                gdn_stream stream);
+
+/* Intra-chunk inverse (I + A)^{-1} of the prefill: the choice the "GDN CTE
+ * Kernel API Reference" page offers as `algorithm` (Parameters), here on
+ * gfx950 terms. SUBSTITUTION: fp32 forward substitution on the 16x16
+ * diagonal blocks (the default); NEUMANN: the exact product
+ * (I - X)(I + X^2)(I + X^4)(I + X^8) of the nilpotent block X on fp32
+ * matrix cores. Both merge the off-diagonal block on fp32 matrix cores. */
+typedef enum {
+    GDN_INV_SUBSTITUTION = 0,
+    GDN_INV_NEUMANN = 1
+} gdn_inverse;
+
+/*
+ * gdn_chunked_prefill_inverse -- gdn_chunked_prefill with the inverse method
+ * chosen by `inverse` (a gdn_inverse value, else GDN_ERR_VALUE). Results of
+ * the two methods agree to fp32 rounding of the inverse.
+ */
+gdn_status gdn_chunked_prefill_inverse(const void* q, const void* k, const void* v,
+                                       const float* g_log, const float* beta, float scale,
+                                       float* state_inout, void* out,
+                                       int B, int Hk, int Hv, int S, int Dk, int Dv,
+                                       int dtype, int inverse, void* workspace,
+                                       size_t workspace_bytes, gdn_stream stream);
 
 /* Device scratch bytes gdn_chunked_prefill needs for these sizes (0 when the
  * arguments are invalid or no scratch is needed). */

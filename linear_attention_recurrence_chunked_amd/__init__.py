@@ -5,7 +5,8 @@ kernels of ``libgdn.so`` (built from ``csrc/`` by
 ``python -m linear_attention_recurrence_chunked_amd.build``). The names
 mirror the C ABI in ``include/gdn.h``:
 
-* :func:`chunked_prefill` -> ``gdn_chunked_prefill``
+* :func:`chunked_prefill` -> ``gdn_chunked_prefill`` (``gdn_chunked_prefill_inverse``
+  when an inverse method is chosen)
 * :func:`decode_step`     -> ``gdn_decode_step``
 * :func:`chunked_prefill_gated` -> ``gdn_chunked_prefill_gated``
 * :func:`decode_step_gated`     -> ``gdn_decode_step_gated``
@@ -26,12 +27,14 @@ import os
 __all__ = ["chunked_prefill", "decode_step", "chunked_prefill_gated", "decode_step_gated",
            "conv1d_prefill", "conv1d_decode", "rmsnorm_gated", "decode_block",
            "prefill_workspace_bytes", "status_string",
-           "GdnError", "LibraryNotBuilt", "load_library", "LIB_PATH", "GDN_F32", "GDN_BF16"]
+           "GdnError", "LibraryNotBuilt", "load_library", "LIB_PATH", "GDN_F32", "GDN_BF16",
+           "GDN_INV_SUBSTITUTION", "GDN_INV_NEUMANN"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
+GDN_INV_SUBSTITUTION, GDN_INV_NEUMANN = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_DTYPE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
           8: "GDN_ERR_HIP", 9: "GDN_ERR_VALUE"}
@@ -66,6 +69,10 @@ def load_library():
     lib.gdn_chunked_prefill.restype = _I
     lib.gdn_chunked_prefill.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                         _I, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.gdn_chunked_prefill_inverse.restype = _I
+    lib.gdn_chunked_prefill_inverse.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                                _I, _I, _I, _I, _I, _I, _I, _I, _P,
+                                                ctypes.c_size_t, _P]
     lib.gdn_chunked_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_chunked_prefill_workspace_bytes.argtypes = [_I] * 7
     lib.gdn_decode_step.restype = _I
@@ -132,12 +139,15 @@ def prefill_workspace_bytes(B, Hk, Hv, S, Dk, Dv, dtype_code):
                                                                   dtype_code))
 
 
-def chunked_prefill(q, k, v, g_log, beta, scale, state, out=None, workspace=None, stream=None):
+def chunked_prefill(q, k, v, g_log, beta, scale, state, out=None, workspace=None, stream=None,
+                    inverse=None):
     """Chunked gated delta-rule prefill (``gdn_chunked_prefill``).
 
     q, k [B,Hk,S,Dk] and v [B,Hv,S,Dv] in bf16 or fp32 (one dtype); g_log, beta
     [B,Hv,S] fp32; state [B,Hv,Dk,Dv] fp32, updated in place. Returns out
-    [B,Hv,S,Dv] in the compute dtype (allocated if not given).
+    [B,Hv,S,Dv] in the compute dtype (allocated if not given). ``inverse``
+    (GDN_INV_SUBSTITUTION or GDN_INV_NEUMANN) selects the intra-chunk inverse
+    through ``gdn_chunked_prefill_inverse``.
     """
     import torch
     lib = load_library()
@@ -162,10 +172,17 @@ def chunked_prefill(q, k, v, g_log, beta, scale, state, out=None, workspace=None
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    rc = lib.gdn_chunked_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), g_log.data_ptr(),
-                                 beta.data_ptr(), float(scale), state.data_ptr(), out.data_ptr(),
-                                 B, Hk, Hv, S, Dk, Dv, code, ws_ptr, ws_bytes,
-                                 _stream(stream, dev))
+    if inverse is None:
+        rc = lib.gdn_chunked_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), g_log.data_ptr(),
+                                     beta.data_ptr(), float(scale), state.data_ptr(),
+                                     out.data_ptr(), B, Hk, Hv, S, Dk, Dv, code, ws_ptr, ws_bytes,
+                                     _stream(stream, dev))
+    else:
+        rc = lib.gdn_chunked_prefill_inverse(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                             g_log.data_ptr(), beta.data_ptr(), float(scale),
+                                             state.data_ptr(), out.data_ptr(), B, Hk, Hv, S, Dk,
+                                             Dv, code, int(inverse), ws_ptr, ws_bytes,
+                                             _stream(stream, dev))
     _raise(rc)
     return out
 

@@ -97,7 +97,7 @@ gdn_status validate_gates(const Common& c, const float* A_log, const float* dt_b
 
 gdn_status prefill_common(const Common& c, bool gated, const float* A_log, const float* dt_bias,
                           float l2_eps, float scale, void* workspace, size_t workspace_bytes,
-                          gdn_stream stream) {
+                          gdn_stream stream, int inverse = GDN_INV_SUBSTITUTION) {
     gdn_status st = validate(c, /*prefill=*/true);
     if (st == GDN_OK && gated) st = validate_gates(c, A_log, dt_bias, l2_eps);
     if (st != GDN_OK) return st;
@@ -106,7 +106,8 @@ gdn_status prefill_common(const Common& c, bool gated, const float* A_log, const
     if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return GDN_ERR_WORKSPACE;
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     const gdn::PrefillArgs a{c.q, c.k, c.v, c.g, c.beta, scale, c.state, c.out,
-                             c.B, c.Hk, c.Hv, c.S, c.Dk, c.Dv, gated, A_log, dt_bias, l2_eps};
+                             c.B, c.Hk, c.Hv, c.S, c.Dk, c.Dv, gated, A_log, dt_bias, l2_eps,
+                             inverse};
     return gdn::launch_prefill(a, c.dtype, (hipStream_t)stream) == hipSuccess ? GDN_OK
                                                                                : GDN_ERR_HIP;
 }
@@ -167,6 +168,20 @@ gdn_status gdn_chunked_prefill(const void* q, const void* k, const void* v,
     const Common c{q, k, v, g_log, beta, state_inout, out, B, Hk, Hv, S, Dk, Dv, dtype};
     return prefill_common(c, false, nullptr, nullptr, 0.0f, scale, workspace, workspace_bytes,
                           stream);
+}
+
+gdn_status gdn_chunked_prefill_inverse(const void* q, const void* k, const void* v,
+                                       const float* g_log, const float* beta, float scale,
+                                       float* state_inout, void* out,
+                                       int B, int Hk, int Hv, int S, int Dk, int Dv,
+                                       int dtype, int inverse, void* workspace,
+                                       size_t workspace_bytes, gdn_stream stream) {
+    const Common c{q, k, v, g_log, beta, state_inout, out, B, Hk, Hv, S, Dk, Dv, dtype};
+    const gdn_status st = validate(c, /*prefill=*/true);
+    if (st != GDN_OK) return st;
+    if (inverse != GDN_INV_SUBSTITUTION && inverse != GDN_INV_NEUMANN) return GDN_ERR_VALUE;
+    return prefill_common(c, false, nullptr, nullptr, 0.0f, scale, workspace, workspace_bytes,
+                          stream, inverse);
 }
 
 gdn_status gdn_chunked_prefill_gated(const void* q, const void* k, const void* v,
@@ -310,7 +325,7 @@ const char* gdn_status_string(int status) {
         case GDN_ERR_ALIAS: return "out or state_inout overlaps another tensor argument";
         case GDN_ERR_WORKSPACE: return "workspace too small";
         case GDN_ERR_HIP: return "HIP launch failed";
-        case GDN_ERR_VALUE: return "invalid scalar argument (an epsilon is negative or not finite)";
+        case GDN_ERR_VALUE: return "invalid scalar argument (an epsilon is negative or not finite, or an unknown inverse method)";
         default: return "unknown status";
     }
 }

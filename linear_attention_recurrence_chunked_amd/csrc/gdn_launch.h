@@ -18,6 +18,7 @@ struct PrefillArgs {
     int B, Hk, Hv, S, Dk, Dv;
     bool gated;
     const float* A_log; const float* dt_bias; float l2_eps;
+    int inverse = 0;   // 0: blocked substitution, 1: Neumann product (ungated only)
 };
 
 struct DecodeArgs {

@@ -59,6 +59,13 @@
 // the P wave adds the two diagonal Q Q^T tiles for rq and folds rq rk_s into
 // P and rq into scale e^gamma (the Q S0 term). The consumers' code is the
 // same for both variants, and no normalised copy of q or k is rounded.
+//
+// INV selects the intra-chunk inverse (the choice the "GDN CTE Kernel API
+// Reference" page offers as its `algorithm` argument, Parameters): 0 =
+// blocked forward substitution (below), 1 = a Neumann product on each 16x16
+// diagonal block, (I + X)^{-1} = (I - X)(I + X^2)(I + X^4)(I + X^8) exactly
+// for the nilpotent X, on fp32 MFMA; both then merge the off-diagonal block
+// the same way.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 #include "gdn_mfma.h"
@@ -180,7 +187,7 @@ __device__ __forceinline__ float pick4(f32x4 v, int e) {
 // per-token decay and write strength and q, k are L2-normalised by the
 // caller; with GATED g_log and beta carry the raw a and b of the prologue
 // and q, k are raw (A_log, dt_bias [Hv] and l2_eps are used only then).
-template <typename E, int C, int DK, int BV, bool GATED>
+template <typename E, int C, int DK, int BV, bool GATED, int INV>
 __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ g_log, const float* __restrict__ beta,
@@ -576,6 +583,77 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
     };
 
+    // Neumann inverse (INV == 1). 16x16 matrices live in the accumulator
+    // layout: lane (j, g) = (l % 16, l / 16) holds rows 4g .. 4g+3 of column j.
+    // A product L R takes L^T and R in that layout: step s pairs lane group
+    // g's k = 4g + s on both sides, so the A operand is element s of L^T's
+    // vector and the B operand element s of R's. Keeping every factor and
+    // its transpose in registers, all products chain without any exchange.
+    auto mm4 = [&](f32x4 Lt, f32x4 R, f32x4 acc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Lt[s2], R[s2], acc, 0, 0, 0);
+        return acc;
+    };
+    // (I + P)^{-1} for nilpotent P, from P and P^T: with X = -P,
+    // T = (I + X)(I + X^2)(I + X^4)(I + X^8), accumulated as T <- T + T X^(2^m).
+    auto neumann16 = [&](f32x4 P, f32x4 Pt) __attribute__((always_inline)) {
+        f32x4 id;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) id[e] = (lc == lr + e) ? 1.f : 0.f;
+        const f32x4 X = -P, Xt = -Pt;
+        const f32x4 X2 = mm4(Xt, X, zero4()), X2t = mm4(X, Xt, zero4());
+        const f32x4 T1 = id + X, T1t = id + Xt;
+        const f32x4 T2 = mm4(T1t, X2, T1), T2t = mm4(X2, T1t, T1t);
+        const f32x4 X4 = mm4(X2t, X2, zero4()), X4t = mm4(X2, X2t, zero4());
+        const f32x4 T4 = mm4(T2t, X4, T2), T4t = mm4(X4, T2t, T2t);
+        const f32x4 X8 = mm4(X4t, X4, zero4());
+        return mm4(T4t, X8, T4);
+    };
+    // T11 and T22^T of chunk c (both in the accumulator layout) into tl, and
+    // the diagonal blocks into the T buffer.
+    auto n_solve = [&](int c, f32x4 (&tl)[2]) __attribute__((always_inline)) {
+        const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
+        const float* A11t = sA + Cf::AB_11T;   // [s][r] = A11[r][s]
+        const float* A22r = sA + Cf::AB_22R;   // [15-r][15-s] = A22[r][s]
+        const f32x4 a11 = *(const f32x4*)(A11t + lc * ALD + lr);          // A11[lr+e][lc]
+        f32x4 a11t, a22;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a11t[e] = A11t[(lr + e) * ALD + lc];                           // A11[lc][lr+e]
+            a22[e] = A22r[(15 - lr - e) * ALD + 15 - lc];                   // A22[lr+e][lc]
+        }
+        const f32x4 w = *(const f32x4*)(A22r + (15 - lc) * ALD + 12 - lr);
+        const f32x4 a22t = {w[3], w[2], w[1], w[0]};                       // A22[lc][lr+e]
+        tl[0] = neumann16(a11, a11t);                                       // T11
+        tl[1] = neumann16(a22t, a22);                                       // (I + A22^T)^{-1} = T22^T
+        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c % Cf::NTBUF) * Cf::SZ_TP);
+        // T11[lr+e][lc]: row lr+e, column tpos(lc); T22[lc][lr+e]: row 16+lc, columns 8g+4 ..
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_pair<SP>(Tp + (lr + e) * LDP + tpos(lc), C, tl[0][e]);
+        if constexpr (SP) {
+            uint32_t h0, l0, h1, l1;
+            split2(tl[1][0], tl[1][1], h0, l0);
+            split2(tl[1][2], tl[1][3], h1, l1);
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            E* p = Tp + (16 + lc) * LDP + 2 * lr + 4;
+            *(u32x2*)p = u32x2{h0, h1};
+            *(u32x2*)(p + C) = u32x2{l0, l1};
+        } else {
+            *(f32x4*)(Tp + (16 + lc) * LDP + 2 * lr + 4) = tl[1];
+        }
+    };
+    // T21 = -T22 (A21 T11) of chunk c from the registers n_solve left.
+    auto n_merge = [&](int c, const f32x4 (&tl)[2]) __attribute__((always_inline)) {
+        const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
+        E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c % Cf::NTBUF) * Cf::SZ_TP);
+        const f32x4 a21 = *(const f32x4*)(sA + Cf::AB_21 + lc * ALD + lr);  // A21[lc][lr+e]
+        const f32x4 Xm = mm4(a21, tl[0], zero4());                          // A21 T11
+        const f32x4 Y = mm4(tl[1], Xm, zero4());                            // T22 (A21 T11)
+        // T21 rows 16 + lr + e, column lc
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_pair<SP>(Tp + (16 + lr + e) * LDP + tpos(lc), C, -Y[e]);
+    };
+
     // P wave: P = scale (Q K^T (.) Mincl). GATED: rq from the diagonal of
     // Q Q^T, P = scale diag(rq) (Q K^T) diag(rk) (.) Mincl, and rq folded into
     // the chunk's scale e^gamma. rk comes from the A builder, which finished
@@ -832,26 +910,33 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
     } else if (wave >= Cf::W_T && wave < Cf::W_T + Cf::NTW) {
         const int pw = wave - Cf::W_T;
-        float x[16];
+        // the solve result waits in registers for the merge
+        typename std::conditional<INV == 0, float[16], f32x4[2]>::type x;
+        auto solve = [&](int c) __attribute__((always_inline)) {
+            if constexpr (INV == 0) t_solve(c, x); else n_solve(c, x);
+        };
+        auto merge = [&](int c) __attribute__((always_inline)) {
+            if constexpr (INV == 0) t_merge(c, x); else n_merge(c, x);
+        };
         __syncthreads();
         if constexpr (!Cf::SPREAD) {
-            if (NC > 0) { build_A(0); wave_lds_fence(); t_solve(0, x); t_merge(0, x); }
+            if (NC > 0) { build_A(0); wave_lds_fence(); solve(0); merge(0); }
         }
         __syncthreads();
         if constexpr (Cf::SPREAD) {
-            if (pw == 0 && NC > 0) { t_solve(0, x); t_merge(0, x); }
-            if (pw == 1 && NC > 1) t_solve(1, x);
+            if (pw == 0 && NC > 0) { solve(0); merge(0); }
+            if (pw == 1 && NC > 1) solve(1);
         }
         __syncthreads();
         for (int i = 0; i < NC; ++i) {
             if constexpr (Cf::SPREAD) {
                 if ((i & 1) == pw) {
-                    if (i + 2 < NC) t_solve(i + 2, x);
+                    if (i + 2 < NC) solve(i + 2);
                 } else {
-                    if (i + 1 < NC) t_merge(i + 1, x);
+                    if (i + 1 < NC) merge(i + 1);
                 }
             } else {
-                if (i + 1 < NC) { build_A(i + 1); wave_lds_fence(); t_solve(i + 1, x); t_merge(i + 1, x); }
+                if (i + 1 < NC) { build_A(i + 1); wave_lds_fence(); solve(i + 1); merge(i + 1); }
             }
             __syncthreads();
         }
@@ -928,14 +1013,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 
 // ---------------------------------------------------------------- launch
 
-template <typename E, int DK, int BV, bool GATED>
+template <typename E, int DK, int BV, bool GATED, int INV>
 static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream)
 {
     using Cf = PipeCfg<E, 32, DK, BV>;
     const int nvt = (a.Dv + BV - 1) / BV;
     const long long blocks = (long long)nvt * a.Hv * a.B;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gdn_prefill_kernel<E, 32, DK, BV, GATED>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((gdn_prefill_kernel<E, 32, DK, BV, GATED, INV>), dim3((unsigned)blocks),
                        dim3(Cf::THREADS), 0, stream,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, a.g_log, a.beta,
                        a.A_log, a.dt_bias, a.l2_eps, a.scale,
@@ -954,30 +1039,31 @@ static int pick_bv(const PrefillArgs& a, int max_bv)
     return 16;
 }
 
-template <typename E, int DK, bool GATED>
+template <typename E, int DK, bool GATED, int INV>
 static hipError_t launch_dk(const PrefillArgs& a, int max_bv, hipStream_t stream)
 {
     switch (pick_bv(a, max_bv)) {
-        case 64: if constexpr (sizeof(E) == 2) return launch_cfg<E, DK, 64, GATED>(a, stream);
+        case 64: if constexpr (sizeof(E) == 2) return launch_cfg<E, DK, 64, GATED, INV>(a, stream);
                  [[fallthrough]];
-        case 32: return launch_cfg<E, DK, 32, GATED>(a, stream);
-        default: return launch_cfg<E, DK, 16, GATED>(a, stream);
+        case 32: return launch_cfg<E, DK, 32, GATED, INV>(a, stream);
+        default: return launch_cfg<E, DK, 16, GATED, INV>(a, stream);
     }
 }
 
-template <bool GATED>
+template <bool GATED, int INV>
 static hipError_t launch_gated(const PrefillArgs& a, int dtype, hipStream_t stream)
 {
     if (dtype == 1)
-        return a.Dk <= 64 ? launch_dk<bf16, 64, GATED>(a, 64, stream)
-                          : launch_dk<bf16, 128, GATED>(a, 64, stream);
-    return a.Dk <= 64 ? launch_dk<float, 64, GATED>(a, 32, stream)
-                      : launch_dk<float, 128, GATED>(a, 32, stream);
+        return a.Dk <= 64 ? launch_dk<bf16, 64, GATED, INV>(a, 64, stream)
+                          : launch_dk<bf16, 128, GATED, INV>(a, 64, stream);
+    return a.Dk <= 64 ? launch_dk<float, 64, GATED, INV>(a, 32, stream)
+                      : launch_dk<float, 128, GATED, INV>(a, 32, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, hipStream_t stream)
 {
-    return a.gated ? launch_gated<true>(a, dtype, stream) : launch_gated<false>(a, dtype, stream);
+    if (a.inverse == 1) return launch_gated<false, 1>(a, dtype, stream);   // ungated only
+    return a.gated ? launch_gated<true, 0>(a, dtype, stream) : launch_gated<false, 0>(a, dtype, stream);
 }
 
 }  // namespace gdn

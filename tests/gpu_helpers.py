@@ -70,12 +70,14 @@ def to_np(t):
     return t.detach().float().cpu().numpy()
 
 
-def run_prefill(d, dtype, scale):
-    """Run gdn_chunked_prefill on the inputs of ``d``; returns (out, state) numpy."""
+def run_prefill(d, dtype, scale, inverse=None):
+    """Run gdn_chunked_prefill (or gdn_chunked_prefill_inverse) on the inputs
+    of ``d``; returns (out, state) numpy."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
     t = upload(d, dtype)
-    out = gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], scale, t["state"])
+    out = gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], scale, t["state"],
+                              inverse=inverse)
     torch.cuda.synchronize()
     return to_np(out), to_np(t["state"])
 

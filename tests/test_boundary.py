@@ -33,6 +33,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"gdn_chunked_prefill", "gdn_decode_step",
                           "gdn_chunked_prefill_gated", "gdn_decode_step_gated",
+                          "gdn_chunked_prefill_inverse",
                           "gdn_conv1d_prefill", "gdn_conv1d_decode", "gdn_rmsnorm_gated",
                           "gdn_decode_block",
                           "gdn_chunked_prefill_workspace_bytes", "gdn_status_string",
@@ -308,3 +309,14 @@ def test_block_written_buffers_overlapping_reads(lib, w, r):
 def test_block_written_buffers_overlapping_each_other(lib):
     assert block(lib, out=fake(BLOCK_ARGS.index("st"), 0)) == ALIAS
     assert block(lib, cout=fake(BLOCK_ARGS.index("out"), 0)) == ALIAS
+
+
+def test_inverse_method_values(lib):
+    P = lambda i: fake(i)
+    call = lambda inv, **kw: lib.gdn_chunked_prefill_inverse(
+        P(0), P(1), P(2), P(3), P(4), 0.1, P(5), P(6), kw.get("B", 2), 2, 4, 128, 64, 64,
+        kw.get("dtype", 1), inv, None, 0, None)
+    for bad in (-1, 2, 7):
+        assert call(bad) == VALUE
+    assert call(1, dtype=3) == DTYPE            # shape/dtype checks come first
+    assert call(1, B=0) == SHAPE

@@ -13,9 +13,10 @@ pytestmark = pytest.mark.gpu
 W = inputs.WORKLOADS
 
 
-def _parity(name, d, dtype, scale):
-    log("prefill parity:", name, {k: v.shape for k, v in d.items() if v is not None})
-    out, st = run_prefill(d, dtype, scale)
+def _parity(name, d, dtype, scale, inverse=None):
+    log("prefill parity:", name, "inverse", inverse,
+        {k: v.shape for k, v in d.items() if v is not None})
+    out, st = run_prefill(d, dtype, scale, inverse=inverse)
     ro, rs = oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], scale, d["state"])
     return check(name, dtype, out, ro, st, rs)
 
@@ -156,3 +157,46 @@ def test_error_writes_nothing():
     assert e.value.code == 2
     torch.cuda.synchronize()
     assert torch.all(out == 7.0) and torch.equal(st, t["state"])
+
+
+# ---------------------------------------------- Neumann-product inverse (A/B)
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_neumann_inverse_workloads(dtype):
+    """The Neumann inverse against the oracle on the small fp32 workload and
+    the S=2048 bf16 workload (shape and dtype of each), and in weak decay
+    where the inverse's off-diagonal entries are largest."""
+    import linear_attention_recurrence_chunked_amd as gdn
+    w = W["tiny_f32"] if dtype == "f32" else W["prefill_s2048"]
+    _parity("neumann " + w.name, inputs.draw_workload(w), w.dtype, w.scale,
+            inverse=gdn.GDN_INV_NEUMANN)
+    d = inputs.draw_prefill(B=1, Hk=4, Hv=8, S=1024, Dk=128, Dv=128, dtype=dtype,
+                            state="normal", decay="weak", seed=(1, 2, 0))
+    _parity("neumann weak/%s" % dtype, d, dtype, 1.0 / np.sqrt(128), inverse=gdn.GDN_INV_NEUMANN)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [
+    dict(B=1, Hk=2, Hv=2, S=64, Dk=64, Dv=64),
+    dict(B=1, Hk=2, Hv=4, S=256, Dk=80, Dv=48),
+    dict(B=1, Hk=1, Hv=2, S=320, Dk=128, Dv=16),
+])
+def test_neumann_inverse_shapes(dtype, shape):
+    import linear_attention_recurrence_chunked_amd as gdn
+    d = inputs.draw_prefill(dtype=dtype, state="normal", decay="weak", seed=(9, 2, 21), **shape)
+    _parity("neumann shape %s %s" % (dtype, shape), d, dtype, 1.0 / np.sqrt(shape["Dk"]),
+            inverse=gdn.GDN_INV_NEUMANN)
+
+
+def test_neumann_matches_substitution():
+    """Both inverse methods on the bench workload's shape (B=1 slice): the
+    outputs agree far inside the tolerance."""
+    import linear_attention_recurrence_chunked_amd as gdn
+    from gpu_helpers import rel_err
+    w = W["prefill_b4_s8192"]
+    d = inputs.draw_workload(w, B=1, S=2048)
+    o1, s1 = run_prefill(d, "bf16", w.scale)
+    o2, s2 = run_prefill(d, "bf16", w.scale, inverse=gdn.GDN_INV_NEUMANN)
+    eo, es = rel_err(o2, o1), rel_err(s2, s1)
+    log("neumann vs substitution: out %.3e state %.3e" % (eo, es))
+    assert eo < 1e-2 and es < 5e-3
