@@ -12,64 +12,89 @@
 // A stream over HBM (o and z read once, y written once). P lanes own one row
 // (P = the power of two covering its 16-byte vectors), the row's sum of
 // squares is a butterfly over those lanes, and each row moves as P
-// contiguous 16-byte vectors.
+// contiguous 16-byte vectors (kNormNR rows per thread, all loaded before any
+// is used). A workgroup's rows form a tile of HT heads x consecutive tokens
+// (HT = 4 when Hv allows): the head-major
+// reads of o then cover runs of consecutive tokens and the token-major z
+// and y runs of consecutive heads, rather than one of the two jumping by a
+// whole [S, Dv] head plane from row to row.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
 constexpr int kNormThreads = 256;
+constexpr int kNormNR = 1;          // rows per thread (2 measured slower)
 
-template <typename E, int P>
+template <typename E, int P, int HT>
 __global__ __launch_bounds__(kNormThreads) void gdn_rmsnorm_gated_kernel(
     const E* __restrict__ o, const E* __restrict__ z, const float* __restrict__ w, float eps,
-    E* __restrict__ out, int Hv, int S, int Dv, long long rows)
+    E* __restrict__ out, int Hv, int S, int Dv, int stiles)
 {
     constexpr int VE = 16 / (int)sizeof(E);
+    constexpr int RW = kNormThreads / P;               // rows per pass of the workgroup
+    constexpr int TT = kNormNR * RW / HT;              // tokens per tile
     typedef typename std::conditional<sizeof(E) == 2, bf16x8, f32x4>::type V;
-    const long long row = (long long)blockIdx.x * (kNormThreads / P) + threadIdx.x / P;
     const int li = threadIdx.x % P;
     const int c0 = li * VE;
-    const bool act = row < rows && c0 < Dv;
-    // token-major output row (b, s, h) <- head-major input row (b, h, s)
-    const long long hs = row % ((long long)S * Hv), b = row / ((long long)S * Hv);
-    const long long s = hs / Hv, h = hs % Hv;
-    const long long orow = (b * Hv + h) * S + s;
-    float ov[VE], zv[VE];
-    float ss = 0.f;
-    if (act) {
-        const V a = *(const V*)(o + orow * Dv + c0);
-        const V g = *(const V*)(z + row * Dv + c0);
+    const long long tile = blockIdx.x;
+    const long long st = tile % stiles, hb = (tile / stiles) % (Hv / HT);
+    const long long b = tile / stiles / (Hv / HT);
+    // kNormNR rows per thread, all loaded before any is used
+    V a[kNormNR], g[kNormNR];
+    long long row[kNormNR];
+    bool act[kNormNR];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            ov[e] = to_f32(a[e]);
-            zv[e] = to_f32(g[e]);
-            ss += ov[e] * ov[e];
+    for (int n = 0; n < kNormNR; ++n) {
+        const int rr = threadIdx.x / P + RW * n;       // row within the tile
+        const long long h = hb * HT + rr / TT, s = st * TT + rr % TT;
+        act[n] = s < S && c0 < Dv;
+        row[n] = (b * S + s) * Hv + h;                 // token-major z / y row
+        const long long orow = (b * Hv + h) * S + s;   // head-major o row
+        if (act[n]) {
+            a[n] = *(const V*)(o + orow * Dv + c0);
+            g[n] = *(const V*)(z + row[n] * Dv + c0);
         }
     }
 #pragma unroll
-    for (int m = 1; m < P; m <<= 1) ss += __shfl_xor(ss, m);
-    if (!act) return;
-    const float r = 1.f / sqrtf(ss / (float)Dv + eps);
-    V y;
+    for (int n = 0; n < kNormNR; ++n) {
+        float ov[VE], ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) {
-        const float gate = zv[e] / (1.f + expf(-zv[e]));
-        y[e] = from_f32<E>(ov[e] * r * w[c0 + e] * gate);
+        for (int e = 0; e < VE; ++e) {
+            ov[e] = act[n] ? to_f32(a[n][e]) : 0.f;
+            ss += ov[e] * ov[e];
+        }
+#pragma unroll
+        for (int m = 1; m < P; m <<= 1) ss += __shfl_xor(ss, m);
+        if (!act[n]) continue;
+        const float r = 1.f / sqrtf(ss / (float)Dv + eps);
+        V y;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            const float zz = to_f32(g[n][e]);
+            y[e] = from_f32<E>(ov[e] * r * w[c0 + e] * (zz / (1.f + expf(-zz))));
+        }
+        *(V*)(out + row[n] * Dv + c0) = y;
     }
-    *(V*)(out + row * Dv + c0) = y;
+}
+
+template <typename E, int P, int HT>
+static hipError_t norm_ph(const NormArgs& a, hipStream_t st)
+{
+    constexpr int TT = kNormNR * kNormThreads / P / HT;
+    const int stiles = (a.S + TT - 1) / TT;
+    const long long blocks = (long long)a.B * (a.Hv / HT) * stiles;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gdn_rmsnorm_gated_kernel<E, P, HT>), dim3((unsigned)blocks),
+                       dim3(kNormThreads), 0, st, (const E*)a.o, (const E*)a.z, a.w, a.eps,
+                       (E*)a.out, a.Hv, a.S, a.Dv, stiles);
+    return hipGetLastError();
 }
 
 template <typename E, int P>
 static hipError_t norm_p(const NormArgs& a, hipStream_t st)
 {
-    const long long rows = (long long)a.B * a.S * a.Hv;
-    const long long blocks = (rows + kNormThreads / P - 1) / (kNormThreads / P);
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gdn_rmsnorm_gated_kernel<E, P>), dim3((unsigned)blocks),
-                       dim3(kNormThreads), 0, st, (const E*)a.o, (const E*)a.z, a.w, a.eps,
-                       (E*)a.out, a.Hv, a.S, a.Dv, rows);
-    return hipGetLastError();
+    return a.Hv % 4 == 0 ? norm_ph<E, P, 4>(a, st) : norm_ph<E, P, 1>(a, st);
 }
 
 template <typename E>
