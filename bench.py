@@ -191,6 +191,7 @@ def bench_decode(torch, gdn, w, state0, steps, reps, warmup, gated=False):
     stream = torch.cuda.current_stream(dev)
 
     def run64(evs=None):
+        stream = torch.cuda.current_stream(dev)      # the capture stream while capturing
         for i, s in enumerate(dev_steps):
             if evs is not None:
                 evs[i][0].record(stream)
@@ -215,7 +216,24 @@ def bench_decode(torch, gdn, w, state0, steps, reps, warmup, gated=False):
     n = reps * len(dev_steps)
     kern_ms = float(np.mean([a.elapsed_time(b) for e in evs for a, b in e]))
     ms_step = (t1 - t0) * 1e3 / n
-    return ms_step, kern_ms, decode_algorithmic(w.B, w.Hk, w.Hv, w.Dk, w.Dv)
+    # the same passes replayed from a HIP graph captured once (no launch gaps)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        run64()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run64()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / n
+    return ms_step, kern_ms, decode_algorithmic(w.B, w.Hk, w.Hv, w.Dk, w.Dv), graph_ms
 
 
 def conv_algorithmic(B, C, T, K, esize=2):
@@ -450,8 +468,8 @@ def main():
     w = inputs.WORKLOADS["prefill_b4_s8192"]
     if args.only in ("decode", "decode_gated"):
         dstate0, dsteps = inputs.draw_decode_steps(dw, raw=True)
-        dms, dkern_ms, dbytes = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm,
-                                             gated=args.only == "decode_gated")
+        dms, dkern_ms, dbytes, _ = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm,
+                                                gated=args.only == "decode_gated")
         print(json.dumps({args.only + "_ms_per_step": dms, "kernel_ms": dkern_ms,
                           "GB_s": dbytes / (dkern_ms / 1e3) / 1e9}), flush=True)
         return
@@ -488,8 +506,9 @@ def main():
     # steady clocks, and the decode passes (with their own warm-up) supply it
     # before the prefill's warm-up steps.
     dstate0, dsteps = inputs.draw_decode_steps(dw, raw=True)
-    dms, dkern_ms, dbytes = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm)
-    gdms, gdkern_ms, _ = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm, gated=True)
+    dms, dkern_ms, dbytes, dgraph_ms = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm)
+    gdms, gdkern_ms, _, gdgraph_ms = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm,
+                                                  gated=True)
     d = inputs.draw_workload(w, raw=True)
     ms_step, kern_ms, nbytes, flops = bench_prefill(torch, gdn, w, d, args.steps, args.warmup)
     gms_step, gkern_ms, _, _ = bench_prefill(torch, gdn, w, d, args.steps, args.warmup,
@@ -531,6 +550,8 @@ def main():
         "decode": {"workload": "decode_b256", "B": dw.B, "Hk": dw.Hk, "Hv": dw.Hv,
                    "value": 1e3 / dms, "unit": "steps/s", "ms_per_step": dms,
                    "tokens_per_s": dw.B * 1e3 / dms,
+                   "graph": {"value": 1e3 / dgraph_ms, "ms_per_step": dgraph_ms,
+                             "note": "the 64-step pass captured once in a HIP graph and replayed"},
                    "roofline": dict(bound="hbm", kernel="gdn_decode_kernel",
                                     traffic=measured_traffic("gdn_decode_kernel"),
                                     **hbm(dbytes, dkern_ms))},
@@ -542,6 +563,7 @@ def main():
                                            **hbm(nbytes, gkern_ms))},
         "decode_gated": {"workload": "decode_b256 (raw q/k, a, b, A_log, dt_bias)",
                          "value": 1e3 / gdms, "unit": "steps/s", "ms_per_step": gdms,
+                         "graph": {"value": 1e3 / gdgraph_ms, "ms_per_step": gdgraph_ms},
                          "l2_eps": L2_EPS,
                          "roofline": dict(bound="hbm", kernel="gdn_decode_kernel (gated)",
                                           traffic=measured_traffic("gdn_decode_kernel_gated"),
