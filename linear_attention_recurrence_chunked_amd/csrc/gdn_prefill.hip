@@ -29,18 +29,22 @@
 //    registers as the B operand), R, U = T R, O = e^gamma Q S0 + P U and the
 //    state update K^T (dl U) -- every intermediate stays in registers; LDS is
 //    only read for K, Q, V, T and P of the chunk;
-//  * the inverse wave builds T = (I + A)^{-1} for chunk i+1 (fp32: 16x16
-//    diagonal blocks by forward substitution, one lane per column, then the
-//    merge T21 = -T22 (A21 T11) on fp32 MFMA);
+//  * two inverse waves build T = (I + A)^{-1}, taking alternate chunks and
+//    spreading a chunk over two steps: fp32 forward substitution of the two
+//    16x16 diagonal blocks for chunk i+2 (one lane per column), then the
+//    merge T21 = -T22 (A21 T11) on fp32 MFMA and the stores for chunk i+1;
+//  * the A wave builds A = diag(beta) (K K^T) (.) Mstrict for chunk i+3;
 //  * the P wave builds P = Q K^T (.) Mincl for chunk i+1;
-//  * two stager waves load chunk i+LEAD from HBM and store it into LDS (with
-//    gamma and the per-token decay scalars); the HBM latency is spent inside
-//    their own step, off the sequential path. On the bf16 path the P wave
-//    also builds A = diag(beta) (K K^T) (.) Mstrict for chunk i+2 (on the
-//    fp32 path the inverse wave builds A).
+//  * two stager waves (K with g and beta; Q with V) issue the loads of chunk
+//    i+LEAD+1 and store chunk i+LEAD (loaded a step earlier) into LDS, with
+//    gamma and the per-token decay scalars; the HBM latency passes during
+//    the rest of the step, off the sequential path.
+// On the fp32 path (tiles twice as large) one inverse wave builds A and T of
+// chunk i+1 in one step and the stagers run LEAD = 2 ahead.
 //
-// LDS holds the input slots of chunks i .. i+LEAD (4 on the bf16 path, 3 on
-// the fp32 path, whose tiles are twice as large) and two T/P buffers.
+// LDS holds the input slots of chunks i .. i+LEAD (5 on the bf16 path, 3 on
+// the fp32 path), three T, two P and three A buffers (two T, two P, one A on
+// the fp32 path).
 // The state-independent work of a chunk therefore never sits on the
 // sequential path. HBM traffic is the algorithmic minimum: q, k, v, g, beta
 // read once per slice, out written once, the state read and written once.
