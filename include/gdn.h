@@ -54,7 +54,7 @@ typedef enum {
 typedef enum {
     GDN_OK = 0,
     GDN_ERR_NULL = 1,         /* a required pointer is NULL                          */
-    GDN_ERR_SHAPE = 2,        /* B, Hk, Hv, S < 1, Hv % Hk != 0, S % 64 != 0 (prefill) */
+    GDN_ERR_SHAPE = 2,        /* B, Hk, Hv, S < 1, Hv % Hk != 0, or a size overflow   */
     GDN_ERR_UNSUPPORTED = 3,  /* Dk or Dv outside [16, 128] or not a multiple of 16;  *
                                * conv1d window K > 8                                 */
     GDN_ERR_DTYPE = 4,        /* dtype is not a gdn_dtype value                       */
@@ -87,7 +87,10 @@ typedef void* gdn_stream;
  *               gdn_chunked_prefill_workspace_bytes(...) bytes; may be NULL
  *               when that size is 0
  *
- * Constraints: Hv % Hk == 0; S % 64 == 0 (the chunk length); 16 <= Dk, Dv
+ * Constraints: Hv % Hk == 0; any S >= 1 (the page asks S to be a multiple
+ * of its chunk length; a partial last chunk is extended exactly here, as if
+ * padded with tokens of g = beta = 0 and k = q = v = 0, whose outputs are
+ * dropped); 16 <= Dk, Dv
  * <= 128, multiples of 16 (the pages' MAX_HEAD_DIM = 128, Notes); all
  * pointers 16-byte aligned; out and state_inout must not overlap each other
  * or any input. The result is deterministic run to run.

@@ -12,7 +12,6 @@
 
 namespace {
 
-constexpr int kChunk = 64;        // prefill chunk length (tokens)
 constexpr int kMaxConvTaps = 8;   // conv1d window width the kernels support
 constexpr int kMaxHeadDim = 128;  // Dk, Dv upper bound ("GDN CTE", Notes)
 
@@ -53,7 +52,6 @@ gdn_status validate(const Common& c, bool prefill) {
     if (c.dtype != GDN_F32 && c.dtype != GDN_BF16) return GDN_ERR_DTYPE;
     if (c.B < 1 || c.Hk < 1 || c.Hv < 1 || c.S < 1) return GDN_ERR_SHAPE;
     if (c.Hv % c.Hk != 0) return GDN_ERR_SHAPE;
-    if (prefill && c.S % kChunk != 0) return GDN_ERR_SHAPE;
     if ((int64_t)c.B * c.Hv > INT32_MAX) return GDN_ERR_SHAPE;
     if (c.Dk < 16 || c.Dk > kMaxHeadDim || c.Dk % 16 != 0) return GDN_ERR_UNSUPPORTED;
     if (c.Dv < 16 || c.Dv > kMaxHeadDim || c.Dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
@@ -318,7 +316,7 @@ const char* gdn_status_string(int status) {
     switch (status) {
         case GDN_OK: return "ok";
         case GDN_ERR_NULL: return "a required pointer is NULL";
-        case GDN_ERR_SHAPE: return "invalid shape (sizes < 1, Hv % Hk != 0, S % 64 != 0, or overflow)";
+        case GDN_ERR_SHAPE: return "invalid shape (sizes < 1, Hv % Hk != 0, or overflow)";
         case GDN_ERR_UNSUPPORTED: return "unsupported size (Dk, Dv must be multiples of 16 in [16, 128]; conv taps K <= 8)";
         case GDN_ERR_DTYPE: return "invalid dtype";
         case GDN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";

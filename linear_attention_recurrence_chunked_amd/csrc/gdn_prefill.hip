@@ -242,7 +242,11 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     const float* bb = beta + bh * (size_t)S;
     E* ob = out + bh * (size_t)S * Dv + v0;
     float* sb = state + bh * (size_t)Dk * Dv + v0;
-    const int NC = S / C;
+    // Any S >= 1: the last chunk may be partial. Its missing tokens read as
+    // zeros (k = q = v = 0, g = beta = 0: the range check of the buffer loads
+    // below), which leave the state unchanged and touch no real token's
+    // output; their outputs are not stored.
+    const int NC = (S + C - 1) / C;
 
     auto slot_ptr = [&](int c) { return smem + Cf::OFF_SLOTS + (c % Cf::NSLOT) * Cf::SZ_SLOT; };
 
@@ -253,10 +257,13 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // step, so no staging registers stay live across the barrier (the
     // register file is shared by all roles).
     // Global loads are buffer loads: a buffer resource per stream (scalar
-    // registers), a uniform row offset (scalar) and a 32-bit lane offset
-    // computed once, clamped in bounds (Dk < DK). No per-load address
-    // registers, no branches: the store that follows a step later waits only
-    // for its own loads. Vectors past a ragged edge are zeroed when stored.
+    // registers) whose size is the stream's extent, and a 32-bit lane offset
+    // (the lane's column, clamped in bounds when Dk < DK, plus the row). The
+    // row goes into the lane offset, not the scalar offset, so the hardware
+    // range check covers it: rows past the end of the sequence read as zero
+    // without touching memory. No branches: the store that follows a step
+    // later waits only for its own loads. Vectors past a ragged Dk or Dv edge
+    // are zeroed when stored.
     constexpr int KPR = DK / VE;                 // 16-byte vectors per K/Q row
     constexpr int KRI = 64 / KPR;                // rows per load instruction
     const bool kfull = Dk == DK;
@@ -269,7 +276,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
         for (int n = 0; n < Cf::NVK; ++n)
             r[n] = __builtin_bit_cast(VecE, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rs, koff, (c0 + KRI * n) * Dk * Cf::ES, 0));
+                                                rs, koff + (uint32_t)((c0 + KRI * n) * Dk * Cf::ES), 0, 0));
     };
     auto store_rows = [&](VecE (&r)[Cf::NVK], E* dst) __attribute__((always_inline)) {
         if (!kfull) {                            // uniform: only with a ragged key dimension
@@ -289,8 +296,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)bb, (short)0, S * 4, kBufDword3);
     auto stage_k_load = [&](int c, KRegs& R) __attribute__((always_inline)) {
         load_rows(R.k, rs_k, c * C);
-        R.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_g, goff, c * C * 4, 0));
-        R.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_b, goff, c * C * 4, 0));
+        R.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_g, goff + (uint32_t)(c * C * 4), 0, 0));
+        R.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_b, goff + (uint32_t)(c * C * 4), 0, 0));
     };
     auto stage_k_store = [&](int c, KRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
@@ -299,8 +306,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         float* sc = (float*)(slot + Cf::OFF_SSC);
         float gl = R.g, be = R.b;
         if constexpr (GATED) {
-            gl = -expA * softplus_f(R.g + dtb);
-            be = __builtin_amdgcn_rcpf(1.f + __expf(-R.b));
+            // the gates of missing tokens past the end of the sequence are 0
+            const bool real = c * C + l < S;
+            gl = real ? -expA * softplus_f(R.g + dtb) : 0.f;
+            be = real ? __builtin_amdgcn_rcpf(1.f + __expf(-R.b)) : 0.f;
         }
         float x = l < C ? gl : 0.f;
 #pragma unroll
@@ -333,7 +342,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
         for (int n = 0; n < Cf::NVV; ++n)
             R.v[n] = __builtin_bit_cast(VecE, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rs_v, voff, (c0 + VRI * n) * Dv * Cf::ES, 0));
+                                                  rs_v, voff + (uint32_t)((c0 + VRI * n) * Dv * Cf::ES), 0, 0));
     };
     auto stage_qv_store = [&](int c, QVRegs& R) __attribute__((always_inline)) {
         char* slot = slot_ptr(c);
@@ -376,11 +385,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // of a chunk), dst[t] = 1/sqrt(|x_t|^2 + eps) for the 32 tokens. Lane
     // (lr/4, lc) holds rows lr + e, column lc, so the lanes with lc / 4 == lr / 4
     // hold the diagonal, in element lc % 4.
-    auto diag_norms = [&](const f32x4 (&d)[2], float* dst) __attribute__((always_inline)) {
+    // Tokens past the end of the sequence (t >= nreal) get the factor 0: their
+    // rows are zero, and 1/sqrt(0 + eps) could be infinite.
+    auto diag_norms = [&](const f32x4 (&d)[2], float* dst, int nreal) __attribute__((always_inline)) {
         if ((lc >> 2) == (lr >> 2)) {
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
-                dst[16 * ti + lc] = __builtin_amdgcn_rsqf(pick4(d[ti], lc & 3) + l2_eps);
+                dst[16 * ti + lc] = 16 * ti + lc < nreal
+                                        ? __builtin_amdgcn_rsqf(pick4(d[ti], lc & 3) + l2_eps) : 0.f;
         }
         // Later reads of dst by other lanes of this wave: LDS accesses of a
         // wave complete in program order, so only the compiler must keep them
@@ -411,7 +423,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
         if constexpr (GATED) {
             const f32x4 dg[2] = {acc3[0], acc3[2]};
-            diag_norms(dg, sc + Cf::SC_RK);
+            diag_norms(dg, sc + Cf::SC_RK, S - c * C);
             if (l < C) {
                 const float rk = sc[Cf::SC_RK + l];
                 sc[Cf::SC_BK + l] *= rk;
@@ -684,14 +696,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                 for (int m = 0; m < NKS; ++m) dq[ti] = O::mma(qf[ti][m], qf[ti][m], dq[ti]);
-            diag_norms(dq, sc + Cf::SC_RQ);
+            diag_norms(dq, sc + Cf::SC_RQ, S - c * C);
             if constexpr (!Cf::SPREAD) {
                 f32x4 dk[2] = {zero4(), zero4()};
 #pragma unroll
                 for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                     for (int m = 0; m < NKS; ++m) dk[ti] = O::mma(kf[ti][m], kf[ti][m], dk[ti]);
-                diag_norms(dk, sc + Cf::SC_RKP);
+                diag_norms(dk, sc + Cf::SC_RKP, S - c * C);
             }
             if (l < C) sc[Cf::SC_EG + l] *= sc[Cf::SC_RQ + l];
         }
@@ -851,7 +863,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 o = O::mma(ul, pf[ti][0], o);
             }
             o = O::mma(uh, pf[ti][0], o);
-            if (wok) {
+            if (wok && c0 + 16 * ti + lc < S) {         // tokens past the end are not stored
                 E* dst = ob + (size_t)(c0 + 16 * ti + lc) * Dv + 16 * wave + lr;
                 if constexpr (SP) {
                     *(bf16x4*)dst = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};

@@ -120,10 +120,17 @@ def test_bad_shape(lib, which, kw):
     assert CALLS[which](lib, **kw) == SHAPE
 
 
-@pytest.mark.parametrize("S", [0, 1, 63, 65, 100, 8191])
-def test_prefill_sequence_length_multiple_of_chunk(lib, S):
+@pytest.mark.parametrize("S", [0, -1, -64])
+def test_prefill_sequence_length_positive(lib, S):
     assert prefill(lib, S=S) == SHAPE
     assert prefill_gated(lib, S=S) == SHAPE
+
+
+@pytest.mark.parametrize("S", [1, 63, 65, 100, 8191])
+def test_prefill_any_sequence_length_accepted(lib, S):
+    # any S >= 1 passes the shape checks (the bad dtype is what fails here)
+    assert prefill(lib, S=S, dtype=9) == DTYPE
+    assert prefill_gated(lib, S=S, dtype=9) == DTYPE
 
 
 @pytest.mark.parametrize("which", sorted(GATED))

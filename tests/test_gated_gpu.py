@@ -198,3 +198,14 @@ def test_gated_error_writes_nothing():
     assert e.value.code == 9
     torch.cuda.synchronize()
     assert torch.all(out == 7.0) and torch.equal(st, t["state"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("eps", [1e-6, 0.0])
+def test_gated_ragged_sequence_length(dtype, eps):
+    """A partial last chunk with the prologue on the device: the missing
+    tokens' gates are zero and their (zero) rows get no norm factor, also
+    with eps = 0."""
+    d = inputs.draw_prefill(B=1, Hk=2, Hv=4, S=71, Dk=128, Dv=64, dtype=dtype, state="normal",
+                            seed=(9, 4, 71), raw=True)
+    _parity("gated ragged S=71 %s eps=%g" % (dtype, eps), d, dtype, 0.125, eps=eps)

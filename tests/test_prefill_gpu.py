@@ -144,17 +144,17 @@ def test_decode_iterated_matches_prefill():
 
 
 def test_error_writes_nothing():
-    """An invalid call (S not a multiple of 64) leaves out and state untouched."""
+    """An invalid call (Dk = 72, not a multiple of 16) leaves out and state untouched."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=1, Hk=1, Hv=1, S=96, Dk=64, Dv=64, dtype="bf16",
+    d = inputs.draw_prefill(B=1, Hk=1, Hv=1, S=96, Dk=72, Dv=64, dtype="bf16",
                             state="normal", seed=(9, 0, 7))
     t = upload(d, "bf16")
     out = torch.full((1, 1, 96, 64), 7.0, dtype=torch.bfloat16, device="cuda")
     st = t["state"].clone()
     with pytest.raises(gdn.GdnError) as e:
         gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], 0.1, st, out=out)
-    assert e.value.code == 2
+    assert e.value.code == 3
     torch.cuda.synchronize()
     assert torch.all(out == 7.0) and torch.equal(st, t["state"])
 
@@ -200,3 +200,60 @@ def test_neumann_matches_substitution():
     eo, es = rel_err(o2, o1), rel_err(s2, s1)
     log("neumann vs substitution: out %.3e state %.3e" % (eo, es))
     assert eo < 1e-2 and es < 5e-3
+
+
+# ------------------------------------------------- sequence lengths of any size
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("S", [1, 5, 31, 33, 100, 1000])
+def test_ragged_sequence_length(dtype, S):
+    """A partial last chunk (S not a multiple of the 32-token chunk): exact,
+    no output past S, state as the oracle's."""
+    d = inputs.draw_prefill(B=2, Hk=2, Hv=4, S=S, Dk=128, Dv=128, dtype=dtype, state="normal",
+                            decay="weak", seed=(9, 3, S))
+    _parity("ragged S=%d %s" % (S, dtype), d, dtype, 1.0 / np.sqrt(128))
+
+
+def test_ragged_neumann_and_shapes():
+    import linear_attention_recurrence_chunked_amd as gdn
+    d = inputs.draw_prefill(B=1, Hk=2, Hv=4, S=77, Dk=80, Dv=48, dtype="bf16", state="normal",
+                            decay="weak", seed=(9, 3, 77))
+    _parity("ragged neumann S=77", d, "bf16", 0.1, inverse=gdn.GDN_INV_NEUMANN)
+    _parity("ragged S=77 Dk=80 Dv=48", d, "bf16", 0.1)
+
+
+def test_ragged_out_untouched_past_end():
+    """Nothing is written past the last token: out sits at the front of a
+    larger buffer filled with a marker, which must survive the call."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    d = inputs.draw_prefill(B=1, Hk=1, Hv=2, S=45, Dk=64, Dv=64, dtype="bf16", state="normal",
+                            seed=(9, 3, 45))
+    t = upload(d, "bf16")
+    n = 1 * 2 * 45 * 64
+    buf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[:n].view(1, 2, 45, 64)
+    gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], 0.1, t["state"], out=out)
+    torch.cuda.synchronize()
+    ro, rs = oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], 0.1, d["state"])
+    check("ragged S=45", "bf16", to_np(out), ro, to_np(t["state"]), rs)
+    assert torch.all(buf[n:] == 7.0)
+
+
+def test_ragged_split_carry_matches_oracle():
+    """prefill(100) then prefill(284) from the carried state matches the
+    oracle over all 384 tokens (chunk boundaries differ from one call of 384)."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    d = inputs.draw_prefill(B=2, Hk=2, Hv=4, S=384, Dk=128, Dv=128, dtype="bf16",
+                            state="normal", decay="weak", seed=(9, 3, 384))
+    t = upload(d, "bf16")
+    st = t["state"].clone()
+    sl = lambda x, a, b: x[:, :, a:b].contiguous()
+    o1 = gdn.chunked_prefill(sl(t["q"], 0, 100), sl(t["k"], 0, 100), sl(t["v"], 0, 100),
+                             sl(t["g_log"], 0, 100), sl(t["beta"], 0, 100), 0.1, st)
+    o2 = gdn.chunked_prefill(sl(t["q"], 100, 384), sl(t["k"], 100, 384), sl(t["v"], 100, 384),
+                             sl(t["g_log"], 100, 384), sl(t["beta"], 100, 384), 0.1, st)
+    torch.cuda.synchronize()
+    ro, rs = oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], 0.1, d["state"])
+    check("ragged split 100+284", "bf16", to_np(torch.cat([o1, o2], dim=2)), ro, to_np(st), rs)
