@@ -87,13 +87,13 @@ typedef void* gdn_stream;
  *               gdn_chunked_prefill_workspace_bytes(...) bytes; may be NULL
  *               when that size is 0
  *
- * Constraints: Hv % Hk == 0; any S >= 1 (the page asks S to be a multiple
- * of its chunk length; a partial last chunk is extended exactly here, as if
- * padded with tokens of g = beta = 0 and k = q = v = 0, whose outputs are
- * dropped); 16 <= Dk, Dv
- * <= 128, multiples of 16 (the pages' MAX_HEAD_DIM = 128, Notes); all
- * pointers 16-byte aligned; out and state_inout must not overlap each other
- * or any input. The result is deterministic run to run.
+ * Constraints: Hv % Hk == 0; 1 <= S <= 4194239 (byte offsets within one
+ * (batch, head) stream are 32-bit). The page asks S to be a multiple of its
+ * chunk length; here a partial last chunk is extended exactly, as if padded
+ * with tokens of g = beta = 0 and k = q = v = 0 whose outputs are dropped.
+ * 16 <= Dk, Dv <= 128, multiples of 16 (the pages' MAX_HEAD_DIM = 128,
+ * Notes); all pointers 16-byte aligned; out and state_inout must not overlap
+ * each other or any input. The result is deterministic run to run.
  */
 gdn_status gdn_chunked_prefill(const void* q, const void* k, const void* v,
                                const float* g_log, const float* beta, float scale,

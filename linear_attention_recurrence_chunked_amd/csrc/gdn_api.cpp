@@ -53,6 +53,9 @@ gdn_status validate(const Common& c, bool prefill) {
     if (c.B < 1 || c.Hk < 1 || c.Hv < 1 || c.S < 1) return GDN_ERR_SHAPE;
     if (c.Hv % c.Hk != 0) return GDN_ERR_SHAPE;
     if ((int64_t)c.B * c.Hv > INT32_MAX) return GDN_ERR_SHAPE;
+    // the prefill addresses one (batch, head) stream of S rows with 32-bit
+    // byte offsets: S * max(Dk, Dv) elements (plus a chunk) must fit
+    if (prefill && ((int64_t)c.S + 64) * 128 * 4 > INT32_MAX) return GDN_ERR_SHAPE;
     if (c.Dk < 16 || c.Dk > kMaxHeadDim || c.Dk % 16 != 0) return GDN_ERR_UNSUPPORTED;
     if (c.Dv < 16 || c.Dv > kMaxHeadDim || c.Dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
     const void* ptrs[] = {c.q, c.k, c.v, c.g, c.beta, c.state, c.out};

@@ -327,3 +327,9 @@ def test_inverse_method_values(lib):
         assert call(bad) == VALUE
     assert call(1, dtype=3) == DTYPE            # shape/dtype checks come first
     assert call(1, B=0) == SHAPE
+
+
+def test_prefill_longest_sequence(lib):
+    # byte offsets within a (batch, head) stream are 32-bit
+    assert prefill(lib, B=1, S=4194240, dtype=9) == SHAPE
+    assert prefill(lib, B=1, S=4194239, dtype=9) == DTYPE
