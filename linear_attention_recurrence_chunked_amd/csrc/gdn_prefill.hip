@@ -139,7 +139,7 @@ struct PipeCfg {
     // LDS layout (bytes)
     static constexpr int SZ_K = C * LDK * ES;
     static constexpr int SZ_V = C * LDV * ES;
-    static constexpr int SZ_SC = (8 * C + 4) * 4;
+    static constexpr int SZ_SC = (9 * C + 4) * 4;
     static constexpr int OFF_SK = 0, OFF_SQ = SZ_K, OFF_SV = 2 * SZ_K, OFF_SSC = 2 * SZ_K + SZ_V;
     static constexpr int SZ_SLOT = 2 * SZ_K + SZ_V + SZ_SC;
     static constexpr int SZ_TP = C * LDP * ES;
@@ -159,12 +159,14 @@ struct PipeCfg {
     static constexpr int OFF_P = OFF_T + NTBUF * SZ_TP;
     static constexpr int OFF_SLOTS = OFF_P + 2 * SZ_TP;
     static constexpr int LDS_BYTES = OFF_SLOTS + NSLOT * SZ_SLOT;
-    // scalar arrays inside a slot (floats): gamma, scale e^gamma, beta, beta e^gamma,
+    // scalar arrays inside a slot (floats): gamma (its fp32 value and, in SC_GAML,
+    // the rest gamma - fp32(gamma)), scale e^gamma, beta, beta e^gamma,
     // e^{gamma_C - gamma}, [0] = e^{gamma_C}; on the GATED path rk (A builder), rq and
-    // the P wave's own rk (P wave), and the second, third and fifth arrays carry the
+    // the P wave's own rk (P wave), and the second, fourth and fifth arrays carry the
     // factors rq, rk, rk once the A builder and the P wave have folded them in.
     static constexpr int SC_GAM = 0, SC_EG = C, SC_B = 2 * C, SC_BK = 3 * C, SC_DL = 4 * C,
-                         SC_RK = 5 * C, SC_RQ = 6 * C, SC_RKP = 7 * C, SC_EGC = 8 * C;
+                         SC_RK = 5 * C, SC_RQ = 6 * C, SC_RKP = 7 * C, SC_GAML = 8 * C,
+                         SC_EGC = 9 * C;
 
     static_assert(C == 32, "the pipeline is laid out for 32-token chunks");
     static_assert(DK % 32 == 0 && BV % 16 == 0 && BV <= 64, "tile sizes");
@@ -311,22 +313,29 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             gl = real ? -expA * softplus_f(R.g + dtb) : 0.f;
             be = real ? __builtin_amdgcn_rcpf(1.f + __expf(-R.b)) : 0.f;
         }
-        float x = l < C ? gl : 0.f;
+        // The prefix sum runs in fp64: with strong decay gamma reaches thousands
+        // within a chunk, where an fp32 sum would lose ~1e-4 absolute, and the
+        // decay between close tokens is a difference of two such sums. gamma
+        // is kept as an fp32 pair (value, rest); e^{gamma_C - gamma} comes from
+        // the fp64 difference.
+        double xd = l < C ? (double)gl : 0.0;
 #pragma unroll
         for (int off = 1; off < C; off <<= 1) {
-            const float y = __shfl_up(x, off);
-            if (l >= off) x += y;
+            const double y = __shfl_up(xd, off);
+            if (l >= off) xd += y;
         }
-        const float gC = __shfl(x, C - 1);
+        const double gCd = __shfl(xd, C - 1);
+        const float x = (float)xd;
         if (l < C) {
             const float eg = __expf(x);
             sc[Cf::SC_GAM + l] = x;
+            sc[Cf::SC_GAML + l] = (float)(xd - (double)x);
             sc[Cf::SC_EG + l] = scale * eg;
             sc[Cf::SC_B + l] = be;
             sc[Cf::SC_BK + l] = be * eg;
-            sc[Cf::SC_DL + l] = __expf(gC - x);   // gC <= x: never overflows
+            sc[Cf::SC_DL + l] = __expf((float)(gCd - xd));   // gamma_C <= gamma: never overflows
         }
-        if (l == 0) sc[Cf::SC_EGC] = __expf(gC);
+        if (l == 0) sc[Cf::SC_EGC] = __expf((float)gCd);
     };
     constexpr int VPR = BV / VE;                 // 16-byte vectors per V row of the slice
     constexpr int VRI = 64 / VPR;
@@ -364,18 +373,22 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // (16 tj + lc) of the three lower 16x16 tiles of a chunk, read once: the
     // row factor is the product of scalar arrays `rowf` and `rowf2`, the
     // column factor scalar array `colf` (each omitted when < 0).
-    struct TileScalars { float gr[2][4], br[2][4], gs[2], cs[2]; };
+    // gamma_r - gamma_s = (gr - gs) + (grl - gsl): the fp32 values' difference
+    // (exact when close, else rounded relative to itself) plus the rests.
+    struct TileScalars { float gr[2][4], grl[2][4], br[2][4], gs[2], gsl[2], cs[2]; };
     auto tile_scalars = [&](const float* sc, int rowf, int rowf2, int colf)
         __attribute__((always_inline)) {
         TileScalars ts;
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
             ts.gs[ti] = sc[Cf::SC_GAM + 16 * ti + lc];
+            ts.gsl[ti] = sc[Cf::SC_GAML + 16 * ti + lc];
             ts.cs[ti] = colf >= 0 ? sc[colf + 16 * ti + lc] : 1.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * ti + lr + e;
                 ts.gr[ti][e] = sc[Cf::SC_GAM + t];
+                ts.grl[ti][e] = sc[Cf::SC_GAML + t];
                 ts.br[ti][e] = (rowf >= 0 ? sc[rowf + t] : 1.f) * (rowf2 >= 0 ? sc[rowf2 + t] : 1.f);
             }
         }
@@ -436,17 +449,17 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         f32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {   // A11, stored transposed: [s][r], one vector per lane
-            const float dec = __expf(ts.gr[0][e] - ts.gs[0]) * ts.cs[0];
+            const float dec = __expf((ts.gr[0][e] - ts.gs[0]) + (ts.grl[0][e] - ts.gsl[0])) * ts.cs[0];
             w[e] = (lc < lr + e) ? ts.br[0][e] * dec * acc3[0][e] : 0.f;
         }
         *(f32x4*)(sA + Cf::AB_11T + lc * ALD + lr) = w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // A21 row-major: [r][s]
-            const float d21 = __expf(ts.gr[1][e] - ts.gs[0]) * ts.cs[0];
+            const float d21 = __expf((ts.gr[1][e] - ts.gs[0]) + (ts.grl[1][e] - ts.gsl[0])) * ts.cs[0];
             sA[Cf::AB_21 + (lr + e) * ALD + lc] = ts.br[1][e] * d21 * acc3[1][e];
             // A22 reversed: entry [15 - r][15 - s]
-            const float d22 = __expf(ts.gr[1][e] - ts.gs[1]) * ts.cs[1];
+            const float d22 = __expf((ts.gr[1][e] - ts.gs[1]) + (ts.grl[1][e] - ts.gsl[1])) * ts.cs[1];
             sA[Cf::AB_22R + (15 - lr - e) * ALD + 15 - lc] =
                 (lc < lr + e) ? ts.br[1][e] * d22 * acc3[2][e] : 0.f;
         }
@@ -718,7 +731,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * ti + lr + e;
-                const float dec = __expf(ts.gr[ti][e] - ts.gs[tj]) * (ts.br[ti][e] * ts.cs[tj]);
+                const float dec = __expf((ts.gr[ti][e] - ts.gs[tj]) + (ts.grl[ti][e] - ts.gsl[tj])) *
+                                  (ts.br[ti][e] * ts.cs[tj]);
                 store_pair<SP>(Pp + r * LDP + tpos(s), C, (s <= r) ? scale * dec * acc[e] : 0.f);
             }
         }
