@@ -56,6 +56,28 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// 32-bit LDS byte address of a generic pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+
+// Hides the value of a per-lane LDS base address from the optimiser, so that
+// reads at base + compile-time constant keep the constant in the
+// instruction's immediate offset instead of hoisting one base + constant
+// register per read out of the enclosing loop.
+__device__ __forceinline__ uint32_t opaque_base(uint32_t a) {
+    asm volatile("" : "+v"(a));
+    return a;
+}
+
+// Typed LDS pointer at a 32-bit byte address.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds_ptr(uint32_t a) {
+    return (__attribute__((address_space(3))) T*)(lds_char*)(uintptr_t)a;
+}
+
 // Wave-local ordering of LDS accesses (no cross-wave barrier).
 __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
@@ -100,6 +122,29 @@ template <> struct Op<bf16> {
         const bf16x4 b = lds_read_tr(p + 16 * ld);
         return F{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
+    // ldc in two parts: the lane's byte offset, and the read of the fragment
+    // at rows r0.., columns k0.. from base = buffer address + that offset.
+    __device__ __forceinline__ static uint32_t ldc_lane(int ld) {
+        const int l = lane_id();
+        return (uint32_t)(((l & 15) * ld + 8 * (l >> 4)) * 2);
+    }
+    __device__ __forceinline__ static F ldc_at(uint32_t base, int ld, int r0, int k0) {
+        return *lds_ptr<const F>(base + (uint32_t)((r0 * ld + k0) * 2));
+    }
+    // ldt in two parts: the lane's byte offset (the same for every tile kt),
+    // and the read of tile kt at base = buffer address + that offset.
+    __device__ __forceinline__ static uint32_t ldt_lane(int ld, int k0) {
+        const int l = lane_id(), g = l >> 4, j = l & 15;
+        return (uint32_t)(((k0 + 4 * g + (j >> 2)) * ld + 8 * (j & 3)) * 2);
+    }
+    __device__ __forceinline__ static F ldt_at(uint32_t base, int ld, int kt) {
+        const lds_char* p = (const lds_char*)(uintptr_t)base + (32 * (kt >> 1) + 4 * (kt & 1)) * 2;
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+        const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(p + 16 * ld * 2));
+        const bf16x4 x = __builtin_bit_cast(bf16x4, a), y = __builtin_bit_cast(bf16x4, b);
+        return F{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    }
     // B fragment from two accumulator tiles (k block 0 = x0 rows, block 1 = x1 rows).
     __device__ __forceinline__ static void split(f32x4 x0, f32x4 x1, F& hi, F& lo) {
         uint32_t h0, h1, h2, h3, w0, w1, w2, w3;
@@ -133,6 +178,33 @@ template <> struct Op<float> {
     __device__ __forceinline__ static F ldt(const float* X, int ld, int kt, int k0) {
         const int l = lane_id(), j = l & 15;
         const float* p = X + (k0 + 4 * (l >> 4)) * ld + 32 * (kt >> 1) + 8 * (j >> 2) + 4 * (kt & 1) + (j & 3);
+        F a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a.v[e] = p[e * ld]; a.v[4 + e] = p[(16 + e) * ld]; }
+        return a;
+    }
+    __device__ __forceinline__ static uint32_t ldc_lane(int ld) {
+        const int l = lane_id();
+        return (uint32_t)(((l & 15) * ld + 8 * (l >> 4)) * 4);
+    }
+    __device__ __forceinline__ static F ldc_at(uint32_t base, int ld, int r0, int k0) {
+        const __attribute__((address_space(3))) float* p =
+            lds_ptr<const float>(base + (uint32_t)((r0 * ld + k0) * 4));
+        const f32x4 a = *(const __attribute__((address_space(3))) f32x4*)p;
+        const f32x4 b = *(const __attribute__((address_space(3))) f32x4*)(p + 4);
+        F r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { r.v[e] = a[e]; r.v[4 + e] = b[e]; }
+        return r;
+    }
+    __device__ __forceinline__ static uint32_t ldt_lane(int ld, int k0) {
+        const int l = lane_id(), j = l & 15;
+        return (uint32_t)(((k0 + 4 * (l >> 4)) * ld + 8 * (j >> 2) + (j & 3)) * 4);
+    }
+    __device__ __forceinline__ static F ldt_at(uint32_t base, int ld, int kt) {
+        const __attribute__((address_space(3))) float* p =
+            (const __attribute__((address_space(3))) float*)((const lds_char*)(uintptr_t)base)
+            + 32 * (kt >> 1) + 4 * (kt & 1);
         F a;
 #pragma unroll
         for (int e = 0; e < 4; ++e) { a.v[e] = p[e * ld]; a.v[4 + e] = p[(16 + e) * ld]; }

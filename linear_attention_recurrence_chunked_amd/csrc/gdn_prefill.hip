@@ -260,17 +260,18 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // register file is shared by all roles).
     // Global loads are buffer loads: a buffer resource per stream (scalar
     // registers) whose size is the stream's extent, and a 32-bit lane offset
-    // (the lane's column, clamped in bounds when Dk < DK, plus the row). The
-    // row goes into the lane offset, not the scalar offset, so the hardware
-    // range check covers it: rows past the end of the sequence read as zero
-    // without touching memory. No branches: the store that follows a step
-    // later waits only for its own loads. Vectors past a ragged Dk or Dv edge
-    // are zeroed when stored.
+    // (the lane's column plus the row). The row goes into the lane offset, not
+    // the scalar offset, so the hardware range check covers it: rows past the
+    // end of the sequence read as zero without touching memory. Lanes whose
+    // vector lies past a ragged Dk or Dv edge get a column offset of 2^31,
+    // beyond every stream's extent (row offsets stay below 2^31), so they read
+    // zeros the same way, with no select in the stores. No branches: the
+    // store that follows a step later waits only for its own loads.
     constexpr int KPR = DK / VE;                 // 16-byte vectors per K/Q row
     constexpr int KRI = 64 / KPR;                // rows per load instruction
-    const bool kfull = Dk == DK;
+    constexpr uint32_t kOutOfRange = 0x80000000u;
     const int kd0 = (l % KPR) * VE;
-    const uint32_t koff = (uint32_t)(((l / KPR) * Dk + min(kd0, Dk - VE)) * Cf::ES);
+    const uint32_t koff = kd0 < Dk ? (uint32_t)(((l / KPR) * Dk + kd0) * Cf::ES) : kOutOfRange;
     const int nrec_k = S * Dk * Cf::ES;
     const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, nrec_k, kBufDword3);
     const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, nrec_k, kBufDword3);
@@ -281,10 +282,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                                                 rs, koff + (uint32_t)((c0 + KRI * n) * Dk * Cf::ES), 0, 0));
     };
     auto store_rows = [&](VecE (&r)[Cf::NVK], E* dst) __attribute__((always_inline)) {
-        if (!kfull) {                            // uniform: only with a ragged key dimension
-#pragma unroll
-            for (int n = 0; n < Cf::NVK; ++n) r[n] = kd0 < Dk ? r[n] : VecE{};
-        }
 #pragma unroll
         for (int n = 0; n < Cf::NVK; ++n) {
             const int id = l + 64 * n, t = id / (DK / VE), d0 = (id % (DK / VE)) * VE;
@@ -339,9 +336,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     };
     constexpr int VPR = BV / VE;                 // 16-byte vectors per V row of the slice
     constexpr int VRI = 64 / VPR;
-    const bool vfull = vcols == BV;
     const int vd0 = (l % VPR) * VE;
-    const uint32_t voff = (uint32_t)(((l / VPR) * Dv + min(vd0, vcols - VE)) * Cf::ES);
+    const uint32_t voff = vd0 < vcols ? (uint32_t)(((l / VPR) * Dv + vd0) * Cf::ES) : kOutOfRange;
     const __amdgpu_buffer_rsrc_t rs_v =
         __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, (S * Dv - v0) * Cf::ES, kBufDword3);
     struct QVRegs { VecE q[Cf::NVK], v[Cf::NVV]; };
@@ -357,10 +353,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         char* slot = slot_ptr(c);
         store_rows(R.q, (E*)(slot + Cf::OFF_SQ));
         E* sV = (E*)(slot + Cf::OFF_SV);
-        if (!vfull) {                            // uniform: only with a ragged value slice
-#pragma unroll
-            for (int n = 0; n < Cf::NVV; ++n) R.v[n] = vd0 < vcols ? R.v[n] : VecE{};
-        }
 #pragma unroll
         for (int n = 0; n < Cf::NVV; ++n) {
             const int id = l + 64 * n, t = id / (BV / VE), d0 = (id % (BV / VE)) * VE;
@@ -425,11 +417,13 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         // K K^T on the three lower tiles; per 32-deep step the K fragments of
         // both row tiles are loaded once and serve as both operands. Decay
         // factors e^{gamma_r - gamma_s} are only used where s < r.
+        // (one base address per buffer and lane, the tile offsets as immediates)
+        const uint32_t kbase = opaque_base(lds_addr(sK) + O::ldc_lane(LDK));
         f32x4 acc3[3] = {zero4(), zero4(), zero4()};
 #pragma unroll
         for (int m = 0; m < NKS; ++m) {
-            const F k0 = O::ldc(sK, LDK, 0, 32 * m);
-            const F k1 = O::ldc(sK, LDK, 16, 32 * m);
+            const F k0 = O::ldc_at(kbase, LDK, 0, 32 * m);
+            const F k1 = O::ldc_at(kbase, LDK, 16, 32 * m);
             acc3[0] = O::mma(k0, k0, acc3[0]);
             acc3[1] = O::mma(k1, k0, acc3[1]);
             acc3[2] = O::mma(k1, k1, acc3[2]);
@@ -453,15 +447,16 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             w[e] = (lc < lr + e) ? ts.br[0][e] * dec * acc3[0][e] : 0.f;
         }
         *(f32x4*)(sA + Cf::AB_11T + lc * ALD + lr) = w;
+        // A22 reversed: entry [15 - r][15 - s], rows 15 - lr - e = (12 - lr) + (3 - e)
+        __attribute__((address_space(3))) float* a22r = lds_ptr<float>(
+            opaque_base(lds_addr(sA) + (uint32_t)((Cf::AB_22R + (12 - lr) * ALD + 15 - lc) * 4)));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // A21 row-major: [r][s]
             const float d21 = __expf((ts.gr[1][e] - ts.gs[0]) + (ts.grl[1][e] - ts.gsl[0])) * ts.cs[0];
             sA[Cf::AB_21 + (lr + e) * ALD + lc] = ts.br[1][e] * d21 * acc3[1][e];
-            // A22 reversed: entry [15 - r][15 - s]
             const float d22 = __expf((ts.gr[1][e] - ts.gs[1]) + (ts.grl[1][e] - ts.gsl[1])) * ts.cs[1];
-            sA[Cf::AB_22R + (15 - lr - e) * ALD + 15 - lc] =
-                (lc < lr + e) ? ts.br[1][e] * d22 * acc3[2][e] : 0.f;
+            a22r[(3 - e) * ALD] = (lc < lr + e) ? ts.br[1][e] * d22 * acc3[2][e] : 0.f;
         }
     };
 
@@ -720,20 +715,38 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             }
             if (l < C) sc[Cf::SC_EG + l] *= sc[Cf::SC_RQ + l];
         }
-        const TileScalars ts = tile_scalars(sc, GATED ? Cf::SC_RQ : -1, -1, GATED ? RKP : -1);
+        // Tiles of (Q K^T)^T = K Q^T: lane (lr/4, lc) holds keys s = 16 tj + lr + e
+        // of query row r = 16 ti + lc, which are adjacent in P's row layout
+        // (tpos(s) = 8 (lr/4) + 4 tj + e), so each tile is stored as one
+        // 8-byte vector per lane (hi and, on the bf16 path, lo).
+        // The scalars' "row" arrays therefore index keys and "column" arrays
+        // queries: rk for the rows, rq for the columns.
+        const TileScalars ts = tile_scalars(sc, GATED ? RKP : -1, -1, GATED ? Cf::SC_RQ : -1);
 #pragma unroll
         for (int tt = 0; tt < 3; ++tt) {
             const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 0; m < NKS; ++m) acc = O::mma(qf[ti][m], kf[tj][m], acc);
-            const int s = 16 * tj + lc;
+            for (int m = 0; m < NKS; ++m) acc = O::mma(kf[tj][m], qf[ti][m], acc);
+            const int r = 16 * ti + lc;
+            f32x4 pv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * ti + lr + e;
-                const float dec = __expf((ts.gr[ti][e] - ts.gs[tj]) + (ts.grl[ti][e] - ts.gsl[tj])) *
-                                  (ts.br[ti][e] * ts.cs[tj]);
-                store_pair<SP>(Pp + r * LDP + tpos(s), C, (s <= r) ? scale * dec * acc[e] : 0.f);
+                const int s2 = 16 * tj + lr + e;
+                const float dec = __expf((ts.gs[ti] - ts.gr[tj][e]) + (ts.gsl[ti] - ts.grl[tj][e])) *
+                                  (ts.br[tj][e] * ts.cs[ti]);
+                pv[e] = (s2 <= r) ? scale * dec * acc[e] : 0.f;
+            }
+            E* dst = Pp + r * LDP + 8 * (lr >> 2) + 4 * tj;
+            if constexpr (SP) {
+                uint32_t h0, l0, h1, l1;
+                split2(pv[0], pv[1], h0, l0);
+                split2(pv[2], pv[3], h1, l1);
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                *(u32x2*)dst = u32x2{h0, h1};
+                *(u32x2*)(dst + C) = u32x2{l0, l1};
+            } else {
+                *(f32x4*)dst = pv;
             }
         }
     };
@@ -813,9 +826,11 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 qs[ti] = O::mma(sh, qf[cb][ti], qs[ti]);
             }
         }
-        // first transposed K tile of the state update
+        // first transposed K tile of the state update (one base address for
+        // all tiles, the tile offsets as immediates)
+        const uint32_t ktb = opaque_base(lds_addr(sK) + O::ldt_lane(LDK, 0));
         F kt_f[2];
-        kt_f[0] = O::ldt(sK, LDK, 0, 0);
+        kt_f[0] = O::ldt_at(ktb, LDK, 0);
         __builtin_amdgcn_sched_barrier(kComputeMayCross);
         // R = beta V - beta e^gamma (K S0)
         f32x4 r[NT];
@@ -848,7 +863,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
             if (kt + 1 < NKT) {
-                kt_f[(kt + 1) & 1] = O::ldt(sK, LDK, kt + 1, 0);
+                kt_f[(kt + 1) & 1] = O::ldt_at(ktb, LDK, kt + 1);
             } else {
 #pragma unroll
                 for (int ti = 0; ti < NT; ++ti) {
