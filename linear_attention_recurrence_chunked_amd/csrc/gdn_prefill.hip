@@ -756,29 +756,54 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     const bool vok = wave < Cf::NCW && vl < vcols;
     const bool wok = wave < Cf::NCW && 16 * wave < vcols;   // this wave's 16 output columns exist
     // accS[kt]: state rows spos(kt, lr/4, e), column vl, held for the whole sequence
-    auto consume = [&](int i, f32x4 (&accS)[NKT]) __attribute__((always_inline)) {
+    // Operands of chunk i that a consumer reads ahead, during the output phase
+    // of chunk i - 1 (before the barrier between them): the first 32-deep K
+    // and Q fragments and, on the bf16 path, V, beta and beta e^gamma of this
+    // lane's rows t = 16 ti + lr + e. The slot of chunk i was stored several
+    // steps earlier and is not written again until step i + 1; beta e^gamma
+    // (folded with rk on the GATED path) was final when the A wave finished
+    // chunk i, three steps ahead. On the fp32 path the A wave builds chunk i
+    // during step i - 1, so those scalars are read at the start of step i.
+    struct ConsPre { F kf[NT], qf[NT]; float vv[NT][4], bt[NT][4], bk[NT][4]; };
+    auto cons_scalars = [&](int i, ConsPre& p) __attribute__((always_inline)) {
+        const char* slot = slot_ptr(i);
+        const E* __restrict__ sV = (const E*)(slot + Cf::OFF_SV);
+        const float* __restrict__ sc = (const float*)(slot + Cf::OFF_SSC);
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * ti + lr + e;
+                p.vv[ti][e] = to_f32(sV[t * LDV + vl]);
+                p.bt[ti][e] = sc[Cf::SC_B + t];
+                p.bk[ti][e] = sc[Cf::SC_BK + t];
+            }
+    };
+    auto cons_prefetch = [&](int i, ConsPre& p) __attribute__((always_inline)) {
         const char* slot = slot_ptr(i);
         const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
         const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
-        const E* __restrict__ sV = (const E*)(slot + Cf::OFF_SV);
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            p.kf[ti] = O::ldc(sK, LDK, 16 * ti, 0);
+            p.qf[ti] = O::ldc(sQ, LDK, 16 * ti, 0);
+        }
+        if constexpr (Cf::SPREAD) cons_scalars(i, p);
+    };
+    auto consume = [&](int i, f32x4 (&accS)[NKT], ConsPre& pre) __attribute__((always_inline)) {
+        const char* slot = slot_ptr(i);
+        const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
+        const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
         const float* __restrict__ sc = (const float*)(slot + Cf::OFF_SSC);
         const E* __restrict__ Tp = (const E*)(smem + Cf::OFF_T + (i % Cf::NTBUF) * Cf::SZ_TP);
         const E* __restrict__ Pp = (const E*)(smem + Cf::OFF_P + (i & 1) * Cf::SZ_TP);
         const int c0 = i * C;
-        // per-row scalars and V values of this lane's rows t = 16 ti + lr + e, read once
-        float vv[NT][4], bt[NT][4], bk[NT][4], dl[NT][4], egt[NT];
+        if constexpr (!Cf::SPREAD) cons_scalars(i, pre);
+        // scale e^gamma of token 16 ti + lc (folded with rq by the P wave during
+        // step i - 1 on the GATED path) and e^{gamma_C}
+        float egt[NT];
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * ti + lr + e;
-                vv[ti][e] = to_f32(sV[t * LDV + vl]);
-                bt[ti][e] = sc[Cf::SC_B + t];
-                bk[ti][e] = sc[Cf::SC_BK + t];
-                dl[ti][e] = sc[Cf::SC_DL + t];
-            }
-            egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];   // scale e^gamma of token 16 ti + lc
-        }
+        for (int ti = 0; ti < NT; ++ti) egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];
         const float egC = sc[Cf::SC_EGC];
         // LDS operands are read one stage ahead of the products that use them
         // (the next 32-deep slice of K and Q, then T, then the transposed K
@@ -793,8 +818,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         F kf[2][NT], qf[2][NT];
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) {
-            kf[0][ti] = O::ldc(sK, LDK, 16 * ti, 0);
-            qf[0][ti] = O::ldc(sQ, LDK, 16 * ti, 0);
+            kf[0][ti] = pre.kf[ti];
+            qf[0][ti] = pre.qf[ti];
         }
         F tf[NT][2];
 #pragma unroll
@@ -826,18 +851,25 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 qs[ti] = O::mma(sh, qf[cb][ti], qs[ti]);
             }
         }
-        // first transposed K tile of the state update (one base address for
-        // all tiles, the tile offsets as immediates)
+        // All transposed K tiles of the state update, issued now (into the
+        // registers the K and Q fragments held) so that they arrive during R
+        // and U; one base address for all tiles, the offsets as immediates.
         const uint32_t ktb = opaque_base(lds_addr(sK) + O::ldt_lane(LDK, 0));
-        F kt_f[2];
-        kt_f[0] = O::ldt_at(ktb, LDK, 0);
+        F kt_f[NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) kt_f[kt] = O::ldt_at(ktb, LDK, kt);
+        float dl[NT][4];                               // e^{gamma_C - gamma} of this lane's rows
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dl[ti][e] = sc[Cf::SC_DL + 16 * ti + lr + e];
         __builtin_amdgcn_sched_barrier(kComputeMayCross);
         // R = beta V - beta e^gamma (K S0)
         f32x4 r[NT];
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[ti][e] = bt[ti][e] * vv[ti][e] - bk[ti][e] * ks[ti][e];
+            for (int e = 0; e < 4; ++e) r[ti][e] = pre.bt[ti][e] * pre.vv[ti][e] - pre.bk[ti][e] * ks[ti][e];
         F rh, rl;
         O::split(r[0], r[1], rh, rl);
         // U = T R
@@ -859,24 +891,23 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             for (int e = 0; e < 4; ++e) ud[ti][e] = u[ti][e] * dl[ti][e];
         F dh, dlo;
         O::split(ud[0], ud[1], dh, dlo);
+        // P of the output, read while the state update runs
         F pf[NT][2];
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-            if (kt + 1 < NKT) {
-                kt_f[(kt + 1) & 1] = O::ldt_at(ktb, LDK, kt + 1);
-            } else {
+        for (int ti = 0; ti < NT; ++ti) {
+            pf[ti][0] = O::ldc(Pp, LDP, 16 * ti, 0);
+            if constexpr (SP) pf[ti][1] = O::ldc(Pp, LDP, 16 * ti, C);
+        }
+        __builtin_amdgcn_sched_barrier(kComputeMayCross);
 #pragma unroll
-                for (int ti = 0; ti < NT; ++ti) {
-                    pf[ti][0] = O::ldc(Pp, LDP, 16 * ti, 0);
-                    if constexpr (SP) pf[ti][1] = O::ldc(Pp, LDP, 16 * ti, C);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(kComputeMayCross);
+        for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) accS[kt][e] *= egC;
-            if constexpr (SP) accS[kt] = O::mma(kt_f[kt & 1], dlo, accS[kt]);
-            accS[kt] = O::mma(kt_f[kt & 1], dh, accS[kt]);
+            if constexpr (SP) accS[kt] = O::mma(kt_f[kt], dlo, accS[kt]);
+            accS[kt] = O::mma(kt_f[kt], dh, accS[kt]);
         }
+        // the next chunk's first operands, read during the output phase
+        cons_prefetch(i + 1, pre);
         // O^T = (Q S0)^T diag(scale e^gamma) + U^T P^T (P carries the scale):
         // lane (g, n) holds 4 consecutive value columns 4g.. of token 16 ti + n,
         // stored as one vector.
@@ -940,9 +971,18 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         __syncthreads();
         __syncthreads();
         __syncthreads();
+        ConsPre pre;
+        cons_prefetch(0, pre);
         for (int i = 0; i < NC; ++i) {
-            consume(i, accS);
-            __syncthreads();
+            consume(i, accS, pre);
+            // The consumers write no LDS, and the only LDS reads they may
+            // still have in flight here are the prefetches of chunk i + 1,
+            // whose slot no wave writes before step i + 2: they pass the
+            // barrier without waiting for those reads (a compiler-only fence
+            // keeps every LDS access on its side of it).
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
         if (vok) {
 #pragma unroll
