@@ -113,11 +113,14 @@ struct PipeCfg {
     // Wave w runs on SIMD w % 4 (waves are placed round-robin): with four
     // consumers, P and A share SIMDs 0 and 1 with the two stagers, and the
     // inverse waves (the heaviest helpers) get SIMDs 2 and 3 to themselves.
+    // The K stager (gamma scan, decay scalars, gates) sits with the A wave
+    // and the lighter QV stager with the P wave, which has more VALU work.
     static constexpr int NTW = SPREAD ? 2 : 1;     // inverse waves
     static constexpr int W_P = NCW;                // P wave
     static constexpr int W_A = SPREAD ? NCW + 1 : -1;   // A wave
     static constexpr int W_T = SPREAD ? NCW + 2 : NCW + 1;   // first inverse wave
     static constexpr int W_S = W_T + NTW;          // first of two stager waves
+    static constexpr int W_SQ = W_S, W_SK = W_S + 1;    // QV stager, K stager
     static constexpr int NW = W_S + 2;
     static constexpr int THREADS = 64 * NW;
     static constexpr int NSLOT = SPREAD ? 5 : 3;   // chunks i .. i+NSLOT-1 resident
@@ -139,7 +142,7 @@ struct PipeCfg {
     // LDS layout (bytes)
     static constexpr int SZ_K = C * LDK * ES;
     static constexpr int SZ_V = C * LDV * ES;
-    static constexpr int SZ_SC = (9 * C + 4) * 4;
+    static constexpr int SZ_SC = (7 * C + 4) * 4;
     static constexpr int OFF_SK = 0, OFF_SQ = SZ_K, OFF_SV = 2 * SZ_K, OFF_SSC = 2 * SZ_K + SZ_V;
     static constexpr int SZ_SLOT = 2 * SZ_K + SZ_V + SZ_SC;
     static constexpr int SZ_TP = C * LDP * ES;
@@ -161,12 +164,11 @@ struct PipeCfg {
     static constexpr int LDS_BYTES = OFF_SLOTS + NSLOT * SZ_SLOT;
     // scalar arrays inside a slot (floats): gamma (its fp32 value and, in SC_GAML,
     // the rest gamma - fp32(gamma)), scale e^gamma, beta, beta e^gamma,
-    // e^{gamma_C - gamma}, [0] = e^{gamma_C}; on the GATED path rk (A builder), rq and
-    // the P wave's own rk (P wave), and the second, fourth and fifth arrays carry the
-    // factors rq, rk, rk once the A builder and the P wave have folded them in.
+    // e^{gamma_C - gamma}, [0] = e^{gamma_C}; on the GATED path rk (from the A
+    // builder, for the P wave), and the second, fourth and fifth arrays carry the
+    // factors rq, rk, rk once the P wave and the A builder have folded them in.
     static constexpr int SC_GAM = 0, SC_EG = C, SC_B = 2 * C, SC_BK = 3 * C, SC_DL = 4 * C,
-                         SC_RK = 5 * C, SC_RQ = 6 * C, SC_RKP = 7 * C, SC_GAML = 8 * C,
-                         SC_EGC = 9 * C;
+                         SC_RK = 5 * C, SC_GAML = 6 * C, SC_EGC = 7 * C;
 
     static_assert(C == 32, "the pipeline is laid out for 32-token chunks");
     static_assert(DK % 32 == 0 && BV % 16 == 0 && BV <= 64, "tile sizes");
@@ -253,9 +255,9 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     auto slot_ptr = [&](int c) { return smem + Cf::OFF_SLOTS + (c % Cf::NSLOT) * Cf::SZ_SLOT; };
 
     // ------------------------------------------------------------ stagers
-    // Two stager waves split each chunk: the K stager (wave W_S) moves K, g
+    // Two stager waves split each chunk: the K stager (wave W_SK) moves K, g
     // and beta and computes gamma and the decay scalars; the QV stager (wave
-    // W_S + 1) moves Q and V. Loads and stores of a chunk happen in the same
+    // W_SQ) moves Q and V. Loads and stores of a chunk happen in the same
     // step, so no staging registers stay live across the barrier (the
     // register file is shared by all roles).
     // Global loads are buffer loads: a buffer resource per stream (scalar
@@ -386,23 +388,30 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
         return ts;
     };
-    // GATED: from the two diagonal 16x16 tiles d[0], d[1] of X X^T (X = K or Q
-    // of a chunk), dst[t] = 1/sqrt(|x_t|^2 + eps) for the 32 tokens. Lane
-    // (lr/4, lc) holds rows lr + e, column lc, so the lanes with lc / 4 == lr / 4
-    // hold the diagonal, in element lc % 4.
-    // Tokens past the end of the sequence (t >= nreal) get the factor 0: their
-    // rows are zero, and 1/sqrt(0 + eps) could be infinite.
-    auto diag_norms = [&](const f32x4 (&d)[2], float* dst, int nreal) __attribute__((always_inline)) {
-        if ((lc >> 2) == (lr >> 2)) {
+    // GATED: norm factors 1/sqrt(|x_t|^2 + eps) of the 32 tokens of a chunk
+    // from the two diagonal 16x16 tiles d[0], d[1] of X X^T (X = K or Q).
+    // Lane (lr/4, lc) holds rows lr + e, column lc of a tile, so the lanes
+    // with lc / 4 == lr / 4 hold the diagonal, in element lc % 4: those lanes
+    // form the factor of token 16 ti + lc (0 for tokens t >= nreal past the
+    // end of the sequence, whose rows are zero). Other lanes fetch it by a
+    // lane shuffle, never through LDS:
+    //   row factors  (token 16 ti + lr + e): lane 20 (lr / 4) + e = 5 lr + e
+    //   column factor (token 16 ti + lc):   lane 16 (lc / 4) + lc
+    struct NormF { float row[2][4], col[2]; };
+    auto norm_factors = [&](const f32x4 (&d)[2], int nreal, bool rows) __attribute__((always_inline)) {
+        NormF f;
+        const int src_col = 16 * (lc >> 2) + lc;
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti)
-                dst[16 * ti + lc] = 16 * ti + lc < nreal
-                                        ? __builtin_amdgcn_rsqf(pick4(d[ti], lc & 3) + l2_eps) : 0.f;
+        for (int ti = 0; ti < 2; ++ti) {
+            const float own = 16 * ti + lc < nreal
+                                  ? __builtin_amdgcn_rsqf(pick4(d[ti], lc & 3) + l2_eps) : 0.f;
+            f.col[ti] = __shfl(own, src_col);
+            if (rows) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f.row[ti][e] = __shfl(own, 5 * lr + e);
+            }
         }
-        // Later reads of dst by other lanes of this wave: LDS accesses of a
-        // wave complete in program order, so only the compiler must keep them
-        // after these writes.
-        __builtin_amdgcn_wave_barrier();
+        return f;
     };
 
     // A = diag(beta) (K K^T) (.) Mstrict of chunk c, into A buffer c % NABUF.
@@ -428,17 +437,27 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             acc3[1] = O::mma(k1, k0, acc3[1]);
             acc3[2] = O::mma(k1, k1, acc3[2]);
         }
+        TileScalars ts = tile_scalars(sc, Cf::SC_B, -1, -1);
         if constexpr (GATED) {
+            // A[r][s] carries rk_r rk_s; rk is folded into the chunk's beta
+            // e^gamma and e^{gamma_C - gamma} (lane l < C: token l, whose
+            // factor is this lane's column factor of tile l / 16) and kept for
+            // the P wave
             const f32x4 dg[2] = {acc3[0], acc3[2]};
-            diag_norms(dg, sc + Cf::SC_RK, S - c * C);
+            const NormF rk = norm_factors(dg, S - c * C, true);
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) {
+                ts.cs[ti] *= rk.col[ti];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ts.br[ti][e] *= rk.row[ti][e];
+            }
             if (l < C) {
-                const float rk = sc[Cf::SC_RK + l];
-                sc[Cf::SC_BK + l] *= rk;
-                sc[Cf::SC_DL + l] *= rk;
+                const float rkl = l < 16 ? rk.col[0] : rk.col[1];
+                sc[Cf::SC_RK + l] = rkl;
+                sc[Cf::SC_BK + l] *= rkl;
+                sc[Cf::SC_DL + l] *= rkl;
             }
         }
-        const TileScalars ts = tile_scalars(sc, Cf::SC_B, GATED ? Cf::SC_RK : -1,
-                                            GATED ? Cf::SC_RK : -1);
         // lane (lr/4, lc) holds rows r = lr + e, column s = lc of each tile
         f32x4 w;
 #pragma unroll
@@ -697,31 +716,36 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 kf[t2][m] = O::ldc(sK, LDK, 16 * t2, 32 * m);
                 qf[t2][m] = O::ldc(sQ, LDK, 16 * t2, 32 * m);
             }
-        constexpr int RKP = Cf::SPREAD ? Cf::SC_RK : Cf::SC_RKP;
+        // The scalars' "row" arrays index keys and "column" arrays queries
+        // (tiles of K Q^T below): rk for the rows, rq for the columns.
+        TileScalars ts = tile_scalars(sc, (GATED && Cf::SPREAD) ? Cf::SC_RK : -1, -1, -1);
         if constexpr (GATED) {
             f32x4 dq[2] = {zero4(), zero4()};
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                 for (int m = 0; m < NKS; ++m) dq[ti] = O::mma(qf[ti][m], qf[ti][m], dq[ti]);
-            diag_norms(dq, sc + Cf::SC_RQ, S - c * C);
+            const NormF rq = norm_factors(dq, S - c * C, false);
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) ts.cs[ti] *= rq.col[ti];
             if constexpr (!Cf::SPREAD) {
                 f32x4 dk[2] = {zero4(), zero4()};
 #pragma unroll
                 for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                     for (int m = 0; m < NKS; ++m) dk[ti] = O::mma(kf[ti][m], kf[ti][m], dk[ti]);
-                diag_norms(dk, sc + Cf::SC_RKP, S - c * C);
+                const NormF rk = norm_factors(dk, S - c * C, true);
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ts.br[ti][e] *= rk.row[ti][e];
             }
-            if (l < C) sc[Cf::SC_EG + l] *= sc[Cf::SC_RQ + l];
+            if (l < C) sc[Cf::SC_EG + l] *= l < 16 ? rq.col[0] : rq.col[1];
         }
         // Tiles of (Q K^T)^T = K Q^T: lane (lr/4, lc) holds keys s = 16 tj + lr + e
         // of query row r = 16 ti + lc, which are adjacent in P's row layout
         // (tpos(s) = 8 (lr/4) + 4 tj + e), so each tile is stored as one
         // 8-byte vector per lane (hi and, on the bf16 path, lo).
-        // The scalars' "row" arrays therefore index keys and "column" arrays
-        // queries: rk for the rows, rq for the columns.
-        const TileScalars ts = tile_scalars(sc, GATED ? RKP : -1, -1, GATED ? Cf::SC_RQ : -1);
 #pragma unroll
         for (int tt = 0; tt < 3; ++tt) {
             const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
@@ -1045,7 +1069,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             if (i + 3 < NC) build_A(i + 3);
             __syncthreads();
         }
-    } else if (wave == Cf::W_S) {
+    } else if (wave == Cf::W_SK) {
         if constexpr (GATED) { expA = expf(A_log[h]); dtb = dt_bias[h]; }
         // Loads are issued a full step before their data is stored: at step i
         // the loads of chunk i + LEAD + 1 go out first, then chunk i + LEAD
