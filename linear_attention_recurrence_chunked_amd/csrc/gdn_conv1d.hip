@@ -135,20 +135,15 @@ __global__ __launch_bounds__(kConvThreads) void gdn_conv1d_prefill_kernel(
             o[e] = silu_f(y);
         }
         store8<E, ALIGNED>(out + (size_t)row * T + tv, n, o);
-        if (tv <= T - 1 && T - 1 < tv + kConvNE) {
-            E* st = state + (size_t)row * K;
-#pragma unroll
-            for (int j = 0; j < K; ++j) {
-                const int i = T - K + j - tv;
-                float vj = 0.f;
-#pragma unroll
-                for (int e = 0; e < kConvNE; ++e) {
-                    if (i == e) vj = cur[v][e];
-                    if (i == e - kConvNE) vj = prev[e];
-                }
-                st[j] = from_f32<E>(T - K + j >= 0 ? vj : 0.f);
-            }
-        }
+    }
+    // Window state: the last K raw tokens of the row (0 before t = 0), copied
+    // from x by the first K threads of the workgroup whose tile holds token
+    // T - 1 (this workgroup has just read them: cache hits). Picking them out
+    // of the registers above would take a runtime index into register arrays,
+    // which compiles to compare-and-select chains over every element.
+    if (tile == tiles - 1 && (int)threadIdx.x < K) {
+        const int j = threadIdx.x, t = T - K + j;
+        state[(size_t)row * K + j] = t >= 0 ? xr[t] : from_f32<E>(0.f);
     }
 }
 
