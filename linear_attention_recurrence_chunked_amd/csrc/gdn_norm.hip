@@ -29,7 +29,7 @@ constexpr int kNormNR = 2;          // rows per thread (1 and 4 measured slower)
 template <typename E, int P, int HT>
 __global__ __launch_bounds__(kNormThreads) void gdn_rmsnorm_gated_kernel(
     const E* __restrict__ o, const E* __restrict__ z, const float* __restrict__ w, float eps,
-    E* __restrict__ out, int Hv, int S, int Dv, int stiles)
+    E* __restrict__ out, int Hv, int S, int Dv, int b0)
 {
     constexpr int VE = 16 / (int)sizeof(E);
     constexpr int RW = kNormThreads / P;               // rows per pass of the workgroup
@@ -37,9 +37,8 @@ __global__ __launch_bounds__(kNormThreads) void gdn_rmsnorm_gated_kernel(
     typedef typename std::conditional<sizeof(E) == 2, bf16x8, f32x4>::type V;
     const int li = threadIdx.x % P;
     const int c0 = li * VE;
-    const long long tile = blockIdx.x;
-    const long long st = tile % stiles, hb = (tile / stiles) % (Hv / HT);
-    const long long b = tile / stiles / (Hv / HT);
+    // grid: x = token tile, y = head tile, z = batch (from b0)
+    const long long st = blockIdx.x, hb = blockIdx.y, b = b0 + (long long)blockIdx.z;
     // kNormNR rows per thread, all loaded before any is used
     V a[kNormNR], g[kNormNR];
     long long row[kNormNR];
@@ -84,13 +83,19 @@ template <typename E, int P, int HT>
 static hipError_t norm_ph(const NormArgs& a, hipStream_t st)
 {
     constexpr int TT = kNormNR * kNormThreads / P / HT;
+    constexpr int kMaxGridYZ = 65535;
     const int stiles = (a.S + TT - 1) / TT;
-    const long long blocks = (long long)a.B * (a.Hv / HT) * stiles;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gdn_rmsnorm_gated_kernel<E, P, HT>), dim3((unsigned)blocks),
-                       dim3(kNormThreads), 0, st, (const E*)a.o, (const E*)a.z, a.w, a.eps,
-                       (E*)a.out, a.Hv, a.S, a.Dv, stiles);
-    return hipGetLastError();
+    if (a.Hv / HT > kMaxGridYZ) return hipErrorInvalidConfiguration;
+    for (int b0 = 0; b0 < a.B; b0 += kMaxGridYZ) {   // one launch unless B > 65535
+        const int nb = a.B - b0 < kMaxGridYZ ? a.B - b0 : kMaxGridYZ;
+        hipLaunchKernelGGL((gdn_rmsnorm_gated_kernel<E, P, HT>),
+                           dim3((unsigned)stiles, (unsigned)(a.Hv / HT), (unsigned)nb),
+                           dim3(kNormThreads), 0, st, (const E*)a.o, (const E*)a.z, a.w, a.eps,
+                           (E*)a.out, a.Hv, a.S, a.Dv, b0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <typename E, int P>
