@@ -83,11 +83,11 @@ __device__ __forceinline__ void store8(E* p, int n, const float (&v)[kConvNE]) {
 template <typename E, int K, bool ALIGNED>
 __global__ __launch_bounds__(kConvThreads) void gdn_conv1d_prefill_kernel(
     const E* __restrict__ x, const float* __restrict__ w, E* __restrict__ out,
-    E* __restrict__ state, int C, int T, int tiles)
+    E* __restrict__ state, int C, int T, int tiles, int tile0)
 {
     static_assert(K >= 1 && K <= kConvNE, "taps");
-    const int row = blockIdx.x / tiles;                 // b * C + c
-    const int tile = blockIdx.x - row * tiles;
+    const int row = blockIdx.x;                         // b * C + c
+    const int tile = tile0 + (int)blockIdx.y;
     const int c = row % C;
     const int lane = threadIdx.x & 63;
     float wk[K];
@@ -205,18 +205,23 @@ __global__ __launch_bounds__(kConvThreads) void gdn_conv1d_decode_kernel(
 template <typename E, int K>
 static hipError_t conv_prefill_k(const ConvArgs& a, hipStream_t s)
 {
+    // grid: x = channel row (b * C + c), y = token tile (from tile0)
+    constexpr int kMaxGridY = 65535;
     const int tiles = (a.T + kConvTile - 1) / kConvTile;
-    const long long blocks = (long long)a.B * a.C * tiles;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (a.T % kConvNE == 0)
-        hipLaunchKernelGGL((gdn_conv1d_prefill_kernel<E, K, true>), dim3((unsigned)blocks),
-                           dim3(kConvThreads), 0, s, (const E*)a.x, a.w, (E*)a.out,
-                           (E*)a.state, a.C, a.T, tiles);
-    else
-        hipLaunchKernelGGL((gdn_conv1d_prefill_kernel<E, K, false>), dim3((unsigned)blocks),
-                           dim3(kConvThreads), 0, s, (const E*)a.x, a.w, (E*)a.out,
-                           (E*)a.state, a.C, a.T, tiles);
-    return hipGetLastError();
+    const long long rows = (long long)a.B * a.C;
+    if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    for (int tile0 = 0; tile0 < tiles; tile0 += kMaxGridY) {   // one launch unless T is huge
+        const dim3 grid((unsigned)rows, (unsigned)(tiles - tile0 < kMaxGridY ? tiles - tile0 : kMaxGridY));
+        if (a.T % kConvNE == 0)
+            hipLaunchKernelGGL((gdn_conv1d_prefill_kernel<E, K, true>), grid, dim3(kConvThreads), 0, s,
+                               (const E*)a.x, a.w, (E*)a.out, (E*)a.state, a.C, a.T, tiles, tile0);
+        else
+            hipLaunchKernelGGL((gdn_conv1d_prefill_kernel<E, K, false>), grid, dim3(kConvThreads), 0, s,
+                               (const E*)a.x, a.w, (E*)a.out, (E*)a.state, a.C, a.T, tiles, tile0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <typename E, int K>
