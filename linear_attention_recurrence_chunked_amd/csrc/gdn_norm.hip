@@ -75,7 +75,9 @@ __global__ __launch_bounds__(kNormThreads) void gdn_rmsnorm_gated_kernel(
             // error ~1e-7, far below the bf16 output rounding and the fp32 checks)
             y[e] = from_f32<E>(ov[e] * r * w[c0 + e] * (zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz))));
         }
-        *(V*)(out + row[n] * Dv + c0) = y;
+        // y is not read again by this pass: a non-temporal store keeps it out
+        // of the caches the o and z streams use
+        __builtin_nontemporal_store(y, (V*)(out + row[n] * Dv + c0));
     }
 }
 

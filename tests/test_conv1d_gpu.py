@@ -46,13 +46,16 @@ def test_conv_prefill_taps(dtype, K):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_conv_prefill_multi_tile_rows(dtype):
-    """Rows of several workgroups (2048 tokens each) with a ragged tail, many
-    channels and batches."""
-    d = inputs.draw_conv(3, 40, 6000, 4, dtype=dtype)
+@pytest.mark.parametrize("B,C,T", [(3, 40, 6000), (2, 12, 20000)])
+def test_conv_prefill_multi_tile_rows(dtype, B, C, T):
+    """Many channels and batches; T = 20000 spreads each row over three
+    workgroups (8192 tokens each) with a ragged tail, so the history across
+    workgroup boundaries and the window state of the last one are covered."""
+    d = inputs.draw_conv(B, C, T, 4, dtype=dtype)
+    log("conv prefill multi-tile", dtype, B, C, T)
     out, st = _prefill(d["x"], d["w"], dtype)
     ro, rs = ref.conv1d_prefill(d["x"], d["w"])
-    check("conv prefill 3x40x6000 %s" % dtype, dtype, out, ro, st, rs)
+    check("conv prefill %dx%dx%d %s" % (B, C, T, dtype), dtype, out, ro, st, rs)
     assert np.array_equal(st, rs)
 
 
