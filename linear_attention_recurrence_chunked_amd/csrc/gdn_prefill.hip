@@ -28,7 +28,8 @@
 //    whole sequence. For chunk i they compute K S0 and Q S0 (state fed from
 //    registers as the B operand), R, U = T R, O = e^gamma Q S0 + P U and the
 //    state update K^T (dl U) -- every intermediate stays in registers; LDS is
-//    only read for K, Q, V, T and P of the chunk;
+//    only read for K, Q, V, T and P of the chunk (the first K/Q slice and
+//    the row scalars of chunk i+1 already during chunk i's output phase);
 //  * two inverse waves build T = (I + A)^{-1}, taking alternate chunks and
 //    spreading a chunk over two steps: fp32 forward substitution of the two
 //    16x16 diagonal blocks for chunk i+2 (one lane per column), then the
@@ -829,11 +830,13 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];
         const float egC = sc[Cf::SC_EGC];
-        // LDS operands are read one stage ahead of the products that use them
-        // (the next 32-deep slice of K and Q, then T, then the transposed K
-        // tiles and P); a scheduling barrier after each batch of reads keeps
-        // the compiler from sinking them back next to their use, while
-        // arithmetic is still free to move across it.
+        // LDS operands are read ahead of the products that use them: the
+        // first 32-deep K and Q slice and the row scalars during the previous
+        // chunk's output phase, each further slice one stage ahead, then T;
+        // the transposed K tiles and e^{gamma_C - gamma} right after K S0;
+        // P before the state update. A scheduling barrier after each batch of
+        // reads keeps the compiler from sinking them back next to their use,
+        // while arithmetic is still free to move across it.
         // K S0 ([token][value column] tiles) and (Q S0)^T ([value column][token]
         // tiles: the same fragments with the operands swapped), S0 from registers
         f32x4 ks[NT], qs[NT];
