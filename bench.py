@@ -43,7 +43,11 @@ known traffic); ``--only prefill|decode`` runs one path alone.
 
 Roofline (per launch, algorithmic, see the workload docstrings below):
 * prefill: HBM bytes = tokens x (q + k + v + out + g + beta) + state in/out;
-  algorithmic MFMA flops reported as "mfma_util" against the bf16 dense peak.
+  algorithmic MFMA flops reported as "mfma_util" against the bf16 dense peak,
+  and under "mfma_util.counter" the issued bf16 MFMA flops that rocprofv3
+  counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, committed summary) over this
+  run's launch time, with the MFMA busy fraction and shader clock measured
+  with them.
 * decode: HBM bytes = 2 x fp32 state + q, k, v, out, g, beta.
 """
 import argparse
@@ -123,6 +127,28 @@ def measured_traffic(kernel):
     if not rec or rec.get("source_sha256_16") != source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+def mfma_counters(kernel, kern_ms):
+    """Counter-based MFMA utilisation of a prefill kernel: the issued bf16
+    MFMA flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) from the
+    committed rocprofv3 summary over this run's launch time, the MFMA busy
+    fraction and the shader clock measured with them; None when the kernel
+    source changed since the counters were taken."""
+    path = os.path.join(PROFILES, "mfma_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_digest(kernel):
+        return None
+    issued = rec["issued_bf16_flops_per_launch"] / (kern_ms / 1e3) / 1e12
+    return {"issued_bf16_tflops": issued, "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": issued / BF16_PEAK_TFLOPS,
+            "issued_bf16_flops_per_launch": rec["issued_bf16_flops_per_launch"],
+            "mfma_busy_fraction": rec["mfma_busy_fraction"], "sclk_ghz": rec["sclk_ghz"],
+            "source": "profiles/mfma_counters.json"}
 
 
 def _events(torch, n):
@@ -579,7 +605,8 @@ def main():
         "mfma_util": {"achieved_tflops": flops / (kern_ms / 1e3) / 1e12,
                       "peak_tflops": BF16_PEAK_TFLOPS,
                       "frac": flops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
-                      "algorithmic_flops_per_launch": flops},
+                      "algorithmic_flops_per_launch": flops,
+                      "counter": mfma_counters("gdn_prefill_kernel", kern_ms)},
         "decode": {"workload": "decode_b256", "B": dw.B, "Hk": dw.Hk, "Hv": dw.Hv,
                    "value": 1e3 / dms, "unit": "steps/s", "ms_per_step": dms,
                    "tokens_per_s": dw.B * 1e3 / dms,
