@@ -447,52 +447,68 @@ def bench_copy(torch, mib, steps):
     return {"copy_bytes_each_way": n * 4, "ms": dt * 1e3, "GB_s": 2 * n * 4 / dt / 1e9}
 
 
+def _repeat_for(fn, min_s, max_reps):
+    """Calls fn() until at least min_s seconds have passed (at most max_reps
+    calls, at least one); returns (calls, seconds)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s or n >= max_reps:
+            return n, dt
+
+
 def cpu_baseline_prefill(w, d):
-    """The oracle on one whole step of the prefill workload (B x S tokens x Hv value heads)."""
+    """The oracle on whole steps of the prefill workload (B x S tokens x Hv
+    value heads), the state carried from step to step as in the GPU timing,
+    repeated for at least 10 s."""
     import oracle
     n = oracle.default_threads()
-    t0 = time.perf_counter()
-    oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], w.scale, d["state"],
-                      nthreads=n)
-    dt = time.perf_counter() - t0
-    return {"value": w.B * w.S / dt, "unit": "tokens/s", "cores": n, "kind": "oracle",
-            "sample": "one whole step of the prefill workload: %d x %d tokens x %d value heads, "
-                      "fp64 token-serial, %.2f s" % (w.B, w.S, w.Hv, dt)}
+    st = [d["state"].astype(np.float64)]
+
+    def step():
+        _, st[0] = oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], w.scale,
+                                     st[0], nthreads=n, inplace=True)
+    reps, dt = _repeat_for(step, 10.0, 16)
+    return {"value": reps * w.B * w.S / dt, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": "%d whole steps of the prefill workload (%d x %d tokens x %d value heads "
+                      "each, state carried), fp64 token-serial, %.1f s" % (reps, w.B, w.S, w.Hv, dt)}
 
 
 def cpu_baseline_decode(w, steps, state0):
-    """The oracle on all decode steps of the workload, state carried."""
+    """The oracle on passes over all decode steps of the workload, state
+    carried, repeated for at least 3 s."""
     import oracle
     n = oracle.default_threads()
-    st = state0.astype(np.float64)
-    t0 = time.perf_counter()
-    for s in steps:
-        _, st = oracle.gdn_serial(s["q"], s["k"], s["v"], s["g_log"], s["beta"], w.scale, st,
-                                  nthreads=n, inplace=True)
-    dt = time.perf_counter() - t0
-    return {"value": len(steps) / dt, "unit": "steps/s", "cores": n, "kind": "oracle",
-            "sample": "all %d decode steps at B=%d, state carried, fp64, %.2f s" % (len(steps), w.B, dt)}
+    st = [state0.astype(np.float64)]
+
+    def run_pass():
+        for s in steps:
+            _, st[0] = oracle.gdn_serial(s["q"], s["k"], s["v"], s["g_log"], s["beta"], w.scale,
+                                         st[0], nthreads=n, inplace=True)
+    reps, dt = _repeat_for(run_pass, 3.0, 16)
+    return {"value": reps * len(steps) / dt, "unit": "steps/s", "cores": n, "kind": "oracle",
+            "sample": "%d pass%s over all %d decode steps at B=%d, state carried, fp64, %.1f s"
+                      % (reps, "" if reps == 1 else "es", len(steps), w.B, dt)}
 
 
 def cpu_baseline_conv(inputs, cw, decode):
-    """The conv1d oracle (numpy fp64): prefill on one batch row of the
-    workload (all C channels, all T tokens), decode on one whole step."""
+    """The conv1d oracle (numpy fp64, one core): prefill on batch rows of the
+    workload (all C channels, all T tokens each), decode on whole steps,
+    repeated for at least 2 s."""
     from oracle import conv1d
     d = inputs.draw_conv(1 if not decode else cw.B, cw.C, cw.T, cw.K, dtype=cw.dtype,
                          decode=decode)
-    t0 = time.perf_counter()
     if decode:
-        conv1d.conv1d_decode(d["x"], d["state"], d["w"])
-    else:
-        conv1d.conv1d_prefill(d["x"], d["w"])
-    dt = time.perf_counter() - t0
-    if decode:
-        return {"value": 1.0 / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
-                "sample": "one decode step at B=%d, C=%d, K=%d, numpy fp64, %.3f s"
-                          % (cw.B, cw.C, cw.K, dt)}
-    return {"value": cw.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "one of the %d batch rows (C=%d channels x T=%d tokens, K=%d), numpy fp64, "
-                      "%.2f s" % (cw.B, cw.C, cw.T, cw.K, dt)}
+        reps, dt = _repeat_for(lambda: conv1d.conv1d_decode(d["x"], d["state"], d["w"]), 2.0, 200)
+        return {"value": reps / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
+                "sample": "%d decode steps at B=%d, C=%d, K=%d, numpy fp64, %.1f s"
+                          % (reps, cw.B, cw.C, cw.K, dt)}
+    reps, dt = _repeat_for(lambda: conv1d.conv1d_prefill(d["x"], d["w"]), 2.0, 16)
+    return {"value": reps * cw.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d batch rows of the %d (C=%d channels x T=%d tokens each, K=%d), numpy "
+                      "fp64, %.1f s" % (reps, cw.B, cw.C, cw.T, cw.K, dt)}
 
 
 def main():
