@@ -42,6 +42,44 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_header_is_c99_and_links(lib, tmp_path):
+    """A plain C caller: gdn.h compiles as strict C99, every function it
+    declares resolves against libgdn.so at link time, and the calls that need
+    no GPU run (version, status strings, workspace query)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = tmp_path / "caller.c"
+    src.write_text("\n".join([
+        "#include <stdio.h>",
+        "#include <string.h>",
+        '#include "gdn.h"',
+        "typedef void (*fn_t)(void);",
+        "int main(void) {",
+        "    const fn_t fns[] = {" + ", ".join("(fn_t)&%s" % n for n in names) + "};",
+        "    for (size_t i = 0; i < sizeof fns / sizeof fns[0]; ++i)",
+        "        if (!fns[i]) return 2;",
+        "    if (gdn_version() < 100) return 3;",
+        "    if (strcmp(gdn_status_string(GDN_OK), \"\") == 0) return 4;",
+        "    if (gdn_chunked_prefill_workspace_bytes(1, 1, 1, 64, 128, 128, GDN_BF16) != 0) return 5;",
+        '    printf("%d functions linked, version %d\\n", (int)(sizeof fns / sizeof fns[0]), gdn_version());',
+        "    return 0;",
+        "}", ""]))
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(gdn.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", os.path.dirname(HEADER), str(src), "-o", str(exe),
+                        "-L", libdir, "-lgdn", "-Wl,-rpath," + libdir],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "%d functions linked" % len(names) in r.stdout
+
+
 def test_status_strings(lib):
     for code in range(10):
         s = lib.gdn_status_string(code).decode()
