@@ -68,3 +68,26 @@ def test_decode_deterministic():
         torch.cuda.synchronize()
         res.append((torch.stack(outs).view(torch.int16).cpu(), st.cpu()))
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_decode_gqa_equals_repeated_heads():
+    """GQA (Hv = 2 Hk) gives bit for bit what the same step gives with q and k
+    repeated per value head (Hk = Hv)."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    w = inputs.WORKLOADS["decode_b256"]
+    state0, steps = inputs.draw_decode_steps(w, nsteps=1, B=8, Hk=4, Hv=8)
+    d = steps[0]
+    dr = dict(d, q=np.repeat(d["q"], 2, axis=1), k=np.repeat(d["k"], 2, axis=1))
+    res = []
+    for dd in (d, dr):
+        t = upload(dd, "bf16")
+        st = torch.from_numpy(state0).cuda()
+        o = gdn.decode_step(t["q"][:, :, 0].contiguous(), t["k"][:, :, 0].contiguous(),
+                            t["v"][:, :, 0].contiguous(), t["g_log"][:, :, 0].contiguous(),
+                            t["beta"][:, :, 0].contiguous(), w.scale, st)
+        torch.cuda.synchronize()
+        res.append((to_np(o), to_np(st)))
+    log("decode GQA vs repeated heads")
+    assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
+    assert np.array_equal(res[0][1].view(np.uint32), res[1][1].view(np.uint32))

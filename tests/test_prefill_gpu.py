@@ -257,3 +257,24 @@ def test_ragged_split_carry_matches_oracle():
     torch.cuda.synchronize()
     ro, rs = oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], 0.1, d["state"])
     check("ragged split 100+284", "bf16", to_np(torch.cat([o1, o2], dim=2)), ro, to_np(st), rs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gqa_equals_repeated_heads(dtype):
+    """GQA (Hv = 4 Hk: value head h reads key head h / 4) gives bit for bit
+    what the same call gives with q and k repeated per value head (Hk = Hv)."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    G = 4
+    d = inputs.draw_prefill(B=2, Hk=2, Hv=2 * G, S=200, Dk=64, Dv=128, dtype=dtype,
+                            state="normal", seed=(71, 0, 0))
+    dr = dict(d, q=np.repeat(d["q"], G, axis=1), k=np.repeat(d["k"], G, axis=1))
+    res = []
+    for dd in (d, dr):
+        t = upload(dd, dtype)
+        o = gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], 0.125, t["state"])
+        torch.cuda.synchronize()
+        res.append((to_np(o), to_np(t["state"])))
+    log("GQA vs repeated heads", dtype)
+    assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
+    assert np.array_equal(res[0][1].view(np.uint32), res[1][1].view(np.uint32))
