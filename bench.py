@@ -494,8 +494,8 @@ def cpu_baseline_decode(w, steps, state0):
 
 
 def cpu_baseline_conv(inputs, cw, decode):
-    """The conv1d oracle (numpy fp64, one core): prefill on batch rows of the
-    workload (all C channels, all T tokens each), decode on whole steps,
+    """The conv1d oracle (numpy fp64, one core): prefill on one batch row of
+    the workload (all C channels, all T tokens), decode on whole steps, each
     repeated for at least 2 s."""
     from oracle import conv1d
     d = inputs.draw_conv(1 if not decode else cw.B, cw.C, cw.T, cw.K, dtype=cw.dtype,
@@ -507,8 +507,8 @@ def cpu_baseline_conv(inputs, cw, decode):
                           % (reps, cw.B, cw.C, cw.K, dt)}
     reps, dt = _repeat_for(lambda: conv1d.conv1d_prefill(d["x"], d["w"]), 2.0, 16)
     return {"value": reps * cw.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d batch rows of the %d (C=%d channels x T=%d tokens each, K=%d), numpy "
-                      "fp64, %.1f s" % (reps, cw.B, cw.C, cw.T, cw.K, dt)}
+            "sample": "one of the %d batch rows (C=%d channels x T=%d tokens, K=%d), run %d "
+                      "times, numpy fp64, %.1f s" % (cw.B, cw.C, cw.T, cw.K, reps, dt)}
 
 
 def main():
