@@ -278,3 +278,44 @@ def test_gqa_equals_repeated_heads(dtype):
     log("GQA vs repeated heads", dtype)
     assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
     assert np.array_equal(res[0][1].view(np.uint32), res[1][1].view(np.uint32))
+
+
+def test_max_sequence_length_addressing():
+    """The longest accepted sequence, S = 4194239, in fp32 at Dk = Dv = 128:
+    byte offsets within a stream reach 2,147,483,136 (just below 2^31) and the
+    last chunk holds 31 tokens. With beta = 0 and g = 0 the state never
+    changes, so out_t = scale S0^T q_t exactly and the final state is S0 bit
+    for bit: q is zero except at sampled tokens (the first chunks, tokens
+    around the middle, the ragged tail), whose outputs are checked against
+    that closed form in fp64, and a few zero-q tokens must give zeros."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    S, D = 4194239, 128
+    dev = torch.device("cuda", 0)
+    rng = np.random.default_rng(4194239)
+    sample = np.unique(np.concatenate([np.arange(0, 70), S // 2 + np.arange(-40, 40),
+                                       np.arange(S - 100, S), rng.integers(0, S, 60)]))
+    zero_q = np.array([100, S // 3, S - 200])
+    qs = rng.standard_normal((len(sample), D)).astype(np.float32)
+    qs /= np.linalg.norm(qs, axis=1, keepdims=True)
+    s0 = (0.02 * rng.standard_normal((D, D))).astype(np.float32)
+    q = torch.zeros((1, 1, S, D), dtype=torch.float32, device=dev)
+    q[0, 0, torch.from_numpy(sample).to(dev)] = torch.from_numpy(qs).to(dev)
+    k = torch.zeros_like(q)
+    v = torch.zeros_like(q)
+    g = torch.zeros((1, 1, S), dtype=torch.float32, device=dev)
+    beta = torch.zeros_like(g)
+    state = torch.from_numpy(s0.reshape(1, 1, D, D).copy()).to(dev)
+    scale = 1.0 / np.sqrt(D)
+    log("max-length prefill: S", S, "fp32, sampled tokens", len(sample))
+    out = gdn.chunked_prefill(q, k, v, g, beta, scale, state)
+    torch.cuda.synchronize()
+    got = out[0, 0, torch.from_numpy(sample).to(dev)].double().cpu().numpy()
+    ref = scale * qs.astype(np.float64) @ s0.astype(np.float64)
+    err = np.max(np.abs(got - ref) / (np.sqrt(np.mean(ref * ref)) + np.abs(ref)))
+    log("max-length prefill: sampled out err %.3e" % err)
+    assert err <= 1e-4
+    assert torch.count_nonzero(out[0, 0, torch.from_numpy(zero_q).to(dev)]).item() == 0
+    assert np.array_equal(state[0, 0].cpu().numpy().view(np.uint32), s0.view(np.uint32))
+    del q, k, v, out
+    torch.cuda.empty_cache()
