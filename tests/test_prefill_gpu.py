@@ -319,3 +319,39 @@ def test_max_sequence_length_addressing():
     assert np.array_equal(state[0, 0].cpu().numpy().view(np.uint32), s0.view(np.uint32))
     del q, k, v, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_exact_key_overwrite(dtype):
+    """g = 0, beta = 1 and orthonormal keys: each step replaces the state's
+    component along k_t by v_t, so with q_t = k_t every output is scale v_t
+    exactly, whatever the initial state (the delta rule's overwrite property;
+    in the chunked form A = 0, T = I and P = scale I)."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    S, D = 96, 128
+    rng = np.random.default_rng(96)
+    qm, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    kk = qm[:S].astype(np.float32)                      # S orthonormal rows
+    if dtype == "bf16":                                  # exact bf16 keys stay near-orthonormal
+        kk = inputs.bf16_round(kk)
+    v = rng.standard_normal((1, 1, S, D)).astype(np.float32)
+    if dtype == "bf16":
+        v = inputs.bf16_round(v)
+    d = {"q": kk[None, None].copy(), "k": kk[None, None].copy(), "v": v,
+         "g_log": np.zeros((1, 1, S), np.float32), "beta": np.ones((1, 1, S), np.float32),
+         "state": (0.5 * rng.standard_normal((1, 1, D, D))).astype(np.float32)}
+    t = upload(d, dtype)
+    scale = 0.25
+    out = gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], scale, t["state"])
+    torch.cuda.synchronize()
+    ref = scale * v.astype(np.float64)
+    if dtype == "bf16":
+        # bf16 keys are orthonormal only to ~1e-3 (their rounding); the oracle
+        # on the same inputs bounds the rounding part
+        ro, _ = oracle.gdn_serial(d["q"], d["k"], d["v"], d["g_log"], d["beta"], scale, d["state"])
+        log("overwrite: oracle vs scale v %.3e" % np.max(np.abs(ro - ref)))
+        ref = ro
+    err = np.max(np.abs(to_np(out) - ref) / (np.sqrt(np.mean(ref * ref)) + np.abs(ref)))
+    log("exact key overwrite %s: out err %.3e" % (dtype, err))
+    assert err <= (1e-4 if dtype == "f32" else 2e-2)
