@@ -438,7 +438,18 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             acc3[1] = O::mma(k1, k0, acc3[1]);
             acc3[2] = O::mma(k1, k1, acc3[2]);
         }
-        TileScalars ts = tile_scalars(sc, Cf::SC_B, -1, -1);
+        const TileScalars ts = tile_scalars(sc, Cf::SC_B, -1, -1);
+        // decay factors first (they do not depend on the norms), then on the
+        // GATED path rk from the diagonal tiles: the wave does not stall on
+        // that chain before the exponentials are issued.
+        // lane (lr/4, lc) holds rows r = lr + e, column s = lc of each tile
+        f32x4 d11, d21, d22;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            d11[e] = ts.br[0][e] * __expf((ts.gr[0][e] - ts.gs[0]) + (ts.grl[0][e] - ts.gsl[0])) * ts.cs[0];
+            d21[e] = ts.br[1][e] * __expf((ts.gr[1][e] - ts.gs[0]) + (ts.grl[1][e] - ts.gsl[0])) * ts.cs[0];
+            d22[e] = ts.br[1][e] * __expf((ts.gr[1][e] - ts.gs[1]) + (ts.grl[1][e] - ts.gsl[1])) * ts.cs[1];
+        }
         if constexpr (GATED) {
             // A[r][s] carries rk_r rk_s; rk is folded into the chunk's beta
             // e^gamma and e^{gamma_C - gamma} (lane l < C: token l, whose
@@ -447,10 +458,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             const f32x4 dg[2] = {acc3[0], acc3[2]};
             const NormF rk = norm_factors(dg, S - c * C, true);
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                ts.cs[ti] *= rk.col[ti];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ts.br[ti][e] *= rk.row[ti][e];
+            for (int e = 0; e < 4; ++e) {
+                d11[e] *= rk.row[0][e] * rk.col[0];
+                d21[e] *= rk.row[1][e] * rk.col[0];
+                d22[e] *= rk.row[1][e] * rk.col[1];
             }
             if (l < C) {
                 const float rkl = l < 16 ? rk.col[0] : rk.col[1];
@@ -459,24 +470,18 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 sc[Cf::SC_DL + l] *= rkl;
             }
         }
-        // lane (lr/4, lc) holds rows r = lr + e, column s = lc of each tile
         f32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {   // A11, stored transposed: [s][r], one vector per lane
-            const float dec = __expf((ts.gr[0][e] - ts.gs[0]) + (ts.grl[0][e] - ts.gsl[0])) * ts.cs[0];
-            w[e] = (lc < lr + e) ? ts.br[0][e] * dec * acc3[0][e] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e)     // A11, stored transposed: [s][r], one vector per lane
+            w[e] = (lc < lr + e) ? d11[e] * acc3[0][e] : 0.f;
         *(f32x4*)(sA + Cf::AB_11T + lc * ALD + lr) = w;
         // A22 reversed: entry [15 - r][15 - s], rows 15 - lr - e = (12 - lr) + (3 - e)
         __attribute__((address_space(3))) float* a22r = lds_ptr<float>(
             opaque_base(lds_addr(sA) + (uint32_t)((Cf::AB_22R + (12 - lr) * ALD + 15 - lc) * 4)));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // A21 row-major: [r][s]
-            const float d21 = __expf((ts.gr[1][e] - ts.gs[0]) + (ts.grl[1][e] - ts.gsl[0])) * ts.cs[0];
-            sA[Cf::AB_21 + (lr + e) * ALD + lc] = ts.br[1][e] * d21 * acc3[1][e];
-            const float d22 = __expf((ts.gr[1][e] - ts.gs[1]) + (ts.grl[1][e] - ts.gsl[1])) * ts.cs[1];
-            a22r[(3 - e) * ALD] = (lc < lr + e) ? ts.br[1][e] * d22 * acc3[2][e] : 0.f;
+            sA[Cf::AB_21 + (lr + e) * ALD + lc] = d21[e] * acc3[1][e];   // A21 row-major: [r][s]
+            a22r[(3 - e) * ALD] = (lc < lr + e) ? d22[e] * acc3[2][e] : 0.f;
         }
     };
 
@@ -719,48 +724,60 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             }
         // The scalars' "row" arrays index keys and "column" arrays queries
         // (tiles of K Q^T below): rk for the rows, rq for the columns.
-        TileScalars ts = tile_scalars(sc, (GATED && Cf::SPREAD) ? Cf::SC_RK : -1, -1, -1);
+        const TileScalars ts = tile_scalars(sc, (GATED && Cf::SPREAD) ? Cf::SC_RK : -1, -1, -1);
+        // GATED: the diagonal Q Q^T tiles for rq (and, on the fp32 path, K K^T
+        // for rk) are issued first; their factors are formed after the tile
+        // products and the decays, which do not depend on them, so the wave
+        // does not stall on that chain before issuing independent work.
+        f32x4 dq[2] = {zero4(), zero4()}, dk[2] = {zero4(), zero4()};
         if constexpr (GATED) {
-            f32x4 dq[2] = {zero4(), zero4()};
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-                for (int m = 0; m < NKS; ++m) dq[ti] = O::mma(qf[ti][m], qf[ti][m], dq[ti]);
-            const NormF rq = norm_factors(dq, S - c * C, false);
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti) ts.cs[ti] *= rq.col[ti];
-            if constexpr (!Cf::SPREAD) {
-                f32x4 dk[2] = {zero4(), zero4()};
-#pragma unroll
-                for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-                    for (int m = 0; m < NKS; ++m) dk[ti] = O::mma(kf[ti][m], kf[ti][m], dk[ti]);
-                const NormF rk = norm_factors(dk, S - c * C, true);
-#pragma unroll
-                for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ts.br[ti][e] *= rk.row[ti][e];
-            }
-            if (l < C) sc[Cf::SC_EG + l] *= l < 16 ? rq.col[0] : rq.col[1];
+                for (int m = 0; m < NKS; ++m) {
+                    dq[ti] = O::mma(qf[ti][m], qf[ti][m], dq[ti]);
+                    if constexpr (!Cf::SPREAD) dk[ti] = O::mma(kf[ti][m], kf[ti][m], dk[ti]);
+                }
         }
         // Tiles of (Q K^T)^T = K Q^T: lane (lr/4, lc) holds keys s = 16 tj + lr + e
         // of query row r = 16 ti + lc, which are adjacent in P's row layout
         // (tpos(s) = 8 (lr/4) + 4 tj + e), so each tile is stored as one
         // 8-byte vector per lane (hi and, on the bf16 path, lo).
+        f32x4 acc[3], dec[3];
 #pragma unroll
         for (int tt = 0; tt < 3; ++tt) {
             const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
-            f32x4 acc = zero4();
+            acc[tt] = zero4();
 #pragma unroll
-            for (int m = 0; m < NKS; ++m) acc = O::mma(kf[tj][m], qf[ti][m], acc);
+            for (int m = 0; m < NKS; ++m) acc[tt] = O::mma(kf[tj][m], qf[ti][m], acc[tt]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dec[tt][e] = scale * ts.br[tj][e] * ts.cs[ti] *
+                             __expf((ts.gs[ti] - ts.gr[tj][e]) + (ts.gsl[ti] - ts.grl[tj][e]));
+        }
+        float colf[2] = {1.f, 1.f}, rowf[2][4] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
+        if constexpr (GATED) {
+            const NormF rq = norm_factors(dq, S - c * C, false);
+            colf[0] = rq.col[0];
+            colf[1] = rq.col[1];
+            if constexpr (!Cf::SPREAD) {
+                const NormF rk = norm_factors(dk, S - c * C, true);
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rowf[ti][e] = rk.row[ti][e];
+            }
+            if (l < C) sc[Cf::SC_EG + l] *= l < 16 ? rq.col[0] : rq.col[1];
+        }
+#pragma unroll
+        for (int tt = 0; tt < 3; ++tt) {
+            const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
             const int r = 16 * ti + lc;
             f32x4 pv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s2 = 16 * tj + lr + e;
-                const float dec = __expf((ts.gs[ti] - ts.gr[tj][e]) + (ts.gsl[ti] - ts.grl[tj][e])) *
-                                  (ts.br[tj][e] * ts.cs[ti]);
-                pv[e] = (s2 <= r) ? scale * dec * acc[e] : 0.f;
+                pv[e] = (s2 <= r) ? dec[tt][e] * (colf[ti] * rowf[tj][e]) * acc[tt][e] : 0.f;
             }
             E* dst = Pp + r * LDP + 8 * (lr >> 2) + 4 * tj;
             if constexpr (SP) {
