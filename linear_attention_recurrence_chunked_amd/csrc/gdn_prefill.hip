@@ -187,6 +187,28 @@ __device__ __forceinline__ float softplus_f(float x) {
     return fmaxf(x, 0.f) + lp;
 }
 
+// DPP controls (GFX9 encoding): row shift right by n = kDppRowShr + n, and
+// lane 15 of each row broadcast to the next row.
+constexpr int kDppRowShr = 0x110, kDppRowBcast15 = 0x142;
+
+// x of the lane that DPP control CTRL selects, in the rows of ROW_MASK; 0 in
+// lanes without a source or outside ROW_MASK.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// x of lane `lane` (uniform), through scalar registers.
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Element e (0..3, lane-dependent) of v, by selection (no indexed register access).
 __device__ __forceinline__ float pick4(f32x4 v, int e) {
     return e == 0 ? v[0] : e == 1 ? v[1] : e == 2 ? v[2] : v[3];
@@ -318,13 +340,16 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         // decay between close tokens is a difference of two such sums. gamma
         // is kept as an fp32 pair (value, rest); e^{gamma_C - gamma} comes from
         // the fp64 difference.
+        // The scan runs in registers with DPP moves: shifts by 1, 2, 4, 8 within
+        // each row of 16 lanes, then row 0's total added to row 1 (lanes past
+        // the chunk hold 0), instead of lane shuffles through the LDS crossbar.
         double xd = l < C ? (double)gl : 0.0;
-#pragma unroll
-        for (int off = 1; off < C; off <<= 1) {
-            const double y = __shfl_up(xd, off);
-            if (l >= off) xd += y;
-        }
-        const double gCd = __shfl(xd, C - 1);
+        xd += dpp_f64<kDppRowShr + 1, 0xf>(xd);
+        xd += dpp_f64<kDppRowShr + 2, 0xf>(xd);
+        xd += dpp_f64<kDppRowShr + 4, 0xf>(xd);
+        xd += dpp_f64<kDppRowShr + 8, 0xf>(xd);
+        xd += dpp_f64<kDppRowBcast15, 0xa>(xd);
+        const double gCd = readlane_f64(xd, C - 1);
         const float x = (float)xd;
         if (l < C) {
             const float eg = __expf(x);
