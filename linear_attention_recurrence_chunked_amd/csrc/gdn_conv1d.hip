@@ -17,7 +17,7 @@
 // (two on the fp32 path), so a wave's load covers 1 KiB contiguously; all
 // four loads are issued before any use (64 bytes per thread in flight). The
 // K-1 tokens of history a thread needs are the last ones of the previous
-// lane's 8, passed by a lane shuffle; lane 0 of each wave reads them from
+// lane's 8, passed by a DPP whole-wave shift; lane 0 of each wave reads them from
 // memory (the previous wave's range: cache hits, except at the first wave of
 // a group). The taps are a template parameter so the filter window stays in
 // registers. Measured on MI355X at B=4, C=8192, T=8192, bf16: 5.4 TB/s,
@@ -34,6 +34,14 @@ constexpr int kConvThreads = 256;
 constexpr int kConvNE = 8;                         // tokens per vector
 constexpr int kConvNV = 4;                         // vectors per thread
 constexpr int kConvTile = kConvThreads * kConvNE * kConvNV;  // tokens per workgroup
+
+// x of the previous lane of the wave (0 in lane 0): a DPP whole-wave shift,
+// in registers rather than through the LDS crossbar.
+__device__ __forceinline__ float lane_shr1(float x) {
+    constexpr int kDppWaveShr1 = 0x138;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), kDppWaveShr1, 0xf, 0xf, false));
+}
 
 __device__ __forceinline__ float silu_f(float y) {
     return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
@@ -113,7 +121,7 @@ __global__ __launch_bounds__(kConvThreads) void gdn_conv1d_prefill_kernel(
         const int tv = tile * kConvTile + kConvNE * (kConvThreads * v + (int)threadIdx.x);
         float prev[kConvNE];
 #pragma unroll
-        for (int e = 0; e < kConvNE; ++e) prev[e] = __shfl_up(cur[v][e], 1);
+        for (int e = 0; e < kConvNE; ++e) prev[e] = lane_shr1(cur[v][e]);
         if (lane == 0) {
             if (tv >= kConvNE) load8<E, ALIGNED>(xr + tv - kConvNE, kConvNE, prev);
             else {
