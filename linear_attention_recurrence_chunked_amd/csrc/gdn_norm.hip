@@ -24,6 +24,30 @@
 namespace gdn {
 
 constexpr int kNormThreads = 256;
+
+// DPP permutation of x within rows of 16 lanes (GFX9 controls).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum of x over each aligned group of P lanes, in every lane of the group.
+// Within a row of 16 lanes the partners come from DPP moves in registers:
+// swap neighbours, swap pairs (quad permutations), then mirror the halves of
+// 8 and the row of 16, each pairing two partial sums of equal size. Groups of
+// 32 add the other row by a lane shuffle.
+template <int P>
+__device__ __forceinline__ float row_sum(float x) {
+    constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+    if constexpr (P >= 2) x += dpp_f32<kQuadSwap1>(x);
+    if constexpr (P >= 4) x += dpp_f32<kQuadSwap2>(x);
+    if constexpr (P >= 8) x += dpp_f32<kRowHalfMirror>(x);
+    if constexpr (P >= 16) x += dpp_f32<kRowMirror>(x);
+    if constexpr (P >= 32) x += __shfl_xor(x, 16);
+    static_assert(P <= 32, "row width");
+    return x;
+}
 constexpr int kNormNR = 2;          // rows per thread (1 and 4 measured slower)
 
 template <typename E, int P, int HT>
@@ -35,6 +59,7 @@ __global__ __launch_bounds__(kNormThreads) void gdn_rmsnorm_gated_kernel(
     constexpr int RW = kNormThreads / P;               // rows per pass of the workgroup
     constexpr int TT = kNormNR * RW / HT;              // tokens per tile
     typedef typename std::conditional<sizeof(E) == 2, bf16x8, f32x4>::type V;
+    const float inv_dv = 1.f / (float)Dv;
     const int li = threadIdx.x % P;
     const int c0 = li * VE;
     // grid: x = token tile, y = head tile, z = batch (from b0)
@@ -63,10 +88,11 @@ __global__ __launch_bounds__(kNormThreads) void gdn_rmsnorm_gated_kernel(
             ov[e] = act[n] ? to_f32(a[n][e]) : 0.f;
             ss += ov[e] * ov[e];
         }
-#pragma unroll
-        for (int m = 1; m < P; m <<= 1) ss += __shfl_xor(ss, m);
+        ss = row_sum<P>(ss);
         if (!act[n]) continue;
-        const float r = 1.f / sqrtf(ss / (float)Dv + eps);
+        // 1/sqrt(mean + eps): mean by the reciprocal of Dv (exact for powers of
+        // two), hardware reciprocal square root (about 1 ulp)
+        const float r = __builtin_amdgcn_rsqf(ss * inv_dv + eps);
         V y;
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
