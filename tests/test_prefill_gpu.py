@@ -355,3 +355,36 @@ def test_exact_key_overwrite(dtype):
     err = np.max(np.abs(to_np(out) - ref) / (np.sqrt(np.mean(ref * ref)) + np.abs(ref)))
     log("exact key overwrite %s: out err %.3e" % (dtype, err))
     assert err <= (1e-4 if dtype == "f32" else 2e-2)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_repeat_launches_bitwise_at_bench_size(gated):
+    """20 launches of the bench workload (B = 4, Hk = 16, Hv = 32, S = 8192)
+    from the same inputs give bitwise the same output and state: a race
+    between the waves of a workgroup (the consumers pass the per-chunk
+    barrier without waiting for their reads of the next chunk) would show as
+    run-to-run differences here."""
+    import torch
+    import linear_attention_recurrence_chunked_amd as gdn
+    from gpu_helpers import upload_raw
+    w = W["prefill_b4_s8192"]
+    d = inputs.draw_workload(w, raw=True)
+    t = upload_raw(d, "bf16") if gated else upload(d, "bf16")
+    st0 = t["state"].clone()
+    out = torch.empty((w.B, w.Hv, w.S, w.Dv), dtype=torch.bfloat16, device="cuda")
+    ref_o = ref_s = None
+    for rep in range(20):
+        st = st0.clone()
+        if gated:
+            gdn.chunked_prefill_gated(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"],
+                                      t["dt_bias"], w.scale, 1e-6, st, out=out)
+        else:
+            gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], w.scale, st,
+                                out=out)
+        if rep == 0:
+            ref_o, ref_s = out.clone(), st.clone()
+        else:
+            assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), "run %d out" % rep
+            assert torch.equal(st.view(torch.int32), ref_s.view(torch.int32)), "run %d state" % rep
+    torch.cuda.synchronize()
+    log("20 launches bitwise identical, gated" if gated else "20 launches bitwise identical")
