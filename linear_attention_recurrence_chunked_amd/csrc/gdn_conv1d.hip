@@ -122,7 +122,10 @@ __global__ __launch_bounds__(kConvThreads) void gdn_conv1d_prefill_kernel(
         float prev[kConvNE];
 #pragma unroll
         for (int e = 0; e < kConvNE; ++e) prev[e] = lane_shr1(cur[v][e]);
-        if (lane == 0) {
+        // lane 0 reads the 8 tokens before its vector from memory, only when
+        // that vector is in the row (tv < T, so those 8 are too; a wave past
+        // the end of the row must not read beyond it)
+        if (lane == 0 && tv < T) {
             if (tv >= kConvNE) load8<E, ALIGNED>(xr + tv - kConvNE, kConvNE, prev);
             else {
 #pragma unroll
