@@ -48,7 +48,7 @@ __device__ __forceinline__ float row_sum(float x) {
     static_assert(P <= 32, "row width");
     return x;
 }
-constexpr int kNormNR = 2;          // rows per thread (1 and 4 measured slower)
+constexpr int kNormNR = 4;          // rows per thread (1, 2 and 8 measured slower)
 
 template <typename E, int P, int HT>
 __global__ __launch_bounds__(kNormThreads) void gdn_rmsnorm_gated_kernel(
@@ -76,7 +76,9 @@ __global__ __launch_bounds__(kNormThreads) void gdn_rmsnorm_gated_kernel(
         row[n] = (b * S + s) * Hv + h;                 // token-major z / y row
         const long long orow = (b * Hv + h) * S + s;   // head-major o row
         if (act[n]) {
-            a[n] = *(const V*)(o + orow * Dv + c0);
+            // o is read by this pass only: a non-temporal load (0.139 -> 0.119 ms
+            // with four rows per thread; the same hint on z measured slower)
+            a[n] = __builtin_nontemporal_load((const V*)(o + orow * Dv + c0));
             g[n] = *(const V*)(z + row[n] * Dv + c0);
         }
     }

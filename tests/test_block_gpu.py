@@ -25,11 +25,13 @@ def _round(x, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("Dv", [16, 48, 64, 128])
-def test_rmsnorm_gated(dtype, Dv):
+@pytest.mark.parametrize("B,Hv,S", [(2, 3, 37), (1, 8, 37)])
+def test_rmsnorm_gated(dtype, Dv, B, Hv, S):
+    """Hv = 3: one head per tile; Hv = 8: tiles of four heads. S = 37 leaves
+    a partial token tile either way."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    r = np.random.default_rng([300, Dv])
-    B, Hv, S = 2, 3, 37
+    r = np.random.default_rng([300, Dv, Hv])
     o = _round(r.standard_normal((B, Hv, S, Dv)).astype(np.float32) * 3.0, dtype)
     z = _round(r.standard_normal((B, S, Hv, Dv)).astype(np.float32), dtype)
     w = (1.0 + 0.1 * r.standard_normal(Dv)).astype(np.float32)
@@ -37,7 +39,7 @@ def test_rmsnorm_gated(dtype, Dv):
     torch.cuda.synchronize()
     ry = ref.rmsnorm_gated(np.transpose(o, (0, 2, 1, 3)), z, w, 1e-5)
     e = rel_err(to_np(y), ry)
-    log("rmsnorm", dtype, Dv, "err %.3e" % e)
+    log("rmsnorm", dtype, Dv, B, Hv, S, "err %.3e" % e)
     assert e <= TOL[dtype]["out"], e
 
 
