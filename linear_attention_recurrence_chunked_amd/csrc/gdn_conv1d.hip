@@ -20,9 +20,10 @@
 // lane's 8, passed by a DPP whole-wave shift; lane 0 of each wave reads them from
 // memory (the previous wave's range: cache hits, except at the first wave of
 // a group). The taps are a template parameter so the filter window stays in
-// registers. Measured on MI355X at B=4, C=8192, T=8192, bf16: 5.4 TB/s,
-// against 5.0 TB/s with each thread's 16 or 32 tokens contiguous, and
-// non-temporal stores were slower still.
+// registers. Measured on MI355X at B=4, C=8192, T=8192, bf16: 5.7 TB/s
+// (5.4 TB/s for this layout before the DPP shift and the 2-D grid, against
+// 5.0 TB/s with each thread's 16 or 32 tokens contiguous); non-temporal
+// loads or stores, and two vectors per thread, were slower.
 // Decode: one thread per (batch, channel); the window row is read and written
 // as one vector where its size allows.
 #include "gdn_common.h"
