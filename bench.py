@@ -7,47 +7,53 @@
 One step = one ``gdn_chunked_prefill`` call on the batched long prefill
 workload (B=4, Hk=16, Hv=32, Dk=Dv=128, S=8192, bf16 q/k/v, fp32 g/beta and
 state, state carried in place from step to step). All inputs are seeded,
-synthetic and resident in HBM before timing starts. W untimed warm-up steps,
-then exactly K timed steps bracketed by device synchronisation; each launch is
-also bracketed by HIP events on the launch stream to get the kernel's own
-duration for the roofline.
+synthetic and resident in HBM before timing starts. W untimed warm-up steps
+and a settling phase (further calls until the device has been busy for at
+least 300 ms: the GPU needs ~100 ms of load to reach its steady clocks, and
+the host-side input draws between sections let them drop), then exactly K
+timed steps bracketed by device synchronisation; each launch is also
+bracketed by HIP events on the launch stream to get the kernel's own duration
+for the roofline. The shader clock (amdsmi) is sampled during the headline's
+settling phase and reported under "sclk".
 
 The decode path (B=256 single-token steps, 64 autoregressive steps with fresh
 inputs) is measured the same way in the same run -- K/10 timed passes of 64
-steps after W/10 warm-up passes -- and reported under "decode". It runs
-first: the GPU takes ~100 ms under load to reach steady clocks (measured:
-3 prefill warm-up steps leave the timed steps ~20 % slow), and the decode
-passes supply that load before the prefill's own warm-up. Prints ONE JSON line.
+steps -- and reported under "decode".
 
 The gated entry points (gate and L2-norm prologue on the device, raw q/k and
 gate pre-activations as inputs) are timed the same way on the same workloads
-and reported under "prefill_gated" and "decode_gated"; the depthwise conv1d
-that precedes them (prefill over the B=4, T=8192 mixed q|k|v tensor with
-C = 8192 channels and K = 4 taps; one decode token at B=256) under
-"conv1d_prefill" and "conv1d_decode"; the RMSNormGated epilogue over the
-prefill output under "rmsnorm_gated"; the fused decode block (conv1d step,
-prologue, recurrence, RMSNormGated; B=256, K=4) under "decode_block".
-The conv1d decode call lasts less than the host's launch gap; its kernel
-time comes from 10 calls captured in a HIP graph and replayed back to back.
+and reported under "prefill_gated" and "decode_gated"; the single-sequence
+prefill workloads (B=1: S=2048 from a zero state; S=65536 from a carried
+state, standard and strong decay) under "prefill_s2048" and
+"prefill_s65536"; the depthwise conv1d that precedes the recurrence (prefill
+over the B=4, T=8192 mixed q|k|v tensor with C = 8192 channels and K = 4
+taps; one decode token at B=256) under "conv1d_prefill" and "conv1d_decode";
+the RMSNormGated epilogue over the prefill output under "rmsnorm_gated"; the
+fused decode block (conv1d step, prologue, recurrence, RMSNormGated; B=256,
+K=4) under "decode_block". The conv1d decode call lasts less than the host's
+launch gap; its kernel time comes from 10 calls captured in a HIP graph and
+replayed back to back.
 
-``--only inverse_ab`` times the prefill with each intra-chunk inverse (blocked
+Last, "inverse_ab" times the prefill with each intra-chunk inverse (blocked
 substitution, the default, and the Neumann product) at S = 128 .. 8192 with
-the rest of the bench workload fixed: the shape of the pages' only measured
-comparison between inverse methods. It is not part of the default run, which
-launches each kernel at one workload only, so that a profiler's per-kernel
-statistics of the default run are those of the reported workloads.
+the other shapes of the headline workload at batch 2 (other kernel instances
+than the headline's, so that a profiler's per-kernel statistics of the run
+keep them apart): the shape of the pages' only measured comparison between
+inverse methods.
 
 ``--only copy`` runs a plain device-to-device copy of ``--copy-mib`` MiB
 (used to calibrate the HBM byte counters of rocprofv3 against a kernel of
-known traffic); ``--only prefill|decode`` runs one path alone.
+known traffic); ``--only <section>`` runs one section alone.
 
 Roofline (per launch, algorithmic, see the workload docstrings below):
 * prefill: HBM bytes = tokens x (q + k + v + out + g + beta) + state in/out;
-  algorithmic MFMA flops reported as "mfma_util" against the bf16 dense peak,
-  and under "mfma_util.counter" the issued bf16 MFMA flops that rocprofv3
-  counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, committed summary) over this
-  run's launch time, with the MFMA busy fraction and shader clock measured
-  with them.
+  algorithmic MFMA flops (a fixed count of the method's work at 64-token
+  chunks, 4.24 MFLOP per token on the headline shapes) reported as
+  "mfma_util" against the bf16 dense peak, the same count at the kernel's own
+  32-token chunks beside it, and under "mfma_util.counter" the issued bf16
+  MFMA flops that rocprofv3 counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512,
+  committed summary) over this run's launch time, with the MFMA busy fraction
+  and shader clock measured with them.
 * decode: HBM bytes = 2 x fp32 state + q, k, v, out, g, beta.
 """
 import argparse
@@ -67,16 +73,18 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "GDN prefill tokens/s + MFMA util (S=8192); decode steps/s + HBM GB/s"
 
 
-def prefill_algorithmic(B, Hk, Hv, S, Dk, Dv, esize=2, chunk=32):
+def prefill_algorithmic(B, Hk, Hv, S, Dk, Dv, esize=2, chunk=64):
     """Algorithmic HBM bytes and MFMA flops of one prefill call.
 
     bytes: q, k [B,Hk,S,Dk] + v, out [B,Hv,S,Dv] in the operand type, g and
     beta fp32 [B,Hv,S], the fp32 state read once and written once.
     flops (per value head and chunk of C tokens; lower-triangular products
-    counted at half size; K K^T and Q K^T shared inside a GQA group; C is the
-    kernel's chunk length, 32):
+    counted at half size; K K^T and Q K^T shared inside a GQA group):
       W = T K and U~ = T V: C^2 (Dk + Dv); W S, Q S, K^T U: 3 x 2 C Dk Dv;
       P U: C^2 Dv; T: C^3 / 3; per key head: K K^T, Q K^T: 2 x C^2 Dk.
+    The reported utilisation uses C = 64, a fixed count of the method's work
+    (4.24 MFLOP per token at Hk=16, Hv=32, Dk=Dv=128) that does not depend on
+    the kernel's own chunk length (32, whose count is reported beside it).
     """
     tokens = B * S
     nbytes = (tokens * (2 * Hk * Dk + 2 * Hv * Dv) * esize + tokens * Hv * 8
@@ -87,6 +95,9 @@ def prefill_algorithmic(B, Hk, Hv, S, Dk, Dv, esize=2, chunk=32):
     nchunks = B * S / C
     flops = nchunks * (Hv * per_chunk_vh + Hk * per_chunk_kh)
     return float(nbytes), float(flops)
+
+
+KERNEL_CHUNK = 32              # the prefill kernel's own chunk length
 
 
 def decode_algorithmic(B, Hk, Hv, Dk, Dv, esize=2):
@@ -157,17 +168,99 @@ def mfma_counters(kernel, kern_ms):
             "source": "profiles/mfma_counters.json"}
 
 
+def mfma_util(flops, kern_ms, w, counter=None):
+    """Algorithmic MFMA utilisation of a prefill launch against the bf16 dense
+    peak (the fixed 64-token count), with the kernel's own 32-token count and
+    the counter-based issue rate beside it."""
+    kflops = prefill_algorithmic(w.B, w.Hk, w.Hv, w.S, w.Dk, w.Dv, chunk=KERNEL_CHUNK)[1]
+    rate = lambda f: f / (kern_ms / 1e3) / 1e12
+    return {"achieved_tflops": rate(flops), "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": rate(flops) / BF16_PEAK_TFLOPS,
+            "algorithmic_flops_per_launch": flops,
+            "flops_per_token": flops / (w.B * w.S),
+            "count": "chunk length 64, triangles at half size, K K^T and Q K^T once per key head",
+            "kernel_chunk32": {"flops_per_launch": kflops, "frac": rate(kflops) / BF16_PEAK_TFLOPS,
+                               "note": "the same count at the kernel's own 32-token chunks"},
+            "counter": counter}
+
+
+def clock_record(clocks):
+    """The shader clock samples taken while the headline prefill settled."""
+    if not clocks:
+        return None
+    c = np.asarray(clocks, dtype=np.float64)
+    return {"median_mhz": float(np.median(c)), "min_mhz": float(c.min()),
+            "max_mhz": float(c.max()), "samples": int(c.size),
+            "source": "amdsmi current gfx clock (torch.cuda.clock_rate), sampled between "
+                      "batches of the settling calls right before the timed prefill calls"}
+
+
+def long_section(row, hbm):
+    """Bench-line section of a single-sequence prefill workload."""
+    wl, lms, lkern, lbytes, lflops = row
+    tokens = wl.B * wl.S
+    return {"workload": wl.name, "B": wl.B, "Hk": wl.Hk, "Hv": wl.Hv, "S": wl.S, "Dk": wl.Dk,
+            "Dv": wl.Dv, "state": "zero" if wl.state == "zero" else "N(0, 0.02^2), carried",
+            "value": tokens / (lms / 1e3), "unit": "tokens/s", "ms_per_step": lms,
+            "roofline": dict(bound="hbm", kernel="gdn_prefill_kernel (B=1 instance)",
+                             traffic=None, **hbm(lbytes, lkern)),
+            "mfma_util": mfma_util(lflops, lkern, wl)}
+
+
 def _events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(n)]
 
 
 L2_EPS = 1e-6                  # epsilon of the gated entry points' q/k normalisation
+SETTLE_MS = 300.0              # minimum busy time before each timed region
 
 
-def bench_prefill(torch, gdn, w, d, steps, warmup, gated=False):
+def progress(msg):
+    """One line on stderr per finished section (the JSON line goes to stdout)."""
+    print("bench: " + msg, file=sys.stderr, flush=True)
+
+
+def _clock_mhz(torch):
+    """Current shader (gfx) clock of device 0 in MHz as amdsmi reports it, or
+    None where that query is unavailable."""
+    try:
+        return float(torch.cuda.clock_rate(0))
+    except Exception:
+        return None
+
+
+def settle(torch, step, warmup, min_ms=SETTLE_MS, clocks=None):
+    """The W warm-up calls, then further calls until the device has been busy
+    for at least ``min_ms`` of wall time: the GPU needs ~100 ms of load to
+    reach its steady clocks, and the host work between timed sections (input
+    draws) lets them drop again. With ``clocks`` (a list), the shader clock is
+    sampled between batches of calls and appended. Returns the number of calls."""
+    for i in range(warmup):
+        step(i)
+    n = warmup
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        for i in range(8):
+            step(i)
+        n += 8
+        if clocks is not None:
+            c = _clock_mhz(torch)
+            if c is not None:
+                clocks.append(c)
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= min_ms:
+                return n
+
+
+
+
+def bench_prefill(torch, gdn, w, d, steps, warmup, gated=False, clocks=None):
     """Times the prefill on the draw ``d`` (ungated: normalised q/k, g_log,
-    beta; gated: the raw q/k, a, b, A_log, dt_bias of the same draw)."""
+    beta; gated: the raw q/k, a, b, A_log, dt_bias of the same draw) with the
+    shapes of ``w``; the state is carried from call to call."""
     dev = torch.device("cuda", 0)
     keys = (("q_raw", "k_raw", "v", "a", "b", "A_log", "dt_bias") if gated
             else ("q", "k", "v", "g_log", "beta"))
@@ -178,7 +271,7 @@ def bench_prefill(torch, gdn, w, d, steps, warmup, gated=False):
     out = torch.empty((w.B, w.Hv, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(i=0):
         if gated:
             gdn.chunked_prefill_gated(t["q_raw"], t["k_raw"], t["v"], t["a"], t["b"], t["A_log"],
                                       t["dt_bias"], w.scale, L2_EPS, state, out=out,
@@ -187,8 +280,7 @@ def bench_prefill(torch, gdn, w, d, steps, warmup, gated=False):
             gdn.chunked_prefill(t["q"], t["k"], t["v"], t["g_log"], t["beta"], w.scale, state,
                                 out=out, stream=stream)
 
-    for _ in range(warmup):
-        step()
+    settle(torch, step, warmup, clocks=clocks)
     ev = _events(torch, steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -241,8 +333,7 @@ def bench_decode(torch, gdn, w, state0, steps, reps, warmup, gated=False):
             if evs is not None:
                 evs[i][1].record(stream)
 
-    for _ in range(warmup):
-        run64()
+    settle(torch, lambda i: run64(), warmup)
     evs = [_events(torch, len(dev_steps)) for _ in range(reps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -281,12 +372,12 @@ def conv_algorithmic(B, C, T, K, esize=2):
     return float(2 * B * C * T * esize + state + C * K * 4)
 
 
-def bench_conv(torch, gdn, inputs, name, steps, warmup):
+def bench_conv(torch, gdn, workloads, name, steps, warmup):
     """Times the conv1d workload ``name`` (prefill: one call per step;
     decode: one token per step, window state carried)."""
-    w = inputs.CONV_WORKLOADS[name]
+    w = workloads.CONV_WORKLOADS[name]
     decode = w.T == 1
-    d = inputs.draw_conv(w.B, w.C, w.T, w.K, dtype=w.dtype, decode=decode)
+    d = workloads.draw_conv(w.B, w.C, w.T, w.K, dtype=w.dtype, decode=decode)
     dev = torch.device("cuda", 0)
     x = torch.from_numpy(d["x"]).to(dev).to(torch.bfloat16)
     wt = torch.from_numpy(d["w"]).to(dev)
@@ -297,14 +388,13 @@ def bench_conv(torch, gdn, inputs, name, steps, warmup):
         st = torch.empty((w.B, w.C, w.K), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(i=0):
         if decode:
             gdn.conv1d_decode(x, st, wt, out=out, stream=stream)
         else:
             gdn.conv1d_prefill(x, wt, out=out, state=st, stream=stream)
 
-    for _ in range(warmup):
-        step()
+    settle(torch, step, warmup)
     ev = _events(torch, steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -348,10 +438,9 @@ CONV_GRAPH_CALLS = 10
 
 
 def _timed(torch, stream, step, steps, warmup):
-    """W untimed calls, then K calls each bracketed by events on ``stream``;
-    returns (wall ms per call, mean event ms per call)."""
-    for _ in range(warmup):
-        step(0)
+    """W untimed calls and the settling calls, then K calls each bracketed by
+    events on ``stream``; returns (wall ms per call, mean event ms per call)."""
+    settle(torch, step, warmup)
     ev = _events(torch, steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -380,13 +469,13 @@ def bench_rmsnorm(torch, gdn, steps, warmup):
     return dict(B=B, Hv=Hv, S=S, Dv=Dv), ms, kern, nbytes
 
 
-def bench_decode_block(torch, gdn, inputs, steps, warmup):
+def bench_decode_block(torch, gdn, workloads, steps, warmup):
     """The fused decode block at B=256, Hk=16, Hv=32, Dk=Dv=128, K=4, bf16:
     eight seeded token draws cycled, conv windows ping-ponged, state carried."""
     B, Hk, Hv, Dk, Dv, K = 256, 16, 32, 128, 128, 4
     dev = torch.device("cuda", 0)
-    d0 = inputs.draw_block(B, Hk, Hv, Dk, Dv, K)
-    toks = [d0] + [inputs.draw_block(B, Hk, Hv, Dk, Dv, K, step=i, with_state=False)
+    d0 = workloads.draw_block(B, Hk, Hv, Dk, Dv, K)
+    toks = [d0] + [workloads.draw_block(B, Hk, Hv, Dk, Dv, K, step=i, with_state=False)
                    for i in range(1, 8)]
     up = lambda a, bf: torch.from_numpy(a).to(dev).to(torch.bfloat16 if bf else torch.float32)
     dtoks = [{k: up(t[k], k in ("mixed", "z")) for k in ("mixed", "z", "a", "b")} for t in toks]
@@ -410,10 +499,17 @@ def bench_decode_block(torch, gdn, inputs, steps, warmup):
     return dict(B=B, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, K=K), ms, kern, nbytes
 
 
-def bench_inverse_ab(torch, gdn, w, d, steps, warmup, lengths=(128, 512, 2048, 8192)):
-    """Kernel time of the prefill with each inverse method over the first S
-    tokens of the draw ``d`` (state carried, as in the main prefill line)."""
+INVERSE_AB_B = 2               # batch of the inverse-method comparison
+
+
+def bench_inverse_ab(torch, gdn, workloads, w, steps, warmup, lengths=(128, 512, 2048, 8192)):
+    """Kernel time of the prefill with each intra-chunk inverse over the first
+    S tokens of a draw with the shapes of ``w`` at batch INVERSE_AB_B (state
+    carried, as in the main prefill line). The batch differs from the headline
+    workload's so that the kernels timed here are other instances than the
+    headline's, and a profiler's per-kernel statistics keep the two apart."""
     dev = torch.device("cuda", 0)
+    d = workloads.draw_workload(w, B=INVERSE_AB_B)
     rows = []
     for S in lengths:
         t = {k: torch.from_numpy(np.ascontiguousarray(d[k][:, :, :S])).to(dev)
@@ -421,7 +517,7 @@ def bench_inverse_ab(torch, gdn, w, d, steps, warmup, lengths=(128, 512, 2048, 8
         for k in ("q", "k", "v"):
             t[k] = t[k].to(torch.bfloat16)
         state = torch.from_numpy(d["state"]).to(dev)
-        out = torch.empty((w.B, w.Hv, S, w.Dv), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((INVERSE_AB_B, w.Hv, S, w.Dv), dtype=torch.bfloat16, device=dev)
         stream = torch.cuda.current_stream(dev)
         row = {"S": S}
         for name, inv in (("substitution", gdn.GDN_INV_SUBSTITUTION),
@@ -433,7 +529,9 @@ def bench_inverse_ab(torch, gdn, w, d, steps, warmup, lengths=(128, 512, 2048, 8
             row[name + "_ms"] = kern
         row["neumann_over_substitution"] = row["neumann_ms"] / row["substitution_ms"]
         rows.append(row)
-    return rows
+    return {"B": INVERSE_AB_B, "Hk": w.Hk, "Hv": w.Hv, "Dk": w.Dk, "Dv": w.Dv, "rows": rows,
+            "note": "kernel time per call (HIP events); the intra-chunk inverse is blocked "
+                    "forward substitution (default) or a Neumann product"}
 
 
 def bench_copy(torch, mib, steps):
@@ -499,12 +597,12 @@ def cpu_baseline_decode(w, steps, state0):
                       % (reps, "" if reps == 1 else "es", len(steps), w.B, dt)}
 
 
-def cpu_baseline_conv(inputs, cw, decode):
+def cpu_baseline_conv(workloads, cw, decode):
     """The conv1d oracle (numpy fp64, one core): prefill on one batch row of
     the workload (all C channels, all T tokens), decode on whole steps, each
     repeated for at least 2 s."""
     from oracle import conv1d
-    d = inputs.draw_conv(1 if not decode else cw.B, cw.C, cw.T, cw.K, dtype=cw.dtype,
+    d = workloads.draw_conv(1 if not decode else cw.B, cw.C, cw.T, cw.K, dtype=cw.dtype,
                          decode=decode)
     if decode:
         reps, dt = _repeat_for(lambda: conv1d.conv1d_decode(d["x"], d["state"], d["w"]), 2.0, 200)
@@ -536,7 +634,7 @@ def main():
 
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    from linear_attention_recurrence_chunked_amd import inputs
+    import workloads
     gdn.load_library()
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -546,18 +644,17 @@ def main():
         print(json.dumps({"copy": bench_copy(torch, args.copy_mib, args.steps)}), flush=True)
         return
     reps, dwarm = max(1, args.steps // 10), max(1, args.warmup // 10)
-    dw = inputs.WORKLOADS["decode_b256"]
-    w = inputs.WORKLOADS["prefill_b4_s8192"]
+    dw = workloads.WORKLOADS["decode_b256"]
+    w = workloads.WORKLOADS["prefill_b4_s8192"]
     if args.only in ("decode", "decode_gated"):
-        dstate0, dsteps = inputs.draw_decode_steps(dw, raw=True)
+        dstate0, dsteps = workloads.draw_decode_steps(dw, raw=True)
         dms, dkern_ms, dbytes, _ = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm,
                                                 gated=args.only == "decode_gated")
         print(json.dumps({args.only + "_ms_per_step": dms, "kernel_ms": dkern_ms,
                           "GB_s": dbytes / (dkern_ms / 1e3) / 1e9}), flush=True)
         return
     if args.only == "inverse_ab":
-        d = inputs.draw_workload(w)
-        print(json.dumps({"inverse_ab": bench_inverse_ab(torch, gdn, w, d, args.steps,
+        print(json.dumps({"inverse_ab": bench_inverse_ab(torch, gdn, workloads, w, args.steps,
                                                          args.warmup)}), flush=True)
         return
     if args.only == "rmsnorm":
@@ -566,19 +663,19 @@ def main():
               flush=True)
         return
     if args.only == "decode_block":
-        _, ms, kern, nb = bench_decode_block(torch, gdn, inputs, args.steps, args.warmup)
+        _, ms, kern, nb = bench_decode_block(torch, gdn, workloads, args.steps, args.warmup)
         print(json.dumps({"decode_block_ms": ms, "kernel_ms": kern,
                           "GB_s": nb / (kern / 1e3) / 1e9}), flush=True)
         return
     if args.only in ("conv_prefill", "conv_decode"):
         name = {"conv_prefill": "conv_prefill_b4_t8192", "conv_decode": "conv_decode_b256"}
-        cw, cms, ckern_ms, cbytes = bench_conv(torch, gdn, inputs, name[args.only], args.steps,
+        cw, cms, ckern_ms, cbytes = bench_conv(torch, gdn, workloads, name[args.only], args.steps,
                                                args.warmup)
         print(json.dumps({args.only + "_ms_per_step": cms, "kernel_ms": ckern_ms,
                           "GB_s": cbytes / (ckern_ms / 1e3) / 1e9}), flush=True)
         return
     if args.only in ("prefill", "prefill_gated"):
-        d = inputs.draw_workload(w, raw=True)
+        d = workloads.draw_workload(w, raw=True)
         ms_step, kern_ms, _, _ = bench_prefill(torch, gdn, w, d, args.steps, args.warmup,
                                                gated=args.only == "prefill_gated")
         print(json.dumps({args.only + "_ms_per_step": ms_step, "kernel_ms": kern_ms,
@@ -587,20 +684,36 @@ def main():
     # Decode first, then prefill: the GPU needs ~100 ms under load to reach its
     # steady clocks, and the decode passes (with their own warm-up) supply it
     # before the prefill's warm-up steps.
-    dstate0, dsteps = inputs.draw_decode_steps(dw, raw=True)
+    dstate0, dsteps = workloads.draw_decode_steps(dw, raw=True)
     dms, dkern_ms, dbytes, dgraph_ms = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm)
+    progress("decode %.4f ms/step" % dms)
     gdms, gdkern_ms, _, gdgraph_ms = bench_decode(torch, gdn, dw, dstate0, dsteps, reps, dwarm,
                                                   gated=True)
-    d = inputs.draw_workload(w, raw=True)
-    ms_step, kern_ms, nbytes, flops = bench_prefill(torch, gdn, w, d, args.steps, args.warmup)
+    d = workloads.draw_workload(w, raw=True)
+    clocks = []
+    ms_step, kern_ms, nbytes, flops = bench_prefill(torch, gdn, w, d, args.steps, args.warmup,
+                                                    clocks=clocks)
+    progress("prefill %.4f ms/step (kernel %.4f ms)" % (ms_step, kern_ms))
     gms_step, gkern_ms, _, _ = bench_prefill(torch, gdn, w, d, args.steps, args.warmup,
                                              gated=True)
-    cpw, cpms, cpkern, cpbytes = bench_conv(torch, gdn, inputs, "conv_prefill_b4_t8192",
+    progress("prefill gated %.4f ms/step" % gms_step)
+    # The single-sequence workloads (B = 1): S = 2048 from a zero state, and
+    # S = 65536 from a carried state with standard and strong decay.
+    long_rows = {}
+    for wname, variant in (("prefill_s2048", "std"), ("prefill_s65536", "std"),
+                           ("prefill_s65536", "strong")):
+        wl = workloads.WORKLOADS[wname]
+        dl = workloads.draw_workload(wl, variant=variant)
+        lms, lkern, lbytes, lflops = bench_prefill(torch, gdn, wl, dl, args.steps, args.warmup)
+        del dl
+        long_rows[(wname, variant)] = (wl, lms, lkern, lbytes, lflops)
+        progress("%s %s %.4f ms/step" % (wname, variant, lms))
+    cpw, cpms, cpkern, cpbytes = bench_conv(torch, gdn, workloads, "conv_prefill_b4_t8192",
                                             args.steps, args.warmup)
-    cdw, cdms, cdkern, cdbytes = bench_conv(torch, gdn, inputs, "conv_decode_b256",
+    cdw, cdms, cdkern, cdbytes = bench_conv(torch, gdn, workloads, "conv_decode_b256",
                                             10 * args.steps, args.warmup)
     rcfg, rms_ms, rms_kern, rms_bytes = bench_rmsnorm(torch, gdn, args.steps, args.warmup)
-    bcfg, blk_ms, blk_kern, blk_bytes = bench_decode_block(torch, gdn, inputs, args.steps,
+    bcfg, blk_ms, blk_kern, blk_bytes = bench_decode_block(torch, gdn, workloads, args.steps,
                                                            args.warmup)
     tokens = w.B * w.S
     hbm = lambda b, ms: {"achieved": b / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -624,11 +737,8 @@ def main():
                    "state": "fp32 in place, carried across steps"},
         "roofline": dict(bound="hbm", kernel="gdn_prefill_kernel",
                          traffic=measured_traffic("gdn_prefill_kernel"), **hbm(nbytes, kern_ms)),
-        "mfma_util": {"achieved_tflops": flops / (kern_ms / 1e3) / 1e12,
-                      "peak_tflops": BF16_PEAK_TFLOPS,
-                      "frac": flops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
-                      "algorithmic_flops_per_launch": flops,
-                      "counter": mfma_counters("gdn_prefill_kernel", kern_ms)},
+        "mfma_util": mfma_util(flops, kern_ms, w, mfma_counters("gdn_prefill_kernel", kern_ms)),
+        "sclk": clock_record(clocks),
         "decode": {"workload": "decode_b256", "B": dw.B, "Hk": dw.Hk, "Hv": dw.Hv,
                    "value": 1e3 / dms, "unit": "steps/s", "ms_per_step": dms,
                    "tokens_per_s": dw.B * 1e3 / dms,
@@ -650,6 +760,9 @@ def main():
                          "roofline": dict(bound="hbm", kernel="gdn_decode_kernel (gated)",
                                           traffic=measured_traffic("gdn_decode_kernel_gated"),
                                           **hbm(dbytes, gdkern_ms))},
+        "prefill_s2048": long_section(long_rows[("prefill_s2048", "std")], hbm),
+        "prefill_s65536": {v: long_section(long_rows[("prefill_s65536", v)], hbm)
+                           for v in ("std", "strong")},
         "conv1d_prefill": {"workload": cpw.name, "B": cpw.B, "C": cpw.C, "T": cpw.T,
                            "K": cpw.K, "value": cpw.B * cpw.T / (cpms / 1e3),
                            "unit": "tokens/s", "ms_per_step": cpms,
@@ -674,11 +787,16 @@ def main():
         "host": {"cpu": platform.processor() or platform.machine(),
                  "gpu": torch.cuda.get_device_name(0)},
     }
+    # The inverse-method comparison runs last, at another batch (other kernel
+    # instances than the headline's).
+    res["inverse_ab"] = bench_inverse_ab(torch, gdn, workloads, w, max(5, args.steps // 2),
+                                         args.warmup)
+    progress("inverse A/B done")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(w, d)
         res["decode"]["cpu_baseline"] = cpu_baseline_decode(dw, dsteps, dstate0)
-        res["conv1d_prefill"]["cpu_baseline"] = cpu_baseline_conv(inputs, cpw, False)
-        res["conv1d_decode"]["cpu_baseline"] = cpu_baseline_conv(inputs, cdw, True)
+        res["conv1d_prefill"]["cpu_baseline"] = cpu_baseline_conv(workloads, cpw, False)
+        res["conv1d_decode"]["cpu_baseline"] = cpu_baseline_conv(workloads, cdw, True)
     print(json.dumps(res), flush=True)
 
 

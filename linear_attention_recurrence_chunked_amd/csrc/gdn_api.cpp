@@ -14,6 +14,10 @@ namespace {
 
 constexpr int kMaxConvTaps = 8;   // conv1d window width the kernels support
 constexpr int kMaxHeadDim = 128;  // Dk, Dv upper bound ("GDN CTE", Notes)
+// Token counts of the conv1d and RMSNormGated streams: the kernels round a
+// count up to whole tiles (at most 8192 tokens) in 32-bit arithmetic, so a
+// count is accepted only with that much headroom below INT32_MAX.
+constexpr int64_t kMaxStreamTokens = INT32_MAX - 65536;
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -132,6 +136,7 @@ gdn_status validate_conv(const void* x, const float* w, const void* state, const
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
     if (B < 1 || C < 1 || T < 1 || K < 1) return GDN_ERR_SHAPE;
     if (K > kMaxConvTaps) return GDN_ERR_UNSUPPORTED;
+    if ((int64_t)T > kMaxStreamTokens) return GDN_ERR_SHAPE;
     const int64_t tiles = ((int64_t)T + 2047) / 2048;  // at least the kernel's tile count
     if ((int64_t)B * C * tiles > INT32_MAX) return GDN_ERR_SHAPE;
     const void* ptrs[] = {x, w, state, out};
@@ -296,6 +301,7 @@ gdn_status gdn_rmsnorm_gated(const void* o, const void* z, const float* norm_wei
     if (!o || !z || !norm_weight || !out) return GDN_ERR_NULL;
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
     if (B < 1 || Hv < 1 || S < 1) return GDN_ERR_SHAPE;
+    if ((int64_t)S > kMaxStreamTokens) return GDN_ERR_SHAPE;
     if (Dv < 16 || Dv > kMaxHeadDim || Dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
     if (!(eps >= 0.0f) || !isfinite(eps)) return GDN_ERR_VALUE;
     const void* ptrs[] = {o, z, norm_weight, out};

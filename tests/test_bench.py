@@ -28,17 +28,50 @@ def test_prefill_algorithmic_bench_workload():
     assert qk + vo + gb == 24832
     nbytes, flops = bench.prefill_algorithmic(4, 16, 32, 8192, 128, 128)
     assert nbytes == tokens * (qk + vo + gb) + state == 830_472_192
-    # flops of one 32-token chunk: per value head T K and T V (triangle: half
-    # of 2 C^2 D each), K S0 / Q S0 / K^T U (2 C Dk Dv each), P U (half of
-    # 2 C^2 Dv), the inverse (C^3 / 3); per key head K K^T and Q K^T (half of
-    # 2 C^2 Dk each)
-    C = 32
-    per_vh = 32 * 32 * 128 * 2 + 3 * 2 * 32 * 128 * 128 + 32 * 32 * 128 + C ** 3 / 3
-    per_kh = 2 * 32 * 32 * 128
-    chunks = tokens // C
-    assert abs(flops - chunks * (32 * per_vh + 16 * per_kh)) < 1.0
-    assert abs(flops - 120_616_998_229.33) < 1.0
-    assert 3.68e6 < flops / tokens < 3.69e6
+    # flops of one chunk of C tokens: per value head T K and T V (triangle:
+    # half of 2 C^2 D each), K S0 / Q S0 / K^T U (2 C Dk Dv each), P U (half
+    # of 2 C^2 Dv), the inverse (C^3 / 3); per key head K K^T and Q K^T (half
+    # of 2 C^2 Dk each). The reported count uses C = 64: 4.24 MFLOP per token.
+    for C, total in ((64, 138_870_609_237.33), (32, 120_616_998_229.33)):
+        per_vh = C * C * 128 * 2 + 3 * 2 * C * 128 * 128 + C * C * 128 + C ** 3 / 3
+        per_kh = 2 * C * C * 128
+        chunks = tokens // C
+        f = bench.prefill_algorithmic(4, 16, 32, 8192, 128, 128, chunk=C)[1]
+        assert abs(f - chunks * (32 * per_vh + 16 * per_kh)) < 1.0
+        assert abs(f - total) < 1.0, (C, f)
+    assert abs(flops - 138_870_609_237.33) < 1.0          # the default count: C = 64
+    assert 4.23e6 < flops / tokens < 4.24e6
+
+
+def test_mfma_util_reports_fixed_count(monkeypatch):
+    """frac = 64-token count / kernel time / 2.5 PFLOP/s; the 32-token count beside it."""
+    import workloads
+    w = workloads.WORKLOADS["prefill_b4_s8192"]
+    nbytes, flops = bench.prefill_algorithmic(w.B, w.Hk, w.Hv, w.S, w.Dk, w.Dv)
+    u = bench.mfma_util(flops, 0.5, w)
+    assert abs(u["frac"] - flops / 0.5e-3 / 2.5e15) < 1e-12
+    assert abs(u["kernel_chunk32"]["frac"] - 120_616_998_229.33 / 0.5e-3 / 2.5e15) < 1e-9
+    assert abs(u["flops_per_token"] - flops / (4 * 8192)) < 1e-6
+
+
+def test_settle_runs_warmup_then_busy_time():
+    """The settling phase runs at least the W warm-up calls and then keeps
+    the device busy for the minimum time (here with a fake torch)."""
+    import time
+
+    class FakeCuda:
+        @staticmethod
+        def synchronize():
+            pass
+
+    class FakeTorch:
+        cuda = FakeCuda
+
+    calls = []
+    t0 = time.perf_counter()
+    n = bench.settle(FakeTorch, lambda i: calls.append(i), 3, min_ms=20.0)
+    assert (time.perf_counter() - t0) * 1e3 >= 20.0
+    assert n == len(calls) >= 3 + 8
 
 
 def test_decode_and_conv_algorithmic_bench_workloads():

@@ -275,6 +275,10 @@ def test_conv_dtype_shape_taps(lib, which):
 def test_conv_prefill_tokens(lib):
     assert conv_prefill(lib, T=0) == SHAPE
     assert conv_prefill(lib, B=1 << 20, C=1 << 12, T=4096) == SHAPE   # grid overflow
+    # token counts within a tile of INT32_MAX would overflow the kernel's
+    # 32-bit tile arithmetic: rejected, never launched
+    for T in (2 ** 31 - 1, 2 ** 31 - 8191, 2 ** 31 - 65536):
+        assert conv_prefill(lib, B=1, C=1, T=T) == SHAPE, T
 
 
 @pytest.mark.parametrize("which", sorted(CONV))
@@ -320,6 +324,8 @@ def test_rmsnorm_checks(lib):
     assert rms(lib, dtype=2) == DTYPE
     for kw in (dict(B=0), dict(Hv=0), dict(S=0)):
         assert rms(lib, **kw) == SHAPE
+    for S in (2 ** 31 - 1, 2 ** 31 - 511, 2 ** 31 - 65536):   # 32-bit tile arithmetic
+        assert rms(lib, B=1, Hv=1, S=S) == SHAPE, S
     for dv in (0, 8, 24, 136):
         assert rms(lib, Dv=dv) == UNSUP
     for eps in (-1.0, float("nan"), float("inf")):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import conv1d as ref
-from linear_attention_recurrence_chunked_amd import inputs
+import workloads
 from gpu_helpers import check, log, to_np, torch_dtype
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +37,7 @@ def _prefill(x, w, dtype):
 @pytest.mark.parametrize("K", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_conv_prefill_taps(dtype, K):
     for T in (1, 3, 8, 9, 100, 2048, 2055):
-        d = inputs.draw_conv(2, 6, T, K, dtype=dtype)
+        d = workloads.draw_conv(2, 6, T, K, dtype=dtype)
         out, st = _prefill(d["x"], d["w"], dtype)
         ro, rs = ref.conv1d_prefill(d["x"], d["w"])
         log("conv prefill", dtype, "K", K, "T", T)
@@ -51,7 +51,7 @@ def test_conv_prefill_multi_tile_rows(dtype, B, C, T):
     """Many channels and batches; T = 20000 spreads each row over three
     workgroups (8192 tokens each) with a ragged tail, so the history across
     workgroup boundaries and the window state of the last one are covered."""
-    d = inputs.draw_conv(B, C, T, 4, dtype=dtype)
+    d = workloads.draw_conv(B, C, T, 4, dtype=dtype)
     log("conv prefill multi-tile", dtype, B, C, T)
     out, st = _prefill(d["x"], d["w"], dtype)
     ro, rs = ref.conv1d_prefill(d["x"], d["w"])
@@ -63,8 +63,8 @@ def test_conv_prefill_workload_sampled():
     """The conv workload the bench times (B=4, C=8192, T=8192, K=4, bf16),
     checked against the oracle on 96 sampled channel rows, and the whole
     window state exactly."""
-    w = inputs.CONV_WORKLOADS["conv_prefill_b4_t8192"]
-    d = inputs.draw_conv(w.B, w.C, w.T, w.K, dtype=w.dtype)
+    w = workloads.CONV_WORKLOADS["conv_prefill_b4_t8192"]
+    d = workloads.draw_conv(w.B, w.C, w.T, w.K, dtype=w.dtype)
     out, st = _prefill(d["x"], d["w"], w.dtype)
     rng = np.random.default_rng(7)
     rows = rng.choice(w.B * w.C, size=96, replace=False)
@@ -82,12 +82,12 @@ def test_conv_prefill_workload_sampled():
 def test_conv_decode_steps(dtype, K):
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_conv(3, 37, 1, K, dtype=dtype, decode=True)
+    d = workloads.draw_conv(3, 37, 1, K, dtype=dtype, decode=True)
     st_dev = _dev(d["state"], dtype)
     wt = _weights(d["w"])
     st_ref = d["state"].astype(np.float64)
     for step in range(5):
-        xs = inputs.draw_conv(3, 37, 1, K, dtype=dtype, step=step + 1, decode=True)["x"]
+        xs = workloads.draw_conv(3, 37, 1, K, dtype=dtype, step=step + 1, decode=True)["x"]
         o = gdn.conv1d_decode(_dev(xs, dtype), st_dev, wt)
         ro, st_ref = ref.conv1d_decode(xs, st_ref, d["w"])
         torch.cuda.synchronize()
@@ -100,13 +100,13 @@ def test_conv_decode_workload():
     """B=256, C=8192, K=4, bf16, eight chained steps."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    w = inputs.CONV_WORKLOADS["conv_decode_b256"]
-    d = inputs.draw_conv(w.B, w.C, 1, w.K, dtype=w.dtype, decode=True)
+    w = workloads.CONV_WORKLOADS["conv_decode_b256"]
+    d = workloads.draw_conv(w.B, w.C, 1, w.K, dtype=w.dtype, decode=True)
     st_dev = _dev(d["state"], w.dtype)
     wt = _weights(d["w"])
     st_ref = d["state"].astype(np.float64)
     for step in range(8):
-        xs = inputs.draw_conv(w.B, w.C, 1, w.K, dtype=w.dtype, step=step + 1, decode=True)["x"]
+        xs = workloads.draw_conv(w.B, w.C, 1, w.K, dtype=w.dtype, step=step + 1, decode=True)["x"]
         o = gdn.conv1d_decode(_dev(xs, w.dtype), st_dev, wt)
         ro, st_ref = ref.conv1d_decode(xs, st_ref, d["w"])
         torch.cuda.synchronize()
@@ -118,7 +118,7 @@ def test_conv_prefill_then_decode():
     the whole sequence."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_conv(2, 24, 300, 4, dtype="bf16")
+    d = workloads.draw_conv(2, 24, 300, 4, dtype="bf16")
     x, wv = d["x"], d["w"]
     ro, rs = ref.conv1d_prefill(x, wv)
     o1, st = gdn.conv1d_prefill(_dev(x[:, :, :290], "bf16"), _weights(wv))

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-from linear_attention_recurrence_chunked_amd import inputs
+import workloads
 from gpu_helpers import check, log, to_np, upload, TOL
 
 pytestmark = pytest.mark.gpu
@@ -14,7 +14,7 @@ def _run_steps(w, nsteps, dtype=None, **over):
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
     dtype = dtype or w.dtype
-    state0, steps = inputs.draw_decode_steps(w, nsteps=nsteps, **over)
+    state0, steps = workloads.draw_decode_steps(w, nsteps=nsteps, **over)
     st_dev = torch.from_numpy(state0).cuda()
     st_ref = state0.astype(np.float64)
     outs, refs = [], []
@@ -37,7 +37,7 @@ def _run_steps(w, nsteps, dtype=None, **over):
                                    dict(B=2, Hk=1, Hv=3, Dk=64, Dv=32),
                                    dict(B=2, Hk=2, Hv=2, Dk=48, Dv=80)])
 def test_decode_small(dtype, shape):
-    w = inputs.WORKLOADS["decode_b256"]
+    w = workloads.WORKLOADS["decode_b256"]
     log("decode small", dtype, shape)
     o, ro, s, rs = _run_steps(w, 8, dtype=dtype, **shape)
     check("decode %s %s" % (dtype, shape), dtype, o, ro, s, rs)
@@ -45,7 +45,7 @@ def test_decode_small(dtype, shape):
 
 def test_decode_b256_64_steps():
     """The full decode workload: B=256, Hk=16, Hv=32, Dk=Dv=128, 64 steps."""
-    w = inputs.WORKLOADS["decode_b256"]
+    w = workloads.WORKLOADS["decode_b256"]
     log("decode_b256 x 64 steps")
     o, ro, s, rs = _run_steps(w, w.steps)
     check("decode_b256 64 steps", "bf16", o, ro, s, rs)
@@ -54,8 +54,8 @@ def test_decode_b256_64_steps():
 def test_decode_deterministic():
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    w = inputs.WORKLOADS["decode_b256"]
-    state0, steps = inputs.draw_decode_steps(w, nsteps=2, B=8)
+    w = workloads.WORKLOADS["decode_b256"]
+    state0, steps = workloads.draw_decode_steps(w, nsteps=2, B=8)
     res = []
     for _ in range(2):
         st = torch.from_numpy(state0).cuda()
@@ -75,8 +75,8 @@ def test_decode_gqa_equals_repeated_heads():
     repeated per value head (Hk = Hv)."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    w = inputs.WORKLOADS["decode_b256"]
-    state0, steps = inputs.draw_decode_steps(w, nsteps=1, B=8, Hk=4, Hv=8)
+    w = workloads.WORKLOADS["decode_b256"]
+    state0, steps = workloads.draw_decode_steps(w, nsteps=1, B=8, Hk=4, Hv=8)
     d = steps[0]
     dr = dict(d, q=np.repeat(d["q"], 2, axis=1), k=np.repeat(d["k"], 2, axis=1))
     res = []

@@ -6,12 +6,12 @@ import numpy as np
 import pytest
 
 import oracle
-from linear_attention_recurrence_chunked_amd import inputs
+import workloads
 from gpu_helpers import check, log, to_np, upload_raw
 
 pytestmark = pytest.mark.gpu
 
-W = inputs.WORKLOADS
+W = workloads.WORKLOADS
 EPS = 1e-6
 
 
@@ -36,24 +36,24 @@ def _parity(name, d, dtype, scale, eps=EPS):
 
 def test_gated_tiny_f32():
     w = W["tiny_f32"]
-    _parity(w.name, inputs.draw_workload(w, raw=True), "f32", w.scale)
+    _parity(w.name, workloads.draw_workload(w, raw=True), "f32", w.scale)
 
 
 def test_gated_prefill_s2048():
     w = W["prefill_s2048"]
-    _parity(w.name, inputs.draw_workload(w, raw=True), "bf16", w.scale)
+    _parity(w.name, workloads.draw_workload(w, raw=True), "bf16", w.scale)
 
 
 def test_gated_prefill_b4_s8192_full():
     """The bench workload with raw inputs, in the configuration the bench times."""
     w = W["prefill_b4_s8192"]
-    _parity(w.name, inputs.draw_workload(w, raw=True), "bf16", w.scale)
+    _parity(w.name, workloads.draw_workload(w, raw=True), "bf16", w.scale)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_gated_strong_decay(dtype):
     w = W["prefill_s65536"]
-    d = inputs.draw_prefill(B=1, Hk=4, Hv=8, S=4096, Dk=128, Dv=128, dtype=dtype,
+    d = workloads.draw_prefill(B=1, Hk=4, Hv=8, S=4096, Dk=128, Dv=128, dtype=dtype,
                             state="normal", decay="strong", seed=(4, 1, 16), raw=True)
     _parity("strong/%s" % dtype, d, dtype, w.scale)
 
@@ -67,7 +67,7 @@ def test_gated_strong_decay(dtype):
     dict(B=1, Hk=1, Hv=2, S=320, Dk=128, Dv=16),    # smallest Dv
 ])
 def test_gated_shapes(dtype, shape):
-    d = inputs.draw_prefill(dtype=dtype, state="normal", decay="weak", seed=(9, 2, 11),
+    d = workloads.draw_prefill(dtype=dtype, state="normal", decay="weak", seed=(9, 2, 11),
                             raw=True, **shape)
     _parity("gated shape %s %s" % (dtype, shape), d, dtype, 1.0 / np.sqrt(shape["Dk"]))
 
@@ -76,12 +76,12 @@ def test_gated_shapes(dtype, shape):
 def test_gated_epsilon_matters(dtype):
     """Short raw q, k (|x|^2 ~ 0.3) with eps = 0.1: the epsilon changes every
     normalised vector by several percent, so its placement is tested."""
-    d = inputs.draw_prefill(B=1, Hk=2, Hv=4, S=256, Dk=128, Dv=64, dtype=dtype,
+    d = workloads.draw_prefill(B=1, Hk=2, Hv=4, S=256, Dk=128, Dv=64, dtype=dtype,
                             state="normal", seed=(9, 0, 12), raw=True)
     for key in ("q_raw", "k_raw"):
         d[key] = (d[key] * np.float32(0.05))
         if dtype == "bf16":
-            d[key] = inputs.bf16_round(d[key])
+            d[key] = workloads.bf16_round(d[key])
     _parity("eps=0.1 %s" % dtype, d, dtype, 0.125, eps=0.1)
 
 
@@ -89,7 +89,7 @@ def test_gated_epsilon_matters(dtype):
 def test_gated_zero_key_rows(dtype):
     """All-zero raw keys (and queries) normalise to zero with eps > 0: those
     tokens only decay the state."""
-    d = inputs.draw_prefill(B=1, Hk=1, Hv=2, S=128, Dk=128, Dv=128, dtype=dtype,
+    d = workloads.draw_prefill(B=1, Hk=1, Hv=2, S=128, Dk=128, Dv=128, dtype=dtype,
                             state="normal", seed=(9, 0, 13), raw=True)
     d["k_raw"][:, :, 5:40:7] = 0.0
     d["q_raw"][:, :, 64:70] = 0.0
@@ -99,7 +99,7 @@ def test_gated_zero_key_rows(dtype):
 def _decode_steps(w, nsteps, dtype, eps=EPS, **over):
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    state0, steps = inputs.draw_decode_steps(w, nsteps=nsteps, raw=True, **over)
+    state0, steps = workloads.draw_decode_steps(w, nsteps=nsteps, raw=True, **over)
     st_dev = torch.from_numpy(state0).cuda()
     st_ref = state0.astype(np.float64)
     outs, refs = [], []
@@ -139,13 +139,13 @@ def test_gated_decode_epsilon_matters():
     w = W["decode_b256"]
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    state0, steps = inputs.draw_decode_steps(w, nsteps=4, raw=True, B=2, Hk=2, Hv=4)
+    state0, steps = workloads.draw_decode_steps(w, nsteps=4, raw=True, B=2, Hk=2, Hv=4)
     st_dev = torch.from_numpy(state0).cuda()
     st_ref = state0.astype(np.float64)
     outs, refs = [], []
     for d in steps:
         for key in ("q_raw", "k_raw"):
-            d[key] = inputs.bf16_round(d[key] * np.float32(0.05))
+            d[key] = workloads.bf16_round(d[key] * np.float32(0.05))
         t = upload_raw(d, "bf16")
         outs.append(to_np(gdn.decode_step_gated(
             t["q"][:, :, 0], t["k"][:, :, 0], t["v"][:, :, 0], t["a"][:, :, 0].contiguous(),
@@ -163,7 +163,7 @@ def test_gated_decode_iterated_matches_gated_prefill():
     it both match the oracle."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=2, Hk=2, Hv=4, S=64, Dk=128, Dv=128, dtype="bf16",
+    d = workloads.draw_prefill(B=2, Hk=2, Hv=4, S=64, Dk=128, Dv=128, dtype="bf16",
                             state="normal", decay="weak", seed=(9, 2, 14), raw=True)
     t = upload_raw(d, "bf16")
     st_p = t["state"].clone()
@@ -187,7 +187,7 @@ def test_gated_error_writes_nothing():
     """A negative epsilon is refused before anything is launched."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=1, Hk=1, Hv=1, S=64, Dk=64, Dv=64, dtype="bf16",
+    d = workloads.draw_prefill(B=1, Hk=1, Hv=1, S=64, Dk=64, Dv=64, dtype="bf16",
                             state="normal", seed=(9, 0, 15), raw=True)
     t = upload_raw(d, "bf16")
     out = torch.full((1, 1, 64, 64), 7.0, dtype=torch.bfloat16, device="cuda")
@@ -206,6 +206,6 @@ def test_gated_ragged_sequence_length(dtype, eps):
     """A partial last chunk with the prologue on the device: the missing
     tokens' gates are zero and their (zero) rows get no norm factor, also
     with eps = 0."""
-    d = inputs.draw_prefill(B=1, Hk=2, Hv=4, S=71, Dk=128, Dv=64, dtype=dtype, state="normal",
+    d = workloads.draw_prefill(B=1, Hk=2, Hv=4, S=71, Dk=128, Dv=64, dtype=dtype, state="normal",
                             seed=(9, 4, 71), raw=True)
     _parity("gated ragged S=71 %s eps=%g" % (dtype, eps), d, dtype, 0.125, eps=eps)

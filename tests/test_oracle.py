@@ -53,10 +53,10 @@ def test_zero_length_and_strong_decay():
 
 
 def test_workload_inputs_are_seeded_and_normalised():
-    from linear_attention_recurrence_chunked_amd import inputs
-    w = inputs.WORKLOADS["tiny_f32"]
-    a = inputs.draw_workload(w)
-    b = inputs.draw_workload(w)
+    import workloads
+    w = workloads.WORKLOADS["tiny_f32"]
+    a = workloads.draw_workload(w)
+    b = workloads.draw_workload(w)
     for key in a:
         assert np.array_equal(a[key], b[key])
     n = np.linalg.norm(a["q"].astype(np.float64), axis=-1)
@@ -64,7 +64,7 @@ def test_workload_inputs_are_seeded_and_normalised():
     assert np.all(a["g_log"] < 0) and np.all((a["beta"] > 0) & (a["beta"] < 1))
     # bf16 rounding: round-to-nearest-even on the upper 16 bits
     x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 1.00390625], np.float32)
-    r = inputs.bf16_round(x)
+    r = workloads.bf16_round(x)
     assert list(r) == [1.0, 1.0 + 4 * 2.0 ** -8, -2.5, 1.0]
 
 

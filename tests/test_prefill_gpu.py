@@ -5,12 +5,12 @@ import numpy as np
 import pytest
 
 import oracle
-from linear_attention_recurrence_chunked_amd import inputs
+import workloads
 from gpu_helpers import check, log, run_prefill, to_np, upload
 
 pytestmark = pytest.mark.gpu
 
-W = inputs.WORKLOADS
+W = workloads.WORKLOADS
 
 
 def _parity(name, d, dtype, scale, inverse=None):
@@ -23,24 +23,24 @@ def _parity(name, d, dtype, scale, inverse=None):
 
 def test_tiny_f32():
     w = W["tiny_f32"]
-    _parity(w.name, inputs.draw_workload(w), "f32", w.scale)
+    _parity(w.name, workloads.draw_workload(w), "f32", w.scale)
 
 
 def test_prefill_s2048():
     w = W["prefill_s2048"]
-    _parity(w.name, inputs.draw_workload(w), "bf16", w.scale)
+    _parity(w.name, workloads.draw_workload(w), "bf16", w.scale)
 
 
 def test_prefill_b4_s8192_full():
     """The bench workload, in the launch configuration the bench times."""
     w = W["prefill_b4_s8192"]
-    _parity(w.name, inputs.draw_workload(w), "bf16", w.scale)
+    _parity(w.name, workloads.draw_workload(w), "bf16", w.scale)
 
 
 @pytest.mark.parametrize("variant", ["std", "strong"])
 def test_prefill_s65536(variant):
     w = W["prefill_s65536"]
-    _parity("%s/%s" % (w.name, variant), inputs.draw_workload(w, variant=variant), "bf16",
+    _parity("%s/%s" % (w.name, variant), workloads.draw_workload(w, variant=variant), "bf16",
             w.scale)
 
 
@@ -49,7 +49,7 @@ def test_weak_decay(dtype):
     """Slow decay (e^g ~ 0.97): the inverse's off-diagonals and the carry
     across chunks matter for many tokens."""
     w = W["prefill_s2048"]
-    d = inputs.draw_prefill(B=1, Hk=4, Hv=8, S=1024, Dk=128, Dv=128, dtype=dtype,
+    d = workloads.draw_prefill(B=1, Hk=4, Hv=8, S=1024, Dk=128, Dv=128, dtype=dtype,
                             state="normal", decay="weak", seed=(1, 2, 0))
     _parity("weak/%s" % dtype, d, dtype, w.scale)
 
@@ -63,13 +63,13 @@ def test_weak_decay(dtype):
     dict(B=1, Hk=1, Hv=2, S=320, Dk=128, Dv=16),    # smallest Dv
 ])
 def test_shapes(dtype, shape):
-    d = inputs.draw_prefill(dtype=dtype, state="normal", decay="weak", seed=(9, 2, 1), **shape)
+    d = workloads.draw_prefill(dtype=dtype, state="normal", decay="weak", seed=(9, 2, 1), **shape)
     _parity("shape %s %s" % (dtype, shape), d, dtype, 1.0 / np.sqrt(shape["Dk"]))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_beta_zero_pure_decay(dtype):
-    d = inputs.draw_prefill(B=1, Hk=2, Hv=4, S=128, Dk=128, Dv=128, dtype=dtype,
+    d = workloads.draw_prefill(B=1, Hk=2, Hv=4, S=128, Dk=128, Dv=128, dtype=dtype,
                             state="normal", decay="weak", seed=(9, 2, 2))
     d["beta"][:] = 0.0
     _parity("beta=0 %s" % dtype, d, dtype, 0.5)
@@ -77,7 +77,7 @@ def test_beta_zero_pure_decay(dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_state_no_decay(dtype):
-    d = inputs.draw_prefill(B=1, Hk=2, Hv=2, S=128, Dk=64, Dv=64, dtype=dtype,
+    d = workloads.draw_prefill(B=1, Hk=2, Hv=2, S=128, Dk=64, Dv=64, dtype=dtype,
                             state="zero", decay="weak", seed=(9, 2, 3))
     d["g_log"][:] = 0.0
     _parity("g=0 %s" % dtype, d, dtype, 0.125)
@@ -88,7 +88,7 @@ def test_split_sequence_carry_is_bitwise():
     prefill(S1 + S2) bit for bit (chunk boundaries coincide)."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=2, Hk=2, Hv=4, S=384, Dk=128, Dv=128, dtype="bf16",
+    d = workloads.draw_prefill(B=2, Hk=2, Hv=4, S=384, Dk=128, Dv=128, dtype="bf16",
                             state="normal", decay="weak", seed=(9, 2, 4))
     t = upload(d, "bf16")
     st_full = t["state"].clone()
@@ -108,7 +108,7 @@ def test_split_sequence_carry_is_bitwise():
 def test_deterministic():
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=2, Hk=4, Hv=8, S=512, Dk=128, Dv=128, dtype="bf16",
+    d = workloads.draw_prefill(B=2, Hk=4, Hv=8, S=512, Dk=128, Dv=128, dtype="bf16",
                             state="normal", seed=(9, 0, 5))
     t = upload(d, "bf16")
     res = []
@@ -124,7 +124,7 @@ def test_decode_iterated_matches_prefill():
     """64 decode steps from a state equal one 64-token prefill from it."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=2, Hk=2, Hv=4, S=64, Dk=128, Dv=128, dtype="bf16",
+    d = workloads.draw_prefill(B=2, Hk=2, Hv=4, S=64, Dk=128, Dv=128, dtype="bf16",
                             state="normal", decay="weak", seed=(9, 2, 6))
     t = upload(d, "bf16")
     st_p = t["state"].clone()
@@ -147,7 +147,7 @@ def test_error_writes_nothing():
     """An invalid call (Dk = 72, not a multiple of 16) leaves out and state untouched."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=1, Hk=1, Hv=1, S=96, Dk=72, Dv=64, dtype="bf16",
+    d = workloads.draw_prefill(B=1, Hk=1, Hv=1, S=96, Dk=72, Dv=64, dtype="bf16",
                             state="normal", seed=(9, 0, 7))
     t = upload(d, "bf16")
     out = torch.full((1, 1, 96, 64), 7.0, dtype=torch.bfloat16, device="cuda")
@@ -168,9 +168,9 @@ def test_neumann_inverse_workloads(dtype):
     where the inverse's off-diagonal entries are largest."""
     import linear_attention_recurrence_chunked_amd as gdn
     w = W["tiny_f32"] if dtype == "f32" else W["prefill_s2048"]
-    _parity("neumann " + w.name, inputs.draw_workload(w), w.dtype, w.scale,
+    _parity("neumann " + w.name, workloads.draw_workload(w), w.dtype, w.scale,
             inverse=gdn.GDN_INV_NEUMANN)
-    d = inputs.draw_prefill(B=1, Hk=4, Hv=8, S=1024, Dk=128, Dv=128, dtype=dtype,
+    d = workloads.draw_prefill(B=1, Hk=4, Hv=8, S=1024, Dk=128, Dv=128, dtype=dtype,
                             state="normal", decay="weak", seed=(1, 2, 0))
     _parity("neumann weak/%s" % dtype, d, dtype, 1.0 / np.sqrt(128), inverse=gdn.GDN_INV_NEUMANN)
 
@@ -183,23 +183,27 @@ def test_neumann_inverse_workloads(dtype):
 ])
 def test_neumann_inverse_shapes(dtype, shape):
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(dtype=dtype, state="normal", decay="weak", seed=(9, 2, 21), **shape)
+    d = workloads.draw_prefill(dtype=dtype, state="normal", decay="weak", seed=(9, 2, 21), **shape)
     _parity("neumann shape %s %s" % (dtype, shape), d, dtype, 1.0 / np.sqrt(shape["Dk"]),
             inverse=gdn.GDN_INV_NEUMANN)
 
 
 def test_neumann_matches_substitution():
     """Both inverse methods on the bench workload's shape (B=1 slice): the
-    outputs agree far inside the tolerance."""
+    states agree to fp32 rounding, and the bf16 outputs differ by at most one
+    bf16 ulp (2^-7 |x|: a rounding flip of the same fp32 result) plus 1e-3 of
+    the RMS."""
     import linear_attention_recurrence_chunked_amd as gdn
-    from gpu_helpers import rel_err
+    from gpu_helpers import rms_err
     w = W["prefill_b4_s8192"]
-    d = inputs.draw_workload(w, B=1, S=2048)
+    d = workloads.draw_workload(w, B=1, S=2048)
     o1, s1 = run_prefill(d, "bf16", w.scale)
     o2, s2 = run_prefill(d, "bf16", w.scale, inverse=gdn.GDN_INV_NEUMANN)
-    eo, es = rel_err(o2, o1), rel_err(s2, s1)
+    rms = float(np.sqrt(np.mean(o1.astype(np.float64) ** 2)))
+    eo = float(np.max(np.maximum(np.abs(o2 - o1) - 2.0 ** -7 * np.abs(o1), 0.0))) / rms
+    es = rms_err(s2, s1)
     log("neumann vs substitution: out %.3e state %.3e" % (eo, es))
-    assert eo < 1e-2 and es < 5e-3
+    assert eo < 1e-3 and es < 1e-5
 
 
 # ------------------------------------------------- sequence lengths of any size
@@ -209,14 +213,14 @@ def test_neumann_matches_substitution():
 def test_ragged_sequence_length(dtype, S):
     """A partial last chunk (S not a multiple of the 32-token chunk): exact,
     no output past S, state as the oracle's."""
-    d = inputs.draw_prefill(B=2, Hk=2, Hv=4, S=S, Dk=128, Dv=128, dtype=dtype, state="normal",
+    d = workloads.draw_prefill(B=2, Hk=2, Hv=4, S=S, Dk=128, Dv=128, dtype=dtype, state="normal",
                             decay="weak", seed=(9, 3, S))
     _parity("ragged S=%d %s" % (S, dtype), d, dtype, 1.0 / np.sqrt(128))
 
 
 def test_ragged_neumann_and_shapes():
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=1, Hk=2, Hv=4, S=77, Dk=80, Dv=48, dtype="bf16", state="normal",
+    d = workloads.draw_prefill(B=1, Hk=2, Hv=4, S=77, Dk=80, Dv=48, dtype="bf16", state="normal",
                             decay="weak", seed=(9, 3, 77))
     _parity("ragged neumann S=77", d, "bf16", 0.1, inverse=gdn.GDN_INV_NEUMANN)
     _parity("ragged S=77 Dk=80 Dv=48", d, "bf16", 0.1)
@@ -227,7 +231,7 @@ def test_ragged_out_untouched_past_end():
     larger buffer filled with a marker, which must survive the call."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=1, Hk=1, Hv=2, S=45, Dk=64, Dv=64, dtype="bf16", state="normal",
+    d = workloads.draw_prefill(B=1, Hk=1, Hv=2, S=45, Dk=64, Dv=64, dtype="bf16", state="normal",
                             seed=(9, 3, 45))
     t = upload(d, "bf16")
     n = 1 * 2 * 45 * 64
@@ -245,7 +249,7 @@ def test_ragged_split_carry_matches_oracle():
     oracle over all 384 tokens (chunk boundaries differ from one call of 384)."""
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    d = inputs.draw_prefill(B=2, Hk=2, Hv=4, S=384, Dk=128, Dv=128, dtype="bf16",
+    d = workloads.draw_prefill(B=2, Hk=2, Hv=4, S=384, Dk=128, Dv=128, dtype="bf16",
                             state="normal", decay="weak", seed=(9, 3, 384))
     t = upload(d, "bf16")
     st = t["state"].clone()
@@ -266,7 +270,7 @@ def test_gqa_equals_repeated_heads(dtype):
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
     G = 4
-    d = inputs.draw_prefill(B=2, Hk=2, Hv=2 * G, S=200, Dk=64, Dv=128, dtype=dtype,
+    d = workloads.draw_prefill(B=2, Hk=2, Hv=2 * G, S=200, Dk=64, Dv=128, dtype=dtype,
                             state="normal", seed=(71, 0, 0))
     dr = dict(d, q=np.repeat(d["q"], G, axis=1), k=np.repeat(d["k"], G, axis=1))
     res = []
@@ -334,10 +338,10 @@ def test_exact_key_overwrite(dtype):
     qm, _ = np.linalg.qr(rng.standard_normal((D, D)))
     kk = qm[:S].astype(np.float32)                      # S orthonormal rows
     if dtype == "bf16":                                  # exact bf16 keys stay near-orthonormal
-        kk = inputs.bf16_round(kk)
+        kk = workloads.bf16_round(kk)
     v = rng.standard_normal((1, 1, S, D)).astype(np.float32)
     if dtype == "bf16":
-        v = inputs.bf16_round(v)
+        v = workloads.bf16_round(v)
     d = {"q": kk[None, None].copy(), "k": kk[None, None].copy(), "v": v,
          "g_log": np.zeros((1, 1, S), np.float32), "beta": np.ones((1, 1, S), np.float32),
          "state": (0.5 * rng.standard_normal((1, 1, D, D))).astype(np.float32)}
@@ -368,7 +372,7 @@ def test_repeat_launches_bitwise_at_bench_size(gated):
     import linear_attention_recurrence_chunked_amd as gdn
     from gpu_helpers import upload_raw
     w = W["prefill_b4_s8192"]
-    d = inputs.draw_workload(w, raw=True)
+    d = workloads.draw_workload(w, raw=True)
     t = upload_raw(d, "bf16") if gated else upload(d, "bf16")
     st0 = t["state"].clone()
     out = torch.empty((w.B, w.Hv, w.S, w.Dv), dtype=torch.bfloat16, device="cuda")

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from linear_attention_recurrence_chunked_amd import inputs
+import workloads
 from gpu_helpers import check, log, to_np, upload
 
 pytestmark = pytest.mark.gpu
@@ -16,10 +16,10 @@ def test_concurrent_streams_match_serial():
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
     shapes = [dict(B=2, Hk=2, Hv=4, S=500, Dk=128, Dv=128), dict(B=1, Hk=3, Hv=6, S=333, Dk=64, Dv=96)]
-    draws = [inputs.draw_prefill(dtype="bf16", state="normal", seed=(61, i, 0), **sh)
+    draws = [workloads.draw_prefill(dtype="bf16", state="normal", seed=(61, i, 0), **sh)
              for i, sh in enumerate(shapes)]
-    w = inputs.WORKLOADS["decode_b256"]
-    state0, steps = inputs.draw_decode_steps(w, nsteps=4, B=16)
+    w = workloads.WORKLOADS["decode_b256"]
+    state0, steps = workloads.draw_decode_steps(w, nsteps=4, B=16)
 
     def launch(stream_of):
         """Two prefills and four decode steps, each problem on its own stream."""

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from linear_attention_recurrence_chunked_amd import inputs
+import workloads
 from gpu_helpers import check, log, run_prefill, to_np, upload, upload_raw
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +28,7 @@ def test_prefill_sweep(case):
     import linear_attention_recurrence_chunked_amd as gdn
     c = CASES[case]
     log("sweep case", case, c)
-    d = inputs.draw_prefill(B=c["B"], Hk=c["Hk"], Hv=c["Hk"] * c["G"], S=c["S"], Dk=c["Dk"],
+    d = workloads.draw_prefill(B=c["B"], Hk=c["Hk"], Hv=c["Hk"] * c["G"], S=c["S"], Dk=c["Dk"],
                             Dv=c["Dv"], dtype=c["dtype"], state="normal", decay=c["decay"],
                             seed=(50, case, 0), raw=c["gated"])
     scale = 1.0 / np.sqrt(c["Dk"])
@@ -55,8 +55,8 @@ def test_decode_sweep(case):
     import linear_attention_recurrence_chunked_amd as gdn
     c = CASES[case]
     log("decode sweep case", case, c)
-    w = inputs.WORKLOADS["decode_b256"]
-    state0, steps = inputs.draw_decode_steps(w, nsteps=3, B=c["B"], Hk=c["Hk"],
+    w = workloads.WORKLOADS["decode_b256"]
+    state0, steps = workloads.draw_decode_steps(w, nsteps=3, B=c["B"], Hk=c["Hk"],
                                              Hv=c["Hk"] * c["G"], Dk=c["Dk"], Dv=c["Dv"])
     st = torch.from_numpy(state0).cuda()
     st_ref = state0.astype(np.float64)

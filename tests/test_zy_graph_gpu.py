@@ -6,7 +6,7 @@ allocates nothing, so every call is a plain kernel node."""
 import numpy as np
 import pytest
 
-from linear_attention_recurrence_chunked_amd import inputs
+import workloads
 from gpu_helpers import log, upload
 
 pytestmark = pytest.mark.gpu
@@ -42,13 +42,13 @@ def _replays_match(run, reset, outputs, nrep=3):
 def test_graph_decode_steps_and_prefill():
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
-    w = inputs.WORKLOADS["decode_b256"]
-    state0, steps = inputs.draw_decode_steps(w, nsteps=6, B=8)
+    w = workloads.WORKLOADS["decode_b256"]
+    state0, steps = workloads.draw_decode_steps(w, nsteps=6, B=8)
     dev = [upload(d, "bf16") for d in steps]
     st0 = torch.from_numpy(state0).cuda()
     st = st0.clone()
     outs = [torch.empty((8, w.Hv, w.Dv), dtype=torch.bfloat16, device="cuda") for _ in steps]
-    pd = inputs.draw_prefill(B=1, Hk=2, Hv=4, S=256, Dk=128, Dv=128, dtype="bf16",
+    pd = workloads.draw_prefill(B=1, Hk=2, Hv=4, S=256, Dk=128, Dv=128, dtype="bf16",
                              state="normal", seed=(9, 0, 30))
     pt = upload(pd, "bf16")
     pst0 = pt["state"].clone()
@@ -75,9 +75,9 @@ def test_graph_decode_block():
     import torch
     import linear_attention_recurrence_chunked_amd as gdn
     B, Hk, Hv, Dk, Dv, K = 4, 2, 4, 128, 128, 4
-    d0 = inputs.draw_block(B, Hk, Hv, Dk, Dv, K)
+    d0 = workloads.draw_block(B, Hk, Hv, Dk, Dv, K)
     up = lambda a, bf: torch.from_numpy(a).cuda().to(torch.bfloat16 if bf else torch.float32)
-    toks = [d0] + [inputs.draw_block(B, Hk, Hv, Dk, Dv, K, step=i, with_state=False)
+    toks = [d0] + [workloads.draw_block(B, Hk, Hv, Dk, Dv, K, step=i, with_state=False)
                    for i in (1, 2, 3)]
     dt = [{k: up(t[k], k in ("mixed", "z")) for k in ("mixed", "z", "a", "b")} for t in toks]
     fx = {k: up(d0[k], False) for k in ("conv_weight", "A_log", "dt_bias", "norm_weight")}
