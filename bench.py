@@ -249,10 +249,11 @@ def settle(torch, step, warmup, min_ms=SETTLE_MS, clocks=None):
             c = _clock_mhz(torch)
             if c is not None:
                 clocks.append(c)
+        # synchronised per batch, so that the time counted is the device's
+        # (the host would otherwise queue far more calls than it waits for)
+        torch.cuda.synchronize()
         if (time.perf_counter() - t0) * 1e3 >= min_ms:
-            torch.cuda.synchronize()
-            if (time.perf_counter() - t0) * 1e3 >= min_ms:
-                return n
+            return n
 
 
 
