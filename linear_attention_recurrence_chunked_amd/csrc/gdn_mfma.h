@@ -99,6 +99,25 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
     hi = h;
 }
 
+// The same pair for values that die here: each difference is one bf16 dot
+// product x + (-1) hi_x + 0 hi_y accumulated into x's own register, which is
+// exact (x - bf16(x) is representable in fp32), so a pair costs two
+// conversions and two dot products. (For a value that stays live the
+// compiler would add a copy per dot product; split2 is cheaper there.)
+// m0 = 0x0000bf80 and m1 = 0xbf800000 are the packed factors (-1, 0) and
+// (0, -1). The caller passes them in registers, opaque to the compiler: the
+// compiler would otherwise encode (-1, 0) as the inline constant -1.0, which
+// this instruction reads as the fp32 bit pattern, i.e. as (0, -1).
+constexpr uint32_t kDotNegLo = 0x0000bf80u, kDotNegHi = 0xbf800000u;
+__device__ __forceinline__ void split2_last(float a, float b, uint32_t& hi, uint32_t& lo,
+                                            uint32_t m0, uint32_t m1) {
+    const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+    const float la = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m0), a, false);
+    const float lb = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m1), b, false);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{la, lb}, bf16x2));
+    hi = __builtin_bit_cast(uint32_t, h);
+}
+
 template <typename E> struct Op;
 
 template <> struct Op<bf16> {
@@ -145,13 +164,19 @@ template <> struct Op<bf16> {
         const bf16x4 x = __builtin_bit_cast(bf16x4, a), y = __builtin_bit_cast(bf16x4, b);
         return F{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     }
-    // B fragment from two accumulator tiles (k block 0 = x0 rows, block 1 = x1 rows).
-    __device__ __forceinline__ static void split(f32x4 x0, f32x4 x1, F& hi, F& lo) {
+    // B fragment from two accumulator tiles (k block 0 = x0 rows, block 1 = x1
+    // rows); LAST: the tiles die here (split2_last, with its factors m0, m1).
+    template <bool LAST = false>
+    __device__ __forceinline__ static void split(f32x4 x0, f32x4 x1, F& hi, F& lo,
+                                                 uint32_t m0 = 0, uint32_t m1 = 0) {
         uint32_t h0, h1, h2, h3, w0, w1, w2, w3;
-        split2(x0[0], x0[1], h0, w0);
-        split2(x0[2], x0[3], h1, w1);
-        split2(x1[0], x1[1], h2, w2);
-        split2(x1[2], x1[3], h3, w3);
+        auto s2 = [&](float a, float b, uint32_t& h, uint32_t& w) {
+            if constexpr (LAST) split2_last(a, b, h, w, m0, m1); else split2(a, b, h, w);
+        };
+        s2(x0[0], x0[1], h0, w0);
+        s2(x0[2], x0[3], h1, w1);
+        s2(x1[0], x1[1], h2, w2);
+        s2(x1[2], x1[3], h3, w3);
         hi = __builtin_bit_cast(F, u32x4{h0, h1, h2, h3});
         lo = __builtin_bit_cast(F, u32x4{w0, w1, w2, w3});
     }
@@ -210,7 +235,9 @@ template <> struct Op<float> {
         for (int e = 0; e < 4; ++e) { a.v[e] = p[e * ld]; a.v[4 + e] = p[(16 + e) * ld]; }
         return a;
     }
-    __device__ __forceinline__ static void split(f32x4 x0, f32x4 x1, F& hi, F& lo) {
+    template <bool LAST = false>
+    __device__ __forceinline__ static void split(f32x4 x0, f32x4 x1, F& hi, F& lo,
+                                                 uint32_t = 0, uint32_t = 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) { hi.v[e] = x0[e]; hi.v[4 + e] = x1[e]; }
         lo = hi;  // unused on the fp32 path

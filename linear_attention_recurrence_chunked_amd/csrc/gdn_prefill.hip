@@ -831,47 +831,60 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     // (folded with rk on the GATED path) was final when the A wave finished
     // chunk i, three steps ahead. On the fp32 path the A wave builds chunk i
     // during step i - 1, so those scalars are read at the start of step i.
-    struct ConsPre { F kf[NT], qf[NT]; float vv[NT][4], bt[NT][4], bk[NT][4]; };
+    // kb, sb: this lane's K/Q fragment and row-scalar addresses in the slot.
+    struct ConsPre { F kf[NT], qf[NT]; float vv[NT][4], bt[NT][4], bk[NT][4]; uint32_t kb, sb; };
+    // A consumer's reads of a chunk follow a few per-lane patterns. Each gets
+    // one address register per chunk (the slot's offset plus the lane's
+    // loop-invariant offset, opaque to the optimiser), and every tile of the
+    // pattern is an immediate offset from it.
+    const uint32_t smem_a = lds_addr(smem);
+    const uint32_t c_kq = O::ldc_lane(LDK);                       // K/Q fragments
+    const uint32_t c_kt = O::ldt_lane(LDK, 0);                    // transposed K
+    const uint32_t c_tp = O::ldc_lane(LDP);                       // T and P fragments
+    const uint32_t c_v = (uint32_t)((lr * LDV + vl) * Cf::ES);     // V rows lr.., column vl
+    auto slot_a = [&](int c) { return smem_a + (uint32_t)(Cf::OFF_SLOTS + (c % Cf::NSLOT) * Cf::SZ_SLOT); };
     auto cons_scalars = [&](int i, ConsPre& p) __attribute__((always_inline)) {
-        const char* slot = slot_ptr(i);
-        const E* __restrict__ sV = (const E*)(slot + Cf::OFF_SV);
-        const float* __restrict__ sc = (const float*)(slot + Cf::OFF_SSC);
-#pragma unroll
-        for (int ti = 0; ti < NT; ++ti)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * ti + lr + e;
-                p.vv[ti][e] = to_f32(sV[t * LDV + vl]);
-                p.bt[ti][e] = sc[Cf::SC_B + t];
-                p.bk[ti][e] = sc[Cf::SC_BK + t];
-            }
-    };
-    auto cons_prefetch = [&](int i, ConsPre& p) __attribute__((always_inline)) {
-        const char* slot = slot_ptr(i);
-        const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
-        const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
+        const uint32_t sa = slot_a(i);
+        const uint32_t vb = opaque_base(sa + Cf::OFF_SV + c_v);
+        p.sb = opaque_base(sa + Cf::OFF_SSC + (uint32_t)(lr * 4));
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) {
-            p.kf[ti] = O::ldc(sK, LDK, 16 * ti, 0);
-            p.qf[ti] = O::ldc(sQ, LDK, 16 * ti, 0);
+            const f32x4 bt4 = *lds_ptr<const f32x4>(p.sb + (uint32_t)((Cf::SC_B + 16 * ti) * 4));
+            const f32x4 bk4 = *lds_ptr<const f32x4>(p.sb + (uint32_t)((Cf::SC_BK + 16 * ti) * 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p.vv[ti][e] = to_f32(*lds_ptr<const E>(vb + (uint32_t)((16 * ti + e) * LDV * Cf::ES)));
+                p.bt[ti][e] = bt4[e];
+                p.bk[ti][e] = bk4[e];
+            }
+        }
+    };
+    auto cons_prefetch = [&](int i, ConsPre& p) __attribute__((always_inline)) {
+        p.kb = opaque_base(slot_a(i) + Cf::OFF_SK + c_kq);
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            p.kf[ti] = O::ldc_at(p.kb, LDK, 16 * ti, 0);
+            p.qf[ti] = O::ldc_at(p.kb + Cf::SZ_K, LDK, 16 * ti, 0);
         }
         if constexpr (Cf::SPREAD) cons_scalars(i, p);
     };
+    // the packed dot-product factors of split2_last, in scalar registers
+    uint32_t dm0 = kDotNegLo, dm1 = kDotNegHi;
+    asm volatile("" : "+s"(dm0), "+s"(dm1));
     auto consume = [&](int i, f32x4 (&accS)[NKT], ConsPre& pre) __attribute__((always_inline)) {
-        const char* slot = slot_ptr(i);
-        const E* __restrict__ sK = (const E*)(slot + Cf::OFF_SK);
-        const E* __restrict__ sQ = (const E*)(slot + Cf::OFF_SQ);
-        const float* __restrict__ sc = (const float*)(slot + Cf::OFF_SSC);
-        const E* __restrict__ Tp = (const E*)(smem + Cf::OFF_T + (i % Cf::NTBUF) * Cf::SZ_TP);
-        const E* __restrict__ Pp = (const E*)(smem + Cf::OFF_P + (i & 1) * Cf::SZ_TP);
+        const uint32_t sa = slot_a(i);
+        const uint32_t tb = opaque_base(smem_a + (uint32_t)(Cf::OFF_T + (i % Cf::NTBUF) * Cf::SZ_TP) + c_tp);
+        const uint32_t pb = opaque_base(smem_a + (uint32_t)(Cf::OFF_P + (i & 1) * Cf::SZ_TP) + c_tp);
         const int c0 = i * C;
         if constexpr (!Cf::SPREAD) cons_scalars(i, pre);
+        const uint32_t kqb = pre.kb, srb = pre.sb;
         // scale e^gamma of token 16 ti + lc (folded with rq by the P wave during
         // step i - 1 on the GATED path) and e^{gamma_C}
+        const uint32_t eb = opaque_base(sa + Cf::OFF_SSC + (uint32_t)(lc * 4));
         float egt[NT];
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti) egt[ti] = sc[Cf::SC_EG + 16 * ti + lc];
-        const float egC = sc[Cf::SC_EGC];
+        for (int ti = 0; ti < NT; ++ti) egt[ti] = *lds_ptr<const float>(eb + (uint32_t)((Cf::SC_EG + 16 * ti) * 4));
+        const float egC = *lds_ptr<const float>(sa + (uint32_t)((Cf::OFF_SSC / 4 + Cf::SC_EGC) * 4));
         // LDS operands are read ahead of the products that use them: the
         // first 32-deep K and Q slice and the row scalars during the previous
         // chunk's output phase, each further slice one stage ahead, then T;
@@ -897,14 +910,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             if (m + 1 < NKS) {
 #pragma unroll
                 for (int ti = 0; ti < NT; ++ti) {
-                    kf[nb][ti] = O::ldc(sK, LDK, 16 * ti, 32 * (m + 1));
-                    qf[nb][ti] = O::ldc(sQ, LDK, 16 * ti, 32 * (m + 1));
+                    kf[nb][ti] = O::ldc_at(kqb, LDK, 16 * ti, 32 * (m + 1));
+                    qf[nb][ti] = O::ldc_at(kqb + Cf::SZ_K, LDK, 16 * ti, 32 * (m + 1));
                 }
             } else {
 #pragma unroll
                 for (int ti = 0; ti < NT; ++ti) {
-                    tf[ti][0] = O::ldc(Tp, LDP, 16 * ti, 0);
-                    if constexpr (SP) tf[ti][1] = O::ldc(Tp, LDP, 16 * ti, C);
+                    tf[ti][0] = O::ldc_at(tb, LDP, 16 * ti, 0);
+                    if constexpr (SP) tf[ti][1] = O::ldc_at(tb, LDP, 16 * ti, C);
                 }
             }
             __builtin_amdgcn_sched_barrier(kComputeMayCross);
@@ -923,15 +936,17 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         // All transposed K tiles of the state update, issued now (into the
         // registers the K and Q fragments held) so that they arrive during R
         // and U; one base address for all tiles, the offsets as immediates.
-        const uint32_t ktb = opaque_base(lds_addr(sK) + O::ldt_lane(LDK, 0));
+        const uint32_t ktb = opaque_base(sa + Cf::OFF_SK + c_kt);
         F kt_f[NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) kt_f[kt] = O::ldt_at(ktb, LDK, kt);
         float dl[NT][4];                               // e^{gamma_C - gamma} of this lane's rows
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti)
+        for (int ti = 0; ti < NT; ++ti) {
+            const f32x4 d4 = *lds_ptr<const f32x4>(srb + (uint32_t)((Cf::SC_DL + 16 * ti) * 4));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dl[ti][e] = sc[Cf::SC_DL + 16 * ti + lr + e];
+            for (int e = 0; e < 4; ++e) dl[ti][e] = d4[e];
+        }
         __builtin_amdgcn_sched_barrier(kComputeMayCross);
         // R = beta V - beta e^gamma (K S0)
         f32x4 r[NT];
@@ -940,7 +955,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[ti][e] = pre.bt[ti][e] * pre.vv[ti][e] - pre.bk[ti][e] * ks[ti][e];
         F rh, rl;
-        O::split(r[0], r[1], rh, rl);
+        O::template split<true>(r[0], r[1], rh, rl, dm0, dm1);
         // U = T R
         f32x4 u[NT];
 #pragma unroll
@@ -959,13 +974,13 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
 #pragma unroll
             for (int e = 0; e < 4; ++e) ud[ti][e] = u[ti][e] * dl[ti][e];
         F dh, dlo;
-        O::split(ud[0], ud[1], dh, dlo);
+        O::template split<true>(ud[0], ud[1], dh, dlo, dm0, dm1);
         // P of the output, read while the state update runs
         F pf[NT][2];
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) {
-            pf[ti][0] = O::ldc(Pp, LDP, 16 * ti, 0);
-            if constexpr (SP) pf[ti][1] = O::ldc(Pp, LDP, 16 * ti, C);
+            pf[ti][0] = O::ldc_at(pb, LDP, 16 * ti, 0);
+            if constexpr (SP) pf[ti][1] = O::ldc_at(pb, LDP, 16 * ti, C);
         }
         __builtin_amdgcn_sched_barrier(kComputeMayCross);
 #pragma unroll
@@ -981,7 +996,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         // lane (g, n) holds 4 consecutive value columns 4g.. of token 16 ti + n,
         // stored as one vector.
         F uh, ul;
-        O::split(u[0], u[1], uh, ul);
+        O::template split<true>(u[0], u[1], uh, ul, dm0, dm1);
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) {
             f32x4 o;
