@@ -111,18 +111,23 @@ struct PipeCfg {
     // (fp32 path, whose tiles are twice as large) one inverse wave builds A
     // and T of a chunk in one step.
     static constexpr bool SPREAD = SP;
-    // Wave w runs on SIMD w % 4 (waves are placed round-robin): with four
+    // Wave w runs on SIMD w % 4 (waves are placed round-robin). With four
     // consumers, P and A share SIMDs 0 and 1 with the two stagers, and the
-    // inverse waves (the heaviest helpers) get SIMDs 2 and 3 to themselves.
-    // The K stager (gamma scan, decay scalars, gates) sits with the A wave
-    // and the lighter QV stager with the P wave, which has more VALU work.
+    // inverse waves (the heaviest helpers) get SIMDs 2 and 3 to themselves
+    // (besides a consumer); the K stager (gamma scan, decay scalars, gates)
+    // sits with the A wave and the lighter QV stager with the P wave, which
+    // has more VALU work. With one or two consumers the consumers share their
+    // SIMDs only with the stagers (the lightest roles) and the inverse waves
+    // go with P and A; with one consumer the K stager has SIMD 3 alone.
     static constexpr int NTW = SPREAD ? 2 : 1;     // inverse waves
+    static constexpr bool FEW = SPREAD && NCW < 4;
     static constexpr int W_P = NCW;                // P wave
     static constexpr int W_A = SPREAD ? NCW + 1 : -1;   // A wave
-    static constexpr int W_T = SPREAD ? NCW + 2 : NCW + 1;   // first inverse wave
-    static constexpr int W_S = W_T + NTW;          // first of two stager waves
-    static constexpr int W_SQ = W_S, W_SK = W_S + 1;    // QV stager, K stager
-    static constexpr int NW = W_S + 2;
+    static constexpr int W_T0 = FEW ? NCW + 4 : (SPREAD ? NCW + 2 : NCW + 1);   // inverse waves
+    static constexpr int W_T1 = W_T0 + NTW - 1;
+    static constexpr int W_SQ = FEW ? (NCW == 1 ? NCW + 3 : NCW + 2) : W_T1 + 1;   // QV stager
+    static constexpr int W_SK = FEW ? (NCW == 1 ? NCW + 2 : NCW + 3) : W_T1 + 2;   // K stager
+    static constexpr int NW = NCW + (SPREAD ? 6 : 4);
     static constexpr int THREADS = 64 * NW;
     static constexpr int NSLOT = SPREAD ? 5 : 3;   // chunks i .. i+NSLOT-1 resident
     static constexpr int LEAD = NSLOT - 1;         // the stagers write chunk i+LEAD
@@ -172,6 +177,9 @@ struct PipeCfg {
                          SC_RK = 5 * C, SC_GAML = 6 * C, SC_EGC = 7 * C;
 
     static_assert(C == 32, "the pipeline is laid out for 32-token chunks");
+    static_assert((1 << W_P | (SPREAD ? 1 << W_A : 0) | 1 << W_T0 | 1 << W_T1 | 1 << W_SQ | 1 << W_SK) ==
+                      (((1 << NW) - 1) & ~((1 << NCW) - 1)),
+                  "every helper role has its own wave after the consumers");
     static_assert(DK % 32 == 0 && BV % 16 == 0 && BV <= 64, "tile sizes");
     static_assert((C * DK / VE) % 64 == 0 && (C * BV / VE) % 64 == 0, "stager vector split");
     static_assert((SZ_K | SZ_V | SZ_SC | SZ_TP | SZ_F | SZ_I) % 16 == 0, "16-byte LDS alignment");
@@ -1077,8 +1085,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                     if (dk < Dk) sb[(size_t)dk * Dv + vl] = accS[kt][e];
                 }
         }
-    } else if (wave >= Cf::W_T && wave < Cf::W_T + Cf::NTW) {
-        const int pw = wave - Cf::W_T;
+    } else if (wave == Cf::W_T0 || wave == Cf::W_T1) {
+        const int pw = wave == Cf::W_T0 ? 0 : 1;
         // the solve result waits in registers for the merge
         typename std::conditional<INV == 0, float[16], f32x4[2]>::type x;
         auto solve = [&](int c) __attribute__((always_inline)) {
