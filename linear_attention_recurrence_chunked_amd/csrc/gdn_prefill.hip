@@ -153,17 +153,15 @@ struct PipeCfg {
     static constexpr int SZ_SLOT = 2 * SZ_K + SZ_V + SZ_SC;
     static constexpr int SZ_TP = C * LDP * ES;
     // A buffer: three 16 x ALD fp32 blocks, each in the layout its reader
-    // wants: A11 transposed, A22 reversed in both indices, A21 row-major.
+    // wants: A11 transposed, A22 and A21 row-major.
     static constexpr int SZ_F = 3 * 16 * ALD * 4;
-    static constexpr int AB_11T = 0, AB_22R = 16 * ALD, AB_21 = 32 * ALD;   // (floats)
-    static constexpr int SZ_I = 16 * 16 * 4;       // 16x16 identity (inverse start vectors)
+    static constexpr int AB_11T = 0, AB_22 = 16 * ALD, AB_21 = 32 * ALD;   // (floats)
     // The small T/P/A buffers sit at the bottom of LDS and the input slots
     // above them, so that their fixed offsets fit the 16-bit immediate offset
     // of LDS instructions (an address above 64 KiB costs an extra address
     // register per access).
     static constexpr int OFF_A = 0;
-    static constexpr int OFF_I = OFF_A + NABUF * SZ_F;
-    static constexpr int OFF_T = OFF_I + SZ_I;
+    static constexpr int OFF_T = OFF_A + NABUF * SZ_F;
     static constexpr int NTBUF = SPREAD ? 3 : 2;   // T of chunks i .. i+NTBUF-1
     static constexpr int OFF_P = OFF_T + NTBUF * SZ_TP;
     static constexpr int OFF_SLOTS = OFF_P + 2 * SZ_TP;
@@ -182,7 +180,7 @@ struct PipeCfg {
                   "every helper role has its own wave after the consumers");
     static_assert(DK % 32 == 0 && BV % 16 == 0 && BV <= 64, "tile sizes");
     static_assert((C * DK / VE) % 64 == 0 && (C * BV / VE) % 64 == 0, "stager vector split");
-    static_assert((SZ_K | SZ_V | SZ_SC | SZ_TP | SZ_F | SZ_I) % 16 == 0, "16-byte LDS alignment");
+    static_assert((SZ_K | SZ_V | SZ_SC | SZ_TP | SZ_F) % 16 == 0, "16-byte LDS alignment");
     static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KiB LDS of a CU");
 };
 
@@ -207,6 +205,20 @@ __device__ __forceinline__ double dpp_f64(double x) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xf, false);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, false);
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// x of lane k (0..3, a constant once unrolled) of this lane's quad: a DPP
+// quad_perm broadcast.
+__device__ __forceinline__ float quad_bcast(float x, int k) {
+    const int xi = __builtin_bit_cast(int, x);
+    int r;
+    switch (k) {
+        case 0: r = __builtin_amdgcn_mov_dpp(xi, 0x00, 0xf, 0xf, false); break;
+        case 1: r = __builtin_amdgcn_mov_dpp(xi, 0x55, 0xf, 0xf, false); break;
+        case 2: r = __builtin_amdgcn_mov_dpp(xi, 0xaa, 0xf, 0xf, false); break;
+        default: r = __builtin_amdgcn_mov_dpp(xi, 0xff, 0xf, 0xf, false); break;
+    }
+    return __builtin_bit_cast(float, r);
 }
 
 // x of lane `lane` (uniform), through scalar registers.
@@ -508,136 +520,99 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         for (int e = 0; e < 4; ++e)     // A11, stored transposed: [s][r], one vector per lane
             w[e] = (lc < lr + e) ? d11[e] * acc3[0][e] : 0.f;
         *(f32x4*)(sA + Cf::AB_11T + lc * ALD + lr) = w;
-        // A22 reversed: entry [15 - r][15 - s], rows 15 - lr - e = (12 - lr) + (3 - e)
-        __attribute__((address_space(3))) float* a22r = lds_ptr<float>(
-            opaque_base(lds_addr(sA) + (uint32_t)((Cf::AB_22R + (12 - lr) * ALD + 15 - lc) * 4)));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sA[Cf::AB_21 + (lr + e) * ALD + lc] = d21[e] * acc3[1][e];   // A21 row-major: [r][s]
-            a22r[(3 - e) * ALD] = (lc < lr + e) ? d22[e] * acc3[2][e] : 0.f;
+        for (int e = 0; e < 4; ++e) {   // A21 and A22 row-major: [r][s]
+            sA[Cf::AB_21 + (lr + e) * ALD + lc] = d21[e] * acc3[1][e];
+            sA[Cf::AB_22 + (lr + e) * ALD + lc] = (lc < lr + e) ? d22[e] * acc3[2][e] : 0.f;
         }
     };
 
     // Inverse wave: T = (I + A)^{-1} of chunk c from A buffer c % NABUF.
     //
-    // Diagonal blocks: forward substitution in fp32, both blocks in the same
-    // instructions. Lane (g, n) of half 0 (g = 0, 1) computes column n of
-    // T11 = (I + A11)^{-1}:  x_r = [r = n] - sum_{s<r} A11[r][s] x_s.
-    // Lane (g, n) of half 1 (g = 2, 3) computes row n of T22 in reverse order,
-    // x_r = T22[n][15 - r]; from x^T (I + A22) = e_n^T this obeys
-    //   x_r = [r = 15 - n] - sum_{s<r} A22[15 - s][15 - r] x_s,
-    // the same recurrence with the coefficient block M[s][r] = A22[15-s][15-r]
-    // in place of M[s][r] = A11[r][s]. Row s of M is read as broadcast
-    // vectors, LA steps ahead of its use.
+    // Diagonal blocks by substitution in fp32, four lanes per column: lane
+    // (j, q) = (l / 4, l % 4) holds rows 4q .. 4q+3 of column j. Step s needs
+    // the finished unknown s of every column, which lives in quarter s / 4 of
+    // the column's quad: a DPP quad broadcast hands it to the four lanes, and
+    // each lane updates its four rows with the coefficients of step s (zero
+    // where the triangle has none, so every lane runs the same instructions).
+    //  * T11 = (I + A11)^{-1} column j, forward (s = 0 .. 14):
+    //      x_r -= A11[r][s] x_s,  coefficients A11[4q..4q+3][s] = row s of
+    //      the transposed A11 block;
+    //  * T22^T = (I + A22^T)^{-1} column j, i.e. row j of T22, backward
+    //      (s = 15 .. 1): y_r -= A22[s][r] y_s, coefficients A22[s][4q..4q+3]
+    //      = row s of the row-major A22 block.
+    // The two chains run in the same loop, and their 16-byte coefficient rows
+    // are read LA steps ahead.
     //
     // Merge: T21 = -T22 (A21 T11) on fp32 MFMA (16x16x4, four steps). The
     // contraction index of step s for lane group g is 4g + s, so the B operand
-    // of X = A21 T11 is T11[4g+s][n] (column n, which half 0 holds) and the A
-    // operand of T22 X is T22[n][4g+s] (row n, which half 1 holds). The two
-    // halves swap the values the other needs with one lane shuffle per step.
-    const int g = l >> 4, n = l & 15, half = l >> 5, godd = g & 1;   // inverse-wave lane roles
-    auto t_solve = [&](int c, float (&x)[16]) __attribute__((always_inline)) {
+    // of X = A21 T11 is T11[4g+s][n] (column n) and the A operand of T22 X is
+    // T22[i][4g+s] = T22^T[4g+s][i]: both are element s of the substitution
+    // results after one lane permutation (lane 16g + n takes lane 4n + g).
+    const int jq = l >> 2, qq = l & 3;            // substitution lane roles: column, quarter
+    auto t_solve = [&](int c, f32x4 (&x)[2]) __attribute__((always_inline)) {
         const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
-        const float* __restrict__ sI = (const float*)(smem + Cf::OFF_I);
-        const float* M = sA + (half ? Cf::AB_22R : Cf::AB_11T);
         constexpr int LA = 4;
-        f32x4 colv[LA + 1][4];
-        auto col = [&](int s2, f32x4* dst) {
-#pragma unroll
-            for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4) dst[c4] = *(const f32x4*)(M + s2 * ALD + 4 * c4);
+        const uint32_t ab = opaque_base(lds_addr(sA) + (uint32_t)(4 * qq * 4));
+        f32x4 ca[LA + 1], cb[LA + 1];
+        auto coef = [&](int t, f32x4& a, f32x4& b) {
+            a = *lds_ptr<const f32x4>(ab + (uint32_t)((Cf::AB_11T + t * ALD) * 4));
+            b = *lds_ptr<const f32x4>(ab + (uint32_t)((Cf::AB_22 + (15 - t) * ALD) * 4));
         };
-        {
-            const float* e0 = sI + (half ? 15 - n : n) * 16;   // unit start vector
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 w = *(const f32x4*)(e0 + 4 * q);
-                x[4 * q] = w[0]; x[4 * q + 1] = w[1]; x[4 * q + 2] = w[2]; x[4 * q + 3] = w[3];
+        for (int t = 0; t < LA; ++t) coef(t, ca[t], cb[t]);
+        f32x4 xa, yb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xa[e] = 4 * qq + e == jq ? 1.f : 0.f;
+            yb[e] = xa[e];
+        }
+#pragma unroll
+        for (int t = 0; t < 15; ++t) {
+            if (t + LA < 15) coef(t + LA, ca[(t + LA) % (LA + 1)], cb[(t + LA) % (LA + 1)]);
+            const int sa = t, sb = 15 - t;
+            const float xs = quad_bcast(xa[sa & 3], sa >> 2);
+            const float ys = quad_bcast(yb[sb & 3], sb >> 2);
+            const f32x4 a = ca[t % (LA + 1)], b = cb[t % (LA + 1)];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xa[e] -= a[e] * xs;
+                yb[e] -= b[e] * ys;
             }
         }
-#pragma unroll
-        for (int s2 = 0; s2 < LA; ++s2) col(s2, colv[s2]);
-#pragma unroll
-        for (int s2 = 0; s2 < 15; ++s2) {
-            if (s2 + LA < 15) col(s2 + LA, colv[(s2 + LA) % (LA + 1)]);
-            const float xs = x[s2];
-            const f32x4* cv = colv[s2 % (LA + 1)];
-#pragma unroll
-            for (int r = s2 + 1; r < 16; ++r) x[r] -= cv[r >> 2][r & 3] * xs;
-            // Keep every element of the loaded vectors live up to here:
-            // otherwise an unused leading element lets the register allocator
-            // hand its register to another value while the load is in flight,
-            // and the write then waits for the load.
-#pragma unroll
-            for (int c4 = (s2 + 1) / 4; c4 < 4; ++c4) asm volatile("" ::"v"(cv[c4]));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // Diagonal blocks into the T buffer: rows [t][hi tpos(s) | lo tpos(s)]
-        // (fp32: [t][tpos(s)]).
+        x[0] = xa;
+        x[1] = yb;
+        // Diagonal blocks into the T buffer, rows [t][hi tpos(s) | lo tpos(s)]
+        // (fp32: [t][tpos(s)]): T11[4q+e][j] at row 4q + e, column tpos(j);
+        // row j of T22, columns 16 + 4q .. 16 + 4q + 3, at row 16 + j, columns
+        // tpos(16 + 4q + e) = 8q + 4 + e.
         E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c % Cf::NTBUF) * Cf::SZ_TP);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_pair<SP>(Tp + (4 * qq + e) * LDP + tpos(jq), C, xa[e]);
+        E* p22 = Tp + (16 + jq) * LDP + 8 * qq + 4;
         if constexpr (SP) {
-            if (half == 0) {
-                // column n of T11: lane group 0 writes the hi parts, group 1 the lo parts
-                uint32_t h[8], w2[8];
-#pragma unroll
-                for (int i2 = 0; i2 < 8; ++i2) split2(x[2 * i2], x[2 * i2 + 1], h[i2], w2[i2]);
-                uint16_t* p = (uint16_t*)(Tp + tpos(n) + (godd ? C : 0));
-#pragma unroll
-                for (int i2 = 0; i2 < 8; ++i2) {
-                    const uint32_t u = godd ? w2[i2] : h[i2];
-                    p[(2 * i2) * LDP] = (uint16_t)u;
-                    p[(2 * i2 + 1) * LDP] = (uint16_t)(u >> 16);
-                }
-            } else {
-                // row n of T22: T[16+n][16+4a+b] = x[15-4a-b], stored at column 8a+4+b;
-                // group 2 writes hi, group 3 lo
-                E* p = Tp + (16 + n) * LDP + 4 + (godd ? C : 0);
-#pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    uint32_t h0, l0, h1, l1;
-                    split2(x[15 - 4 * a4], x[14 - 4 * a4], h0, l0);
-                    split2(x[13 - 4 * a4], x[12 - 4 * a4], h1, l1);
-                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                    *(u32x2*)(p + 8 * a4) = godd ? u32x2{l0, l1} : u32x2{h0, h1};
-                }
-            }
+            uint32_t h0, l0, h1, l1;
+            split2(yb[0], yb[1], h0, l0);
+            split2(yb[2], yb[3], h1, l1);
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            *(u32x2*)p22 = u32x2{h0, h1};
+            *(u32x2*)(p22 + C) = u32x2{l0, l1};
         } else {
-            if (half == 0) {
-                if (!godd) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) Tp[r * LDP + tpos(n)] = x[r];
-                }
-            } else {
-                // row n of T22: columns 8a+4 .. 8a+7 hold T22[n][4a .. 4a+3] = x[15-4a], ..;
-                // group 2 writes a = 0, 1, group 3 a = 2, 3
-#pragma unroll
-                for (int a2 = 0; a2 < 2; ++a2) {
-                    const int a4 = 2 * godd + a2, o = 15 - 4 * a4;
-                    *(f32x4*)(Tp + (16 + n) * LDP + 8 * a4 + 4) = f32x4{x[o], x[o - 1], x[o - 2], x[o - 3]};
-                }
-            }
+            *(f32x4*)p22 = yb;
         }
     };
 
-    auto t_merge = [&](int c, const float (&x)[16]) __attribute__((always_inline)) {
+    auto t_merge = [&](int c, const f32x4 (&x)[2]) __attribute__((always_inline)) {
         const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
         E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c % Cf::NTBUF) * Cf::SZ_TP);
-        const f32x4 a21 = *(const f32x4*)(sA + Cf::AB_21 + n * ALD + 4 * g);   // A21[n][4g..4g+3]
-        // Merge operands: half 0 sends T11[8+4g+s][n] (for lane group g+2),
-        // half 1 sends T22[n][4(g-2)+s] (for lane group g-2).
+        const f32x4 a21 = *(const f32x4*)(sA + Cf::AB_21 + lc * ALD + lr);   // A21[lc][lr..lr+3]
+        // lane 16g + n takes element s of lane 4n + g
+        const int src = 4 * (4 * lc + (lr >> 2));
         float b11[4], a22[4];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-            // The candidates are pinned to registers first: a lane-dependent
-            // choice between array elements would otherwise become a choice
-            // of address and push x out to scratch memory.
-            float v[8] = {x[s2], x[4 + s2], x[8 + s2], x[12 + s2],
-                          x[15 - s2], x[11 - s2], x[7 - s2], x[3 - s2]};
-#pragma unroll
-            for (int q = 0; q < 8; ++q) asm("" : "+v"(v[q]));
-            const float send = half ? (godd ? v[5] : v[4]) : (godd ? v[3] : v[2]);
-            const float recv = __shfl_xor(send, 32);
-            b11[s2] = half ? recv : (godd ? v[1] : v[0]);
-            a22[s2] = half ? (godd ? v[7] : v[6]) : recv;
+            b11[s2] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, (float)x[0][s2])));
+            a22[s2] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, (float)x[1][s2])));
         }
         f32x4 X = zero4();
 #pragma unroll
@@ -645,24 +620,9 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         f32x4 Y = zero4();
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a22[s2], X[s2], Y, 0, 0, 0);
-        // T21 into the T buffer
-        if constexpr (SP) {
-            // T21 rows 16 + 4g + e, column n
-            uint32_t th[2], tl[2];
-            split2(-Y[0], -Y[1], th[0], tl[0]);
-            split2(-Y[2], -Y[3], th[1], tl[1]);
-            uint16_t* q = (uint16_t*)(Tp + (16 + 4 * g) * LDP + tpos(n));
+        // T21 rows 16 + 4g + e, column n
 #pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2) {
-                q[(2 * i2) * LDP] = (uint16_t)th[i2];
-                q[(2 * i2 + 1) * LDP] = (uint16_t)(th[i2] >> 16);
-                q[(2 * i2) * LDP + C] = (uint16_t)tl[i2];
-                q[(2 * i2 + 1) * LDP + C] = (uint16_t)(tl[i2] >> 16);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Tp[(16 + 4 * g + e) * LDP + tpos(n)] = -Y[e];
-        }
+        for (int e = 0; e < 4; ++e) store_pair<SP>(Tp + (16 + lr + e) * LDP + tpos(lc), C, -Y[e]);
     };
 
     // Neumann inverse (INV == 1). 16x16 matrices live in the accumulator
@@ -696,16 +656,15 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     auto n_solve = [&](int c, f32x4 (&tl)[2]) __attribute__((always_inline)) {
         const float* __restrict__ sA = (const float*)(smem + Cf::OFF_A + (c % Cf::NABUF) * Cf::SZ_F);
         const float* A11t = sA + Cf::AB_11T;   // [s][r] = A11[r][s]
-        const float* A22r = sA + Cf::AB_22R;   // [15-r][15-s] = A22[r][s]
+        const float* A22 = sA + Cf::AB_22;     // row-major
         const f32x4 a11 = *(const f32x4*)(A11t + lc * ALD + lr);          // A11[lr+e][lc]
         f32x4 a11t, a22;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             a11t[e] = A11t[(lr + e) * ALD + lc];                           // A11[lc][lr+e]
-            a22[e] = A22r[(15 - lr - e) * ALD + 15 - lc];                   // A22[lr+e][lc]
+            a22[e] = A22[(lr + e) * ALD + lc];                              // A22[lr+e][lc]
         }
-        const f32x4 w = *(const f32x4*)(A22r + (15 - lc) * ALD + 12 - lr);
-        const f32x4 a22t = {w[3], w[2], w[1], w[0]};                       // A22[lc][lr+e]
+        const f32x4 a22t = *(const f32x4*)(A22 + lc * ALD + lr);          // A22[lc][lr+e]
         tl[0] = neumann16(a11, a11t);                                       // T11
         tl[1] = neumann16(a22t, a22);                                       // (I + A22^T)^{-1} = T22^T
         E* __restrict__ Tp = (E*)(smem + Cf::OFF_T + (c % Cf::NTBUF) * Cf::SZ_TP);
@@ -1040,15 +999,13 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     //  otherwise:
     //   inverse wave      A, substitution, merge and T stores for chunk i+1
     // The upper-right 16x16 blocks of T and P are zero for every chunk; they
-    // are written once, for both buffers of each; so is the identity table.
+    // are written once, for both buffers of each.
     for (int id = threadIdx.x; id < (Cf::NTBUF + 2) * 256; id += Cf::THREADS) {
         const int which = id >> 8, r = (id >> 4) & 15, col = tpos(16 + (id & 15));
         E* base = (E*)(smem + (which < Cf::NTBUF ? Cf::OFF_T + which * Cf::SZ_TP
                                                  : Cf::OFF_P + (which - Cf::NTBUF) * Cf::SZ_TP));
         store_pair<SP>(base + r * LDP + col, C, 0.f);
     }
-    for (int id = threadIdx.x; id < 256; id += Cf::THREADS)
-        ((float*)(smem + Cf::OFF_I))[id] = (id >> 4) == (id & 15) ? 1.f : 0.f;
 
     if (wave < Cf::NCW) {
         f32x4 accS[NKT];
@@ -1088,7 +1045,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     } else if (wave == Cf::W_T0 || wave == Cf::W_T1) {
         const int pw = wave == Cf::W_T0 ? 0 : 1;
         // the solve result waits in registers for the merge
-        typename std::conditional<INV == 0, float[16], f32x4[2]>::type x;
+        f32x4 x[2];
         auto solve = [&](int c) __attribute__((always_inline)) {
             if constexpr (INV == 0) t_solve(c, x); else n_solve(c, x);
         };
