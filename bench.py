@@ -113,8 +113,8 @@ KERNEL_SOURCES = {
 }
 KERNEL_SOURCES["gdn_prefill_kernel_gated"] = KERNEL_SOURCES["gdn_prefill_kernel"]
 KERNEL_SOURCES["gdn_decode_kernel_gated"] = KERNEL_SOURCES["gdn_decode_kernel"]
-KERNEL_SOURCES["gdn_conv1d_prefill_kernel"] = "linear_attention_recurrence_chunked_amd/csrc/gdn_conv1d.hip"
-KERNEL_SOURCES["gdn_conv1d_decode_kernel"] = KERNEL_SOURCES["gdn_conv1d_prefill_kernel"]
+KERNEL_SOURCES["gdn_conv1d_prefill_tile_kernel"] = "linear_attention_recurrence_chunked_amd/csrc/gdn_conv1d.hip"
+KERNEL_SOURCES["gdn_conv1d_decode_kernel"] = KERNEL_SOURCES["gdn_conv1d_prefill_tile_kernel"]
 KERNEL_SOURCES["gdn_rmsnorm_gated_kernel"] = "linear_attention_recurrence_chunked_amd/csrc/gdn_norm.hip"
 KERNEL_SOURCES["gdn_decode_kernel_block"] = KERNEL_SOURCES["gdn_decode_kernel"]
 
@@ -767,8 +767,8 @@ def main():
         "conv1d_prefill": {"workload": cpw.name, "B": cpw.B, "C": cpw.C, "T": cpw.T,
                            "K": cpw.K, "value": cpw.B * cpw.T / (cpms / 1e3),
                            "unit": "tokens/s", "ms_per_step": cpms,
-                           "roofline": dict(bound="hbm", kernel="gdn_conv1d_prefill_kernel",
-                                            traffic=measured_traffic("gdn_conv1d_prefill_kernel"),
+                           "roofline": dict(bound="hbm", kernel="gdn_conv1d_prefill_tile_kernel",
+                                            traffic=measured_traffic("gdn_conv1d_prefill_tile_kernel"),
                                             **hbm(cpbytes, cpkern))},
         "conv1d_decode": {"workload": cdw.name, "B": cdw.B, "C": cdw.C, "K": cdw.K,
                           "value": 1e3 / cdms, "unit": "steps/s", "ms_per_step": cdms,
