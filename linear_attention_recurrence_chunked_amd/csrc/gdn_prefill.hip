@@ -104,13 +104,20 @@ struct PipeCfg {
     static constexpr bool SP = O::SPLIT;
     static constexpr int ES = (int)sizeof(E);
     static constexpr int VE = Vec16<E>::N;
-    static constexpr int NCW = BV / 16;            // consumer waves (16 value columns each)
+    static constexpr int NCW = BV / 16;            // 16-column strips of the state
     // SPREAD (bf16 path): two inverse waves take alternate chunks and spread
     // the inverse of a chunk over two steps (substitution, then merge and
     // stores), and an A wave builds A three chunks ahead. Without SPREAD
     // (fp32 path, whose tiles are twice as large) one inverse wave builds A
     // and T of a chunk in one step.
     static constexpr bool SPREAD = SP;
+    // PAIR (a single strip on the bf16 path, Dk = 128: the instance that runs
+    // when batch x heads cannot fill the chip): two consumer waves share the
+    // strip, each holding half of its key rows, and exchange their partial
+    // K S0 and Q S0 products through LDS within the step.
+    static constexpr bool PAIR = SPREAD && NCW == 1 && DK == 128;
+    static constexpr int NCWW = PAIR ? 2 : NCW;    // consumer waves
+    static constexpr int NKTW = (DK / 16) / (PAIR ? 2 : 1);   // state tiles per consumer wave
     // Wave w runs on SIMD w % 4 (waves are placed round-robin). With four
     // consumers, P and A share SIMDs 0 and 1 with the two stagers, and the
     // inverse waves (the heaviest helpers) get SIMDs 2 and 3 to themselves
@@ -120,14 +127,14 @@ struct PipeCfg {
     // SIMDs only with the stagers (the lightest roles) and the inverse waves
     // go with P and A; with one consumer the K stager has SIMD 3 alone.
     static constexpr int NTW = SPREAD ? 2 : 1;     // inverse waves
-    static constexpr bool FEW = SPREAD && NCW < 4;
-    static constexpr int W_P = NCW;                // P wave
-    static constexpr int W_A = SPREAD ? NCW + 1 : -1;   // A wave
-    static constexpr int W_T0 = FEW ? NCW + 4 : (SPREAD ? NCW + 2 : NCW + 1);   // inverse waves
+    static constexpr bool FEW = SPREAD && NCWW < 4;
+    static constexpr int W_P = NCWW;               // P wave
+    static constexpr int W_A = SPREAD ? NCWW + 1 : -1;   // A wave
+    static constexpr int W_T0 = FEW ? NCWW + 4 : (SPREAD ? NCWW + 2 : NCWW + 1);   // inverse waves
     static constexpr int W_T1 = W_T0 + NTW - 1;
-    static constexpr int W_SQ = FEW ? (NCW == 1 ? NCW + 3 : NCW + 2) : W_T1 + 1;   // QV stager
-    static constexpr int W_SK = FEW ? (NCW == 1 ? NCW + 2 : NCW + 3) : W_T1 + 2;   // K stager
-    static constexpr int NW = NCW + (SPREAD ? 6 : 4);
+    static constexpr int W_SQ = FEW ? (NCWW == 1 ? NCWW + 3 : NCWW + 2) : W_T1 + 1;   // QV stager
+    static constexpr int W_SK = FEW ? (NCWW == 1 ? NCWW + 2 : NCWW + 3) : W_T1 + 2;   // K stager
+    static constexpr int NW = NCWW + (SPREAD ? 6 : 4);
     static constexpr int THREADS = 64 * NW;
     static constexpr int NSLOT = SPREAD ? 5 : 3;   // chunks i .. i+NSLOT-1 resident
     static constexpr int LEAD = NSLOT - 1;         // the stagers write chunk i+LEAD
@@ -165,7 +172,13 @@ struct PipeCfg {
     static constexpr int NTBUF = SPREAD ? 3 : 2;   // T of chunks i .. i+NTBUF-1
     static constexpr int OFF_P = OFF_T + NTBUF * SZ_TP;
     static constexpr int OFF_SLOTS = OFF_P + 2 * SZ_TP;
-    static constexpr int LDS_BYTES = OFF_SLOTS + NSLOT * SZ_SLOT;
+    // PAIR exchange: per consumer wave three 1 KiB blocks (its partial K S0
+    // tiles 0 and 1, and its partial Q S0 tile of the other wave's output
+    // rows: one f32x4 per lane each) and a step counter.
+    static constexpr int OFF_X = OFF_SLOTS + NSLOT * SZ_SLOT;
+    static constexpr int SZ_XW = 3 * 64 * 16;
+    static constexpr int OFF_XF = OFF_X + 2 * SZ_XW;
+    static constexpr int LDS_BYTES = PAIR ? OFF_XF + 16 : OFF_X;
     // scalar arrays inside a slot (floats): gamma (its fp32 value and, in SC_GAML,
     // the rest gamma - fp32(gamma)), scale e^gamma, beta, beta e^gamma,
     // e^{gamma_C - gamma}, [0] = e^{gamma_C}; on the GATED path rk (from the A
@@ -176,7 +189,7 @@ struct PipeCfg {
 
     static_assert(C == 32, "the pipeline is laid out for 32-token chunks");
     static_assert((1 << W_P | (SPREAD ? 1 << W_A : 0) | 1 << W_T0 | 1 << W_T1 | 1 << W_SQ | 1 << W_SK) ==
-                      (((1 << NW) - 1) & ~((1 << NCW) - 1)),
+                      (((1 << NW) - 1) & ~((1 << NCWW) - 1)),
                   "every helper role has its own wave after the consumers");
     static_assert(DK % 32 == 0 && BV % 16 == 0 && BV <= 64, "tile sizes");
     static_assert((C * DK / VE) % 64 == 0 && (C * BV / VE) % 64 == 0, "stager vector split");
@@ -786,9 +799,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     };
 
     // ------------------------------------------------------------ consumers
-    const int vl = 16 * wave + lc;             // column of this lane within the slice
-    const bool vok = wave < Cf::NCW && vl < vcols;
-    const bool wok = wave < Cf::NCW && 16 * wave < vcols;   // this wave's 16 output columns exist
+    const int strip = Cf::PAIR ? 0 : wave;     // 16-column strip of a consumer wave
+    const int vl = 16 * strip + lc;            // column of this lane within the slice
+    const bool vok = wave < Cf::NCWW && vl < vcols;
+    const bool wok = wave < Cf::NCWW && 16 * strip < vcols;   // this wave's 16 output columns exist
     // accS[kt]: state rows spos(kt, lr/4, e), column vl, held for the whole sequence
     // Operands of chunk i that a consumer reads ahead, during the output phase
     // of chunk i - 1 (before the barrier between them): the first 32-deep K
@@ -809,6 +823,9 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     const uint32_t c_kt = O::ldt_lane(LDK, 0);                    // transposed K
     const uint32_t c_tp = O::ldc_lane(LDP);                       // T and P fragments
     const uint32_t c_v = (uint32_t)((lr * LDV + vl) * Cf::ES);     // V rows lr.., column vl
+    // PAIR: consumer wave h holds key rows 64h .. 64h+63, i.e. the 32-deep
+    // steps m = 2h, 2h+1 of K S0 and Q S0 and state tiles kt = 4h .. 4h+3.
+    const uint32_t kq0 = Cf::PAIR ? (uint32_t)(64 * (wave & 1) * Cf::ES) : 0u;
     auto slot_a = [&](int c) { return smem_a + (uint32_t)(Cf::OFF_SLOTS + (c % Cf::NSLOT) * Cf::SZ_SLOT); };
     auto cons_scalars = [&](int i, ConsPre& p) __attribute__((always_inline)) {
         const uint32_t sa = slot_a(i);
@@ -827,7 +844,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
     };
     auto cons_prefetch = [&](int i, ConsPre& p) __attribute__((always_inline)) {
-        p.kb = opaque_base(slot_a(i) + Cf::OFF_SK + c_kq);
+        p.kb = opaque_base(slot_a(i) + Cf::OFF_SK + c_kq + kq0);
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) {
             p.kf[ti] = O::ldc_at(p.kb, LDK, 16 * ti, 0);
@@ -985,6 +1002,139 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
     };
 
+    // PAIR consumer wave h (0 or 1) of chunk i: the same steps as consume()
+    // on key rows 64h .. 64h+63 (accS holds state tiles 4h .. 4h+3). Its
+    // partial K S0 (both token tiles) and Q S0 (the other wave's output tile)
+    // go to LDS, a step counter is released, and the other wave's partials are
+    // added once its counter shows this step; both waves then hold the same
+    // K S0 (a + b = b + a), form the same R and U, update their own rows and
+    // store output token tile h.
+    auto consume_pair = [&](int i, f32x4 (&accS)[Cf::NKTW], ConsPre& pre, int h) __attribute__((always_inline)) {
+        const uint32_t sa = slot_a(i);
+        const uint32_t tb = opaque_base(smem_a + (uint32_t)(Cf::OFF_T + (i % Cf::NTBUF) * Cf::SZ_TP) + c_tp);
+        const uint32_t pb = opaque_base(smem_a + (uint32_t)(Cf::OFF_P + (i & 1) * Cf::SZ_TP) + c_tp +
+                                        (uint32_t)(16 * h * LDP * Cf::ES));
+        const int c0 = i * C;
+        const uint32_t kqb = pre.kb, srb = pre.sb;
+        const uint32_t eb = opaque_base(sa + Cf::OFF_SSC + (uint32_t)((16 * h + lc) * 4));
+        const float egh = *lds_ptr<const float>(eb + (uint32_t)(Cf::SC_EG * 4));
+        const float egC = *lds_ptr<const float>(sa + (uint32_t)((Cf::OFF_SSC / 4 + Cf::SC_EGC) * 4));
+        f32x4 ks[NT], qs[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) { ks[ti] = zero4(); qs[ti] = zero4(); }
+        F kf[2][NT], qf[2][NT], tf[NT][2];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            kf[0][ti] = pre.kf[ti];
+            qf[0][ti] = pre.qf[ti];
+            kf[1][ti] = O::ldc_at(kqb, LDK, 16 * ti, 32);
+            qf[1][ti] = O::ldc_at(kqb + Cf::SZ_K, LDK, 16 * ti, 32);
+        }
+        __builtin_amdgcn_sched_barrier(kComputeMayCross);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            if (m == 1) {
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti) {
+                    tf[ti][0] = O::ldc_at(tb, LDP, 16 * ti, 0);
+                    tf[ti][1] = O::ldc_at(tb, LDP, 16 * ti, C);
+                }
+                __builtin_amdgcn_sched_barrier(kComputeMayCross);
+            }
+            F sh, sl;
+            O::split(accS[2 * m], accS[2 * m + 1], sh, sl);
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) {
+                ks[ti] = O::mma(kf[m][ti], sl, ks[ti]);
+                qs[ti] = O::mma(sl, qf[m][ti], qs[ti]);
+                ks[ti] = O::mma(kf[m][ti], sh, ks[ti]);
+                qs[ti] = O::mma(sh, qf[m][ti], qs[ti]);
+            }
+        }
+        // exchange: this wave's block h, the other wave's block 1 - h
+        const uint32_t xo = smem_a + (uint32_t)(Cf::OFF_X + h * Cf::SZ_XW + l * 16);
+        const uint32_t xp = smem_a + (uint32_t)(Cf::OFF_X + (1 - h) * Cf::SZ_XW + l * 16);
+        int* flags = (int*)(smem + Cf::OFF_XF);
+        *lds_ptr<f32x4>(xo) = ks[0];
+        *lds_ptr<f32x4>(xo + 1024) = ks[1];
+        *lds_ptr<f32x4>(xo + 2048) = h ? qs[0] : qs[1];
+        __hip_atomic_store(&flags[h], i + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // the transposed K tiles of this wave's rows and e^{gamma_C - gamma}
+        // are read while the other wave finishes its half
+        const uint32_t ktb = opaque_base(sa + Cf::OFF_SK + c_kt + (uint32_t)(64 * h * Cf::ES));
+        F kt_f[Cf::NKTW];
+#pragma unroll
+        for (int kt = 0; kt < Cf::NKTW; ++kt) kt_f[kt] = O::ldt_at(ktb, LDK, kt);
+        float dl[NT][4];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            const f32x4 d4 = *lds_ptr<const f32x4>(srb + (uint32_t)((Cf::SC_DL + 16 * ti) * 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dl[ti][e] = d4[e];
+        }
+        // Bounded wait for the other wave's counter: it always arrives (both
+        // waves run the same steps), and the bound keeps every wave finite.
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__hip_atomic_load(&flags[1 - h], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > i) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const f32x4 pk0 = *lds_ptr<const f32x4>(xp);
+        const f32x4 pk1 = *lds_ptr<const f32x4>(xp + 1024);
+        const f32x4 pq = *lds_ptr<const f32x4>(xp + 2048);
+        ks[0] += pk0;
+        ks[1] += pk1;
+        const f32x4 qh = (h ? qs[1] : qs[0]) + pq;
+        __builtin_amdgcn_sched_barrier(kComputeMayCross);
+        // R = beta V - beta e^gamma (K S0), U = T R (both token tiles)
+        f32x4 r[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[ti][e] = pre.bt[ti][e] * pre.vv[ti][e] - pre.bk[ti][e] * ks[ti][e];
+        F rh, rl;
+        O::template split<true>(r[0], r[1], rh, rl, dm0, dm1);
+        f32x4 u[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            u[ti] = zero4();
+            u[ti] = O::mma(tf[ti][1], rh, u[ti]);
+            u[ti] = O::mma(tf[ti][0], rl, u[ti]);
+            u[ti] = O::mma(tf[ti][0], rh, u[ti]);
+        }
+        f32x4 ud[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ud[ti][e] = u[ti][e] * dl[ti][e];
+        F dh, dlo;
+        O::template split<true>(ud[0], ud[1], dh, dlo, dm0, dm1);
+        // P rows of output tile h, read while the state update runs
+        const F p0 = O::ldc_at(pb, LDP, 0, 0);
+        const F p1 = O::ldc_at(pb, LDP, 0, C);
+        __builtin_amdgcn_sched_barrier(kComputeMayCross);
+#pragma unroll
+        for (int kt = 0; kt < Cf::NKTW; ++kt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accS[kt][e] *= egC;
+            accS[kt] = O::mma(kt_f[kt], dlo, accS[kt]);
+            accS[kt] = O::mma(kt_f[kt], dh, accS[kt]);
+        }
+        cons_prefetch(i + 1, pre);
+        F uh, ul;
+        O::template split<true>(u[0], u[1], uh, ul, dm0, dm1);
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = qh[e] * egh;
+        o = O::mma(uh, p1, o);
+        o = O::mma(ul, p0, o);
+        o = O::mma(uh, p0, o);
+        if (wok && c0 + 16 * h + lc < S) {
+            E* dst = ob + (size_t)(c0 + 16 * h + lc) * Dv + lr;
+            if constexpr (SP) *(bf16x4*)dst = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+            else *(f32x4*)dst = o;
+        }
+    };
+
     // ------------------------------------------------------------ schedule
     // Each role runs its own program: three prologue barriers, then one
     // barrier per step i = 0 .. NC-1. Values a role carries from step to step
@@ -1007,13 +1157,19 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         store_pair<SP>(base + r * LDP + col, C, 0.f);
     }
 
-    if (wave < Cf::NCW) {
-        f32x4 accS[NKT];
+    if constexpr (Cf::PAIR) {
+        if (threadIdx.x < 2) ((int*)(smem + Cf::OFF_XF))[threadIdx.x] = 0;   // exchange step counters
+    }
+
+    if (wave < Cf::NCWW) {
+        // state tiles kt0 .. kt0 + NKTW - 1 of the strip (all of them unless PAIR)
+        const int kt0 = Cf::PAIR ? Cf::NKTW * wave : 0;
+        f32x4 accS[Cf::NKTW];
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
+        for (int kt = 0; kt < Cf::NKTW; ++kt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int dk = spos(kt, lr >> 2, e);
+                const int dk = spos(kt0 + kt, lr >> 2, e);
                 accS[kt][e] = (vok && dk < Dk) ? sb[(size_t)dk * Dv + vl] : 0.f;
             }
         }
@@ -1023,22 +1179,24 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         ConsPre pre;
         cons_prefetch(0, pre);
         for (int i = 0; i < NC; ++i) {
-            consume(i, accS, pre);
-            // The consumers write no LDS, and the only LDS reads they may
-            // still have in flight here are the prefetches of chunk i + 1,
-            // whose slot no wave writes before step i + 2: they pass the
-            // barrier without waiting for those reads (a compiler-only fence
-            // keeps every LDS access on its side of it).
+            if constexpr (Cf::PAIR) consume_pair(i, accS, pre, wave);
+            else consume(i, accS, pre);
+            // The only LDS reads a consumer may still have in flight here are
+            // the prefetches of chunk i + 1, whose slot no wave writes before
+            // step i + 2 (a PAIR wave's exchange reads were consumed within
+            // the step, and its exchange writes precede its counter release):
+            // they pass the barrier without waiting for those reads (a
+            // compiler-only fence keeps every LDS access on its side of it).
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
         if (vok) {
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
+            for (int kt = 0; kt < Cf::NKTW; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int dk = spos(kt, lr >> 2, e);
+                    const int dk = spos(kt0 + kt, lr >> 2, e);
                     if (dk < Dk) sb[(size_t)dk * Dv + vl] = accS[kt][e];
                 }
         }
