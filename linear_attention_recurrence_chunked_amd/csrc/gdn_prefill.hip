@@ -1076,7 +1076,6 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         // waves run the same steps), and the bound keeps every wave finite.
         for (int spin = 0; spin < (1 << 22); ++spin) {
             if (__hip_atomic_load(&flags[1 - h], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > i) break;
-            __builtin_amdgcn_s_sleep(1);
         }
         const f32x4 pk0 = *lds_ptr<const f32x4>(xp);
         const f32x4 pk1 = *lds_ptr<const f32x4>(xp + 1024);
