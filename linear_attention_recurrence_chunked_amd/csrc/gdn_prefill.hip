@@ -29,11 +29,14 @@
 //    registers as the B operand), R, U = T R, O = e^gamma Q S0 + P U and the
 //    state update K^T (dl U) -- every intermediate stays in registers; LDS is
 //    only read for K, Q, V, T and P of the chunk (the first K/Q slice and
-//    the row scalars of chunk i+1 already during chunk i's output phase);
+//    the row scalars of chunk i+1 already during chunk i's output phase).
+//    With a single strip (PAIR) two waves share it, each holding half of
+//    the key rows, and exchange their partial K S0 / Q S0 through LDS;
 //  * two inverse waves build T = (I + A)^{-1}, taking alternate chunks and
-//    spreading a chunk over two steps: fp32 forward substitution of the two
-//    16x16 diagonal blocks for chunk i+2 (one lane per column), then the
-//    merge T21 = -T22 (A21 T11) on fp32 MFMA and the stores for chunk i+1;
+//    spreading a chunk over two steps: fp32 substitution of the two 16x16
+//    diagonal blocks for chunk i+2 (four lanes per column, the finished
+//    unknown passed by a DPP quad broadcast), then the merge
+//    T21 = -T22 (A21 T11) on fp32 MFMA and the stores for chunk i+1;
 //  * the A wave builds A = diag(beta) (K K^T) (.) Mstrict for chunk i+3;
 //  * the P wave builds P = Q K^T (.) Mincl for chunk i+1;
 //  * two stager waves (K with g and beta; Q with V) issue the loads of chunk
@@ -45,7 +48,7 @@
 //
 // LDS holds the input slots of chunks i .. i+LEAD (5 on the bf16 path, 3 on
 // the fp32 path), three T, two P and three A buffers (two T, two P, one A on
-// the fp32 path).
+// the fp32 path), and with PAIR the consumers' exchange blocks.
 // The state-independent work of a chunk therefore never sits on the
 // sequential path. HBM traffic is the algorithmic minimum: q, k, v, g, beta
 // read once per slice, out written once, the state read and written once.
