@@ -115,11 +115,14 @@ struct PipeCfg {
     // and T of a chunk in one step.
     static constexpr bool SPREAD = SP;
     // PAIR (a single strip on the bf16 path, Dk = 128: the instance that runs
-    // when batch x heads cannot fill the chip): two consumer waves share the
-    // strip, each holding half of its key rows, and exchange their partial
-    // K S0 and Q S0 products through LDS within the step.
+    // when batch x heads cannot fill the chip with wider slices): two
+    // consumer waves share the strip, each holding half of its key rows, and
+    // exchange their partial K S0 and Q S0 products through LDS within the
+    // step. Consumer wave w works on strip w / 2 and key half w % 2. (With two
+    // strips the pairs measured 9 % slower: four consumer waves then share
+    // SIMDs with the helpers, and R and U run twice per strip.)
     static constexpr bool PAIR = SPREAD && NCW == 1 && DK == 128;
-    static constexpr int NCWW = PAIR ? 2 : NCW;    // consumer waves
+    static constexpr int NCWW = PAIR ? 2 * NCW : NCW;    // consumer waves
     static constexpr int NKTW = (DK / 16) / (PAIR ? 2 : 1);   // state tiles per consumer wave
     // Wave w runs on SIMD w % 4 (waves are placed round-robin). With four
     // consumers, P and A share SIMDs 0 and 1 with the two stagers, and the
@@ -180,8 +183,8 @@ struct PipeCfg {
     // rows: one f32x4 per lane each) and a step counter.
     static constexpr int OFF_X = OFF_SLOTS + NSLOT * SZ_SLOT;
     static constexpr int SZ_XW = 3 * 64 * 16;
-    static constexpr int OFF_XF = OFF_X + 2 * SZ_XW;
-    static constexpr int LDS_BYTES = PAIR ? OFF_XF + 16 : OFF_X;
+    static constexpr int OFF_XF = OFF_X + NCWW * SZ_XW;
+    static constexpr int LDS_BYTES = PAIR ? OFF_XF + 4 * NCWW : OFF_X;
     // scalar arrays inside a slot (floats): gamma (its fp32 value and, in SC_GAML,
     // the rest gamma - fp32(gamma)), scale e^gamma, beta, beta e^gamma,
     // e^{gamma_C - gamma}, [0] = e^{gamma_C}; on the GATED path rk (from the A
@@ -802,7 +805,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     };
 
     // ------------------------------------------------------------ consumers
-    const int strip = Cf::PAIR ? 0 : wave;     // 16-column strip of a consumer wave
+    const int strip = Cf::PAIR ? wave >> 1 : wave;   // 16-column strip of a consumer wave
     const int vl = 16 * strip + lc;            // column of this lane within the slice
     const bool vok = wave < Cf::NCWW && vl < vcols;
     const bool wok = wave < Cf::NCWW && 16 * strip < vcols;   // this wave's 16 output columns exist
@@ -1054,14 +1057,14 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
                 qs[ti] = O::mma(sh, qf[m][ti], qs[ti]);
             }
         }
-        // exchange: this wave's block h, the other wave's block 1 - h
-        const uint32_t xo = smem_a + (uint32_t)(Cf::OFF_X + h * Cf::SZ_XW + l * 16);
-        const uint32_t xp = smem_a + (uint32_t)(Cf::OFF_X + (1 - h) * Cf::SZ_XW + l * 16);
+        // exchange: this wave's block, the partner's (wave ^ 1) block
+        const uint32_t xo = smem_a + (uint32_t)(Cf::OFF_X + wave * Cf::SZ_XW + l * 16);
+        const uint32_t xp = smem_a + (uint32_t)(Cf::OFF_X + (wave ^ 1) * Cf::SZ_XW + l * 16);
         int* flags = (int*)(smem + Cf::OFF_XF);
         *lds_ptr<f32x4>(xo) = ks[0];
         *lds_ptr<f32x4>(xo + 1024) = ks[1];
         *lds_ptr<f32x4>(xo + 2048) = h ? qs[0] : qs[1];
-        __hip_atomic_store(&flags[h], i + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&flags[wave], i + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         // the transposed K tiles of this wave's rows and e^{gamma_C - gamma}
         // are read while the other wave finishes its half
         const uint32_t ktb = opaque_base(sa + Cf::OFF_SK + c_kt + (uint32_t)(64 * h * Cf::ES));
@@ -1078,7 +1081,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         // Bounded wait for the other wave's counter: it always arrives (both
         // waves run the same steps), and the bound keeps every wave finite.
         for (int spin = 0; spin < (1 << 22); ++spin) {
-            if (__hip_atomic_load(&flags[1 - h], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > i) break;
+            if (__hip_atomic_load(&flags[wave ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > i) break;
         }
         const f32x4 pk0 = *lds_ptr<const f32x4>(xp);
         const f32x4 pk1 = *lds_ptr<const f32x4>(xp + 1024);
@@ -1131,7 +1134,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         o = O::mma(ul, p0, o);
         o = O::mma(uh, p0, o);
         if (wok && c0 + 16 * h + lc < S) {
-            E* dst = ob + (size_t)(c0 + 16 * h + lc) * Dv + lr;
+            E* dst = ob + (size_t)(c0 + 16 * h + lc) * Dv + 16 * strip + lr;
             if constexpr (SP) *(bf16x4*)dst = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
             else *(f32x4*)dst = o;
         }
@@ -1160,12 +1163,12 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
     }
 
     if constexpr (Cf::PAIR) {
-        if (threadIdx.x < 2) ((int*)(smem + Cf::OFF_XF))[threadIdx.x] = 0;   // exchange step counters
+        if ((int)threadIdx.x < Cf::NCWW) ((int*)(smem + Cf::OFF_XF))[threadIdx.x] = 0;   // exchange step counters
     }
 
     if (wave < Cf::NCWW) {
         // state tiles kt0 .. kt0 + NKTW - 1 of the strip (all of them unless PAIR)
-        const int kt0 = Cf::PAIR ? Cf::NKTW * wave : 0;
+        const int kt0 = Cf::PAIR ? Cf::NKTW * (wave & 1) : 0;
         f32x4 accS[Cf::NKTW];
 #pragma unroll
         for (int kt = 0; kt < Cf::NKTW; ++kt) {
@@ -1181,7 +1184,7 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         ConsPre pre;
         cons_prefetch(0, pre);
         for (int i = 0; i < NC; ++i) {
-            if constexpr (Cf::PAIR) consume_pair(i, accS, pre, wave);
+            if constexpr (Cf::PAIR) consume_pair(i, accS, pre, wave & 1);
             else consume(i, accS, pre);
             // The only LDS reads a consumer may still have in flight here are
             // the prefetches of chunk i + 1, whose slot no wave writes before

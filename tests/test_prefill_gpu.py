@@ -54,6 +54,18 @@ def test_weak_decay(dtype):
     _parity("weak/%s" % dtype, d, dtype, w.scale)
 
 
+@pytest.mark.parametrize("B,Dv", [(1, 128), (2, 128), (2, 112)])
+def test_consumer_pair_slices(B, Dv):
+    """Batch x heads too small for four-strip slices: B = 1 runs one 16-column
+    strip per workgroup and B = 2 two strips (Hv = 32, Dk = 128), each strip
+    shared by two consumer waves that exchange partial products; Dv = 112
+    leaves the second strip of the last slice without columns. Ragged S, a
+    carried state, weak decay (the exchange's sums feed every later chunk)."""
+    d = workloads.draw_prefill(B=B, Hk=16, Hv=32, S=328, Dk=128, Dv=Dv, dtype="bf16",
+                               state="normal", decay="weak", seed=(9, 3, B))
+    _parity("pair B=%d Dv=%d" % (B, Dv), d, "bf16", 128 ** -0.5)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [
     dict(B=1, Hk=2, Hv=2, S=64, Dk=64, Dv=64),      # one chunk, G = 1
