@@ -46,11 +46,13 @@ def test_conv_prefill_taps(dtype, K):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("B,C,T", [(3, 40, 6000), (2, 12, 20000)])
+@pytest.mark.parametrize("B,C,T", [(3, 40, 6000), (2, 12, 20000), (2, 10, 17001)])
 def test_conv_prefill_multi_tile_rows(dtype, B, C, T):
     """Many channels and batches; T = 20000 spreads each row over three
     workgroups (8192 tokens each) with a ragged tail, so the history across
-    workgroup boundaries and the window state of the last one are covered."""
+    workgroup boundaries and the window state of the last one are covered
+    (T % 8 == 0: the range-checked tile kernel); T = 17001 does the same on
+    the general kernel (a last vector only partly inside the row)."""
     d = workloads.draw_conv(B, C, T, 4, dtype=dtype)
     log("conv prefill multi-tile", dtype, B, C, T)
     out, st = _prefill(d["x"], d["w"], dtype)
