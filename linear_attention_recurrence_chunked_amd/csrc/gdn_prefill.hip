@@ -143,7 +143,7 @@ struct PipeCfg {
     static constexpr int NW = NCWW + (SPREAD ? 6 : 4);
     static constexpr int THREADS = 64 * NW;
     static constexpr int NSLOT = SPREAD ? 5 : 3;   // chunks i .. i+NSLOT-1 resident
-    static constexpr int LEAD = NSLOT - 1;         // the stagers write chunk i+LEAD
+    static constexpr int LEAD = NSLOT - 1;         // the stagers write chunk i+LEAD (even)
     static constexpr int NABUF = SPREAD ? 3 : 1;   // A of chunks i+1 .. i+3
     // Row strides (elements), chosen so that the 16-byte fragment reads and
     // the transpose reads of each buffer spread over the LDS banks (on the
@@ -194,6 +194,7 @@ struct PipeCfg {
                          SC_RK = 5 * C, SC_GAML = 6 * C, SC_EGC = 7 * C;
 
     static_assert(C == 32, "the pipeline is laid out for 32-token chunks");
+    static_assert(LEAD % 2 == 0, "the stagers' prologue stores chunks in pairs");
     static_assert((1 << W_P | (SPREAD ? 1 << W_A : 0) | 1 << W_T0 | 1 << W_T1 | 1 << W_SQ | 1 << W_SK) ==
                       (((1 << NW) - 1) & ~((1 << NCWW) - 1)),
                   "every helper role has its own wave after the consumers");
@@ -1218,6 +1219,8 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         __syncthreads();
         if constexpr (!Cf::SPREAD) {
             if (NC > 0) { build_A(0); wave_lds_fence(); solve(0); merge(0); }
+        } else {
+            if (NC > 1 + pw) build_A(1 + pw);          // beside the A wave's chunk 0
         }
         __syncthreads();
         if constexpr (Cf::SPREAD) {
@@ -1249,8 +1252,10 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             __syncthreads();
         }
     } else if (wave == Cf::W_A) {
+        // A of chunks 0, 1, 2 between the first two barriers: chunk 0 here,
+        // chunks 1 and 2 by the inverse waves, which are idle until the second
         __syncthreads();
-        for (int c = 0; c < 3 && c < NC; ++c) build_A(c);
+        build_A(0);
         __syncthreads();
         __syncthreads();
         for (int i = 0; i < NC; ++i) {
@@ -1259,15 +1264,27 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
         }
     } else if (wave == Cf::W_SK) {
         if constexpr (GATED) { expA = expf(A_log[h]); dtb = dt_bias[h]; }
-        // Loads are issued a full step before their data is stored: at step i
-        // the loads of chunk i + LEAD + 1 go out first, then chunk i + LEAD
-        // (loaded during step i - 1) is stored. Two register sets alternate
-        // (the loop is unrolled by two), so the HBM latency passes during the
-        // rest of the step and the barrier instead of inside the store.
-        for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
-            KRegs R;
-            stage_k_load(c, R);
-            stage_k_store(c, R);
+        // Chunks 0 .. LEAD-1 are stored before the first barrier, their loads
+        // running two chunks ahead of the stores (two register sets), so the
+        // HBM latency is paid about once instead of once per chunk. (NC >= 1;
+        // loads past the last chunk reload it, harmlessly.)
+        // Then loads are issued a full step before their data is stored: at
+        // step i the loads of chunk i + LEAD + 1 go out first, then chunk
+        // i + LEAD (loaded during step i - 1) is stored. Two register sets
+        // alternate (the loop is unrolled by two), so the HBM latency passes
+        // during the rest of the step and the barrier instead of inside the
+        // store.
+        {
+            KRegs P0, P1;
+            stage_k_load(0, P0);
+            stage_k_load(min(1, NC - 1), P1);
+#pragma unroll
+            for (int c = 0; c < Cf::LEAD; c += 2) {
+                if (c < NC) stage_k_store(c, P0);
+                if (c + 2 < Cf::LEAD) stage_k_load(min(c + 2, NC - 1), P0);
+                if (c + 1 < NC) stage_k_store(c + 1, P1);
+                if (c + 3 < Cf::LEAD) stage_k_load(min(c + 3, NC - 1), P1);
+            }
         }
         KRegs Ra, Rb;
         stage_k_load(min(Cf::LEAD, NC - 1), Ra);
@@ -1285,10 +1302,17 @@ __global__ __launch_bounds__((PipeCfg<E, C, DK, BV>::THREADS)) void gdn_prefill_
             }
         }
     } else {
-        for (int c = 0; c < Cf::LEAD && c < NC; ++c) {
-            QVRegs R;
-            stage_qv_load(c, R);
-            stage_qv_store(c, R);
+        {
+            QVRegs P0, P1;                             // as the K stager's prologue
+            stage_qv_load(0, P0);
+            stage_qv_load(min(1, NC - 1), P1);
+#pragma unroll
+            for (int c = 0; c < Cf::LEAD; c += 2) {
+                if (c < NC) stage_qv_store(c, P0);
+                if (c + 2 < Cf::LEAD) stage_qv_load(min(c + 2, NC - 1), P0);
+                if (c + 1 < NC) stage_qv_store(c + 1, P1);
+                if (c + 3 < Cf::LEAD) stage_qv_load(min(c + 3, NC - 1), P1);
+            }
         }
         QVRegs Ra, Rb;
         stage_qv_load(min(Cf::LEAD, NC - 1), Ra);
