@@ -37,6 +37,16 @@ def test_prefill_b4_s8192_full():
     _parity(w.name, workloads.draw_workload(w), "bf16", w.scale)
 
 
+def test_prefill_b2_s8192_two_strip_slices():
+    """B = 2 at the bench's heads and length: the two-strip (32-column)
+    slices, element by element over the full 8192 tokens with a carried
+    state."""
+    w = W["prefill_b4_s8192"]
+    d = workloads.draw_prefill(B=2, Hk=16, Hv=32, S=8192, Dk=128, Dv=128, dtype="bf16",
+                               state="normal", decay="std", seed=(11, 2, 0))
+    _parity("b2 s8192", d, "bf16", w.scale)
+
+
 @pytest.mark.parametrize("variant", ["std", "strong"])
 def test_prefill_s65536(variant):
     w = W["prefill_s65536"]
@@ -56,11 +66,12 @@ def test_weak_decay(dtype):
 
 @pytest.mark.parametrize("B,Dv", [(1, 128), (2, 128), (2, 112)])
 def test_consumer_pair_slices(B, Dv):
-    """Batch x heads too small for four-strip slices: B = 1 runs one 16-column
-    strip per workgroup and B = 2 two strips (Hv = 32, Dk = 128), each strip
-    shared by two consumer waves that exchange partial products; Dv = 112
-    leaves the second strip of the last slice without columns. Ragged S, a
-    carried state, weak decay (the exchange's sums feed every later chunk)."""
+    """Batch x heads too small for four-strip slices (Hv = 32, Dk = 128):
+    B = 1 runs one 16-column strip per workgroup, shared by two consumer
+    waves that exchange partial products; B = 2 runs two strips per
+    workgroup, one consumer wave each, and Dv = 112 leaves the second strip
+    of the last slice without columns. Ragged S, a carried state, weak decay
+    (the exchange's sums feed every later chunk)."""
     d = workloads.draw_prefill(B=B, Hk=16, Hv=32, S=328, Dk=128, Dv=Dv, dtype="bf16",
                                state="normal", decay="weak", seed=(9, 3, B))
     _parity("pair B=%d Dv=%d" % (B, Dv), d, "bf16", 128 ** -0.5)
